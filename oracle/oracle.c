@@ -1,0 +1,355 @@
+/*
+ * oracle.c -- plain, slow fp64 CPU oracle for the Gemma 4 interleaved attention
+ * block (sliding-window local attention and global attention with GQA, K=V and
+ * p-RoPE).
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path links, loads or calls
+ * this file: only the tests, the smoke check of the package entry module and
+ * the CPU-baseline leg of the benchmark use it.  It shares no code, header,
+ * table or constant with the HIP library.
+ *
+ * What it computes is the plain definition of causal attention with rotary
+ * position encoding, written out with no tiling, no online softmax, no
+ * fusion: every output row is
+ *     out[b,i,h] = sum_j w_j v_j / sum_j w_j,   w_j = exp(s_j - max_j s_j),
+ *     s_j = <R(pos_i) q[b,i,h], R(pos_j) k[b,j,h/G]> / sqrt(d)
+ * over the keys j that row i may see.  Sources, by page and section:
+ *
+ *  - Local vs global layers, window sizes, causal "whole preceding sequence":
+ *    "Guia visual do Gemma 4" (pt.news.hada.io), section "Intercalacao de
+ *    camadas de atencao (Interleaving Layers)"; and "Gemma 4: yak Google
+ *    DeepMind ..." (techtoday.in.ua), section "Optymizovana uvaha: lokalni y
+ *    hlobalni shary".
+ *  - GQA (8 query heads per KV head in global layers; 2 in local layers):
+ *    "Guia visual do Gemma 4", section "GQA (Grouped Query Attention)";
+ *    techtoday page, same attention section.
+ *  - K=V (keys and values are the same tensor in global layers):
+ *    "Guia visual do Gemma 4", section "Tecnica K=V".
+ *  - p-RoPE (only a fraction p of the rotary pairs is rotated; the
+ *    low-frequency pairs are left alone to carry meaning):
+ *    "Guia visual do Gemma 4", section "p-RoPE".
+ *  - KV cache grows with prompt + generated tokens (decode):
+ *    "Visao geral do modelo Gemma 4" (ai.google.dev), section "Principais
+ *    Consideracoes para o planejamento de memoria".
+ *
+ * Readings taken where the pages are silent (each is listed with the others in
+ * the design notes of the repository):
+ *  - n_rot = floor(p * d / 2) pairs are rotated: pairs t = 0 .. n_rot-1, which
+ *    are the highest-frequency ones; pair t occupies dims (2t, 2t+1) and turns
+ *    by angle pos * theta^(-2t/d) (frequency over the full head dim d).
+ *  - The rotation is counter-clockwise: (x, y) -> (x c - y s, x s + y c).
+ *  - Window W keeps keys with 0 <= i - j < W (W keys including self); W = 0
+ *    means unbounded (global).  Both layer kinds are causal.  The mask uses the
+ *    sequence index; positions only feed the rotation.
+ *  - Scores are scaled by 1/sqrt(d), d the layer's own head dim.
+ *  - K=V: the same raw tensor is rotated for the scores and used raw as values.
+ *  - Query head h reads KV head floor(h / G), G = Hq / Hkv.
+ *
+ * parity unpinned: the pair layout (adjacent pairs) and the frequency
+ * convention are not fixed by any worked example on the pages; the pins in the
+ * tests fix them only as the reading above.
+ *
+ * Inputs are read exactly (fp32, or bf16 bit patterns widened to fp64);
+ * every intermediate is fp64; the softmax is two-pass.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define G4O_OK 0
+#define G4O_EINVAL (-1)
+#define G4O_ENOMEM (-2)
+
+/* element idx of an input array of dtype 0 (fp32) or 1 (bf16 bits) */
+static double g4o_in(const void* base, int dtype, size_t idx) {
+  if (dtype == 0) return (double)((const float*)base)[idx];
+  uint32_t bits = ((uint32_t)((const uint16_t*)base)[idx]) << 16;
+  float f;
+  memcpy(&f, &bits, sizeof f);
+  return (double)f;
+}
+
+/* Number of rotated pairs for rotated fraction p of a head of dim d. */
+int g4o_nrot(int d, double p) {
+  int n = (int)floor(p * (double)d / 2.0);
+  if (n < 0) n = 0;
+  if (n > d / 2) n = d / 2;
+  return n;
+}
+
+/* Angle of pair t at position pos: pos * theta^(-2t/d). */
+static double g4o_angle(double pos, int t, int d, double theta) {
+  return pos * pow(theta, -2.0 * (double)t / (double)d);
+}
+
+/* R(pos) applied in place to one head vector x[d] (p-RoPE section). */
+void g4o_rope(double* x, int d, int n_rot, double theta, double pos) {
+  for (int t = 0; t < n_rot; ++t) {
+    double a = g4o_angle(pos, t, d, theta);
+    double c = cos(a), s = sin(a);
+    double x0 = x[2 * t], x1 = x[2 * t + 1];
+    x[2 * t] = x0 * c - x1 * s;
+    x[2 * t + 1] = x0 * s + x1 * c;
+  }
+}
+
+/* First visible key of query index i (window 0 = unbounded). */
+static int64_t g4o_first_key(int64_t i, int window) {
+  if (window <= 0) return 0;
+  int64_t lo = i - window + 1;
+  return lo < 0 ? 0 : lo;
+}
+
+static int g4o_check(int B, int S, int Hq, int Hkv, int d, int window, double theta, double p) {
+  if (B < 0 || S < 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || (d & 1)) return G4O_EINVAL;
+  if (Hq % Hkv) return G4O_EINVAL;
+  if (window < 0 || !(theta > 0.0) || !(p >= 0.0 && p <= 1.0)) return G4O_EINVAL;
+  return G4O_OK;
+}
+
+/*
+ * Causal prefill attention.
+ *   q   [B, S, Hq,  d]     k, v [B, S, Hkv, d]   (k == v for the K=V layer)
+ *   pos [B, S] int32 positions (rotation only)
+ *   rows: NULL -> every row, out is [B, S, Hq, d];
+ *         else nrows flattened row ids b*S + i, out is [nrows, Hq, d].
+ * Returns 0, or a negative code for invalid arguments / out of memory.
+ */
+int g4o_prefill(const void* q, const void* k, const void* v, int dtype, const int32_t* pos,
+                int B, int S, int Hq, int Hkv, int d, int window, double theta, double p,
+                const int64_t* rows, int64_t nrows, double* out) {
+  int rc = g4o_check(B, S, Hq, Hkv, d, window, theta, p);
+  if (rc) return rc;
+  if (!q || !k || !v || !pos || !out || (dtype != 0 && dtype != 1)) return G4O_EINVAL;
+  const int G = Hq / Hkv;
+  const int n_rot = g4o_nrot(d, p);
+  const int64_t nr = rows ? nrows : (int64_t)B * S;
+  if (nr == 0) return G4O_OK;
+  for (int64_t r = 0; rows && r < nr; ++r)
+    if (rows[r] < 0 || rows[r] >= (int64_t)B * S) return G4O_EINVAL;
+
+  /* Cache of cos/sin of the key angles, per (b, j, pair): these depend only on
+   * the key's position, so each is evaluated once. */
+  const int64_t BS = (int64_t)B * S;
+  double* cs = NULL;
+  if (n_rot > 0) {
+    cs = (double*)malloc(sizeof(double) * 2 * (size_t)BS * (size_t)n_rot);
+    if (!cs) return G4O_ENOMEM;
+    /* Only keys some requested row can see: per batch row b, the span from
+     * the lowest first-visible key to the highest query index requested. */
+    int64_t* lo = (int64_t*)malloc(sizeof(int64_t) * (size_t)B);
+    int64_t* hi = (int64_t*)malloc(sizeof(int64_t) * (size_t)B);
+    if (!lo || !hi) { free(cs); free(lo); free(hi); return G4O_ENOMEM; }
+    for (int b = 0; b < B; ++b) { lo[b] = S; hi[b] = -1; }
+    for (int64_t r = 0; r < nr; ++r) {
+      int64_t row = rows ? rows[r] : r;
+      int64_t b = row / S, i = row % S, j0 = g4o_first_key(i, window);
+      if (j0 < lo[b]) lo[b] = j0;
+      if (i > hi[b]) hi[b] = i;
+    }
+#pragma omp parallel for schedule(static)
+    for (int64_t bj = 0; bj < BS; ++bj) {
+      const int64_t b = bj / S, j = bj % S;
+      if (j < lo[b] || j > hi[b]) continue;
+      double P = (double)pos[bj];
+      for (int t = 0; t < n_rot; ++t) {
+        double a = g4o_angle(P, t, d, theta);
+        cs[(bj * n_rot + t) * 2 + 0] = cos(a);
+        cs[(bj * n_rot + t) * 2 + 1] = sin(a);
+      }
+    }
+    free(lo);
+    free(hi);
+  }
+
+  const double scale = 1.0 / sqrt((double)d);
+  int err = 0;
+#pragma omp parallel
+  {
+    double* qr = (double*)malloc(sizeof(double) * (size_t)G * d);
+    double* kr = (double*)malloc(sizeof(double) * (size_t)d);
+    double* sc = (double*)malloc(sizeof(double) * (size_t)G * (S > 0 ? S : 1));
+    if (!qr || !kr || !sc) {
+#pragma omp atomic write
+      err = 1;
+    } else {
+#pragma omp for schedule(dynamic, 1)
+      for (int64_t task = 0; task < nr * Hkv; ++task) {
+        const int64_t r = task / Hkv;
+        const int g = (int)(task % Hkv);
+        const int64_t row = rows ? rows[r] : r;
+        const int64_t b = row / S, i = row % S;
+        const int64_t j0 = g4o_first_key(i, window);
+        const int64_t nk = i - j0 + 1;
+        /* rotated queries of the G heads that share KV head g */
+        for (int hh = 0; hh < G; ++hh) {
+          const int h = g * G + hh;
+          const size_t qoff = (((size_t)b * S + i) * Hq + h) * (size_t)d;
+          for (int e = 0; e < d; ++e) qr[hh * d + e] = g4o_in(q, dtype, qoff + e);
+          g4o_rope(qr + hh * d, d, n_rot, theta, (double)pos[b * S + i]);
+        }
+        /* scores s_j for every visible key */
+        for (int64_t jj = 0; jj < nk; ++jj) {
+          const int64_t j = j0 + jj;
+          const size_t koff = (((size_t)b * S + j) * Hkv + g) * (size_t)d;
+          for (int e = 0; e < d; ++e) kr[e] = g4o_in(k, dtype, koff + e);
+          const double* c = cs ? cs + ((size_t)(b * S + j) * n_rot) * 2 : NULL;
+          for (int t = 0; t < n_rot; ++t) {
+            double x0 = kr[2 * t], x1 = kr[2 * t + 1];
+            kr[2 * t] = x0 * c[2 * t] - x1 * c[2 * t + 1];
+            kr[2 * t + 1] = x0 * c[2 * t + 1] + x1 * c[2 * t];
+          }
+          for (int hh = 0; hh < G; ++hh) {
+            double s = 0.0;
+            for (int e = 0; e < d; ++e) s += qr[hh * d + e] * kr[e];
+            sc[(size_t)hh * nk + jj] = s * scale;
+          }
+        }
+        /* two-pass softmax and weighted sum of raw values */
+        for (int hh = 0; hh < G; ++hh) {
+          const int h = g * G + hh;
+          double* o = out + ((size_t)r * Hq + h) * (size_t)d;
+          double* srow = sc + (size_t)hh * nk;
+          double m = -INFINITY;
+          for (int64_t jj = 0; jj < nk; ++jj) if (srow[jj] > m) m = srow[jj];
+          double l = 0.0;
+          for (int64_t jj = 0; jj < nk; ++jj) { srow[jj] = exp(srow[jj] - m); l += srow[jj]; }
+          for (int e = 0; e < d; ++e) o[e] = 0.0;
+          for (int64_t jj = 0; jj < nk; ++jj) {
+            const size_t voff = (((size_t)b * S + j0 + jj) * Hkv + g) * (size_t)d;
+            const double w = srow[jj];
+            for (int e = 0; e < d; ++e) o[e] += w * g4o_in(v, dtype, voff + e);
+          }
+          for (int e = 0; e < d; ++e) o[e] /= l;
+        }
+      }
+    }
+    free(qr); free(kr); free(sc);
+  }
+  free(cs);
+  return err ? G4O_ENOMEM : G4O_OK;
+}
+
+/*
+ * Probability row of query (b, i, h) over all S keys (0 outside the mask).
+ * Debug output used by the tests: each row must sum to 1.
+ */
+int g4o_probs(const void* q, const void* k, int dtype, const int32_t* pos, int B, int S, int Hq,
+              int Hkv, int d, int window, double theta, double p, int b, int i, int h,
+              double* probs) {
+  int rc = g4o_check(B, S, Hq, Hkv, d, window, theta, p);
+  if (rc) return rc;
+  if (!q || !k || !pos || !probs || b < 0 || b >= B || i < 0 || i >= S || h < 0 || h >= Hq)
+    return G4O_EINVAL;
+  const int G = Hq / Hkv, g = h / G, n_rot = g4o_nrot(d, p);
+  double* qr = (double*)malloc(sizeof(double) * d);
+  double* kr = (double*)malloc(sizeof(double) * d);
+  if (!qr || !kr) { free(qr); free(kr); return G4O_ENOMEM; }
+  const size_t qoff = (((size_t)b * S + i) * Hq + h) * (size_t)d;
+  for (int e = 0; e < d; ++e) qr[e] = g4o_in(q, dtype, qoff + e);
+  g4o_rope(qr, d, n_rot, theta, (double)pos[(size_t)b * S + i]);
+  const int64_t j0 = g4o_first_key(i, window);
+  double m = -INFINITY;
+  for (int64_t j = 0; j < S; ++j) {
+    if (j < j0 || j > i) { probs[j] = -INFINITY; continue; }
+    const size_t koff = (((size_t)b * S + j) * Hkv + g) * (size_t)d;
+    for (int e = 0; e < d; ++e) kr[e] = g4o_in(k, dtype, koff + e);
+    g4o_rope(kr, d, n_rot, theta, (double)pos[(size_t)b * S + j]);
+    double s = 0.0;
+    for (int e = 0; e < d; ++e) s += qr[e] * kr[e];
+    probs[j] = s / sqrt((double)d);
+    if (probs[j] > m) m = probs[j];
+  }
+  double l = 0.0;
+  for (int64_t j = 0; j < S; ++j) {
+    probs[j] = (j < j0 || j > i) ? 0.0 : exp(probs[j] - m);
+    l += probs[j];
+  }
+  for (int64_t j = 0; j < S; ++j) probs[j] /= l;
+  free(qr); free(kr);
+  return G4O_OK;
+}
+
+/*
+ * Decode: one query token per sequence against a KV cache of raw (unrotated)
+ * keys/values.
+ *   q [B, Hq, d];  k_cache, v_cache [B, Hkv, capacity, d] (v_cache NULL: K=V);
+ *   pos [B]: position of the query token, whose own key is already cached.
+ *   window > 0: ring cache, capacity == window, position t lives in slot
+ *               t mod window; the query sees positions max(0, P-W+1) .. P.
+ *   window = 0: linear cache, row t holds position t; the query sees 0 .. P.
+ * A row whose position is negative, or beyond a linear cache, is all NaN.
+ * This is row P of the prefill over the sequence the cache holds.
+ */
+int g4o_decode(const void* q, const void* kc, const void* vc, int dtype, const int32_t* pos, int B,
+               int Hq, int Hkv, int d, int capacity, int window, double theta, double p,
+               double* out) {
+  int rc = g4o_check(B, 1, Hq, Hkv, d, window, theta, p);
+  if (rc) return rc;
+  if (!q || !kc || !pos || !out || capacity <= 0 || (dtype != 0 && dtype != 1)) return G4O_EINVAL;
+  if (window > 0 && capacity != window) return G4O_EINVAL;
+  if (!vc) vc = kc;
+  const int G = Hq / Hkv, n_rot = g4o_nrot(d, p);
+  const double scale = 1.0 / sqrt((double)d);
+  int err = 0;
+#pragma omp parallel
+  {
+    double* qr = (double*)malloc(sizeof(double) * (size_t)G * d);
+    double* kr = (double*)malloc(sizeof(double) * d);
+    double* sc = (double*)malloc(sizeof(double) * (size_t)G * (size_t)capacity);
+    if (!qr || !kr || !sc) {
+#pragma omp atomic write
+      err = 1;
+    } else {
+#pragma omp for schedule(dynamic, 1)
+      for (int64_t task = 0; task < (int64_t)B * Hkv; ++task) {
+        const int b = (int)(task / Hkv), g = (int)(task % Hkv);
+        const int64_t P = pos[b];
+        const int bad = P < 0 || (window == 0 && P >= capacity);
+        if (bad) {
+          for (int hh = 0; hh < G; ++hh)
+            for (int e = 0; e < d; ++e) out[((size_t)b * Hq + g * G + hh) * d + e] = NAN;
+          continue;
+        }
+        const int64_t t0 = g4o_first_key(P, window);
+        const int64_t nk = P - t0 + 1;
+        for (int hh = 0; hh < G; ++hh) {
+          const size_t qoff = ((size_t)b * Hq + g * G + hh) * (size_t)d;
+          for (int e = 0; e < d; ++e) qr[hh * d + e] = g4o_in(q, dtype, qoff + e);
+          g4o_rope(qr + hh * d, d, n_rot, theta, (double)P);
+        }
+        for (int64_t jj = 0; jj < nk; ++jj) {
+          const int64_t t = t0 + jj;
+          const int64_t slot = window > 0 ? t % window : t;
+          const size_t koff = (((size_t)b * Hkv + g) * capacity + slot) * (size_t)d;
+          for (int e = 0; e < d; ++e) kr[e] = g4o_in(kc, dtype, koff + e);
+          g4o_rope(kr, d, n_rot, theta, (double)t);
+          for (int hh = 0; hh < G; ++hh) {
+            double s = 0.0;
+            for (int e = 0; e < d; ++e) s += qr[hh * d + e] * kr[e];
+            sc[(size_t)hh * nk + jj] = s * scale;
+          }
+        }
+        for (int hh = 0; hh < G; ++hh) {
+          double* o = out + ((size_t)b * Hq + g * G + hh) * (size_t)d;
+          double* srow = sc + (size_t)hh * nk;
+          double m = -INFINITY;
+          for (int64_t jj = 0; jj < nk; ++jj) if (srow[jj] > m) m = srow[jj];
+          double l = 0.0;
+          for (int64_t jj = 0; jj < nk; ++jj) { srow[jj] = exp(srow[jj] - m); l += srow[jj]; }
+          for (int e = 0; e < d; ++e) o[e] = 0.0;
+          for (int64_t jj = 0; jj < nk; ++jj) {
+            const int64_t t = t0 + jj;
+            const int64_t slot = window > 0 ? t % window : t;
+            const size_t voff = (((size_t)b * Hkv + g) * capacity + slot) * (size_t)d;
+            for (int e = 0; e < d; ++e) o[e] += srow[jj] * g4o_in(vc, dtype, voff + e);
+          }
+          for (int e = 0; e < d; ++e) o[e] /= l;
+        }
+      }
+    }
+    free(qr); free(kr); free(sc);
+  }
+  return err ? G4O_ENOMEM : G4O_OK;
+}

@@ -1,0 +1,49 @@
+"""Dense brute-force attention in numpy (tiny shapes only): an independent
+formulation used to pin the oracle.
+
+Rotation is written with complex numbers (pair (x, y) -> (x + iy) * e^{i angle}),
+GQA by materialising repeated KV heads, the mask as an explicit boolean matrix and
+the softmax as a dense row operation.  Shares no code with ``oracle/``.
+"""
+import numpy as np
+
+
+def rotate(x, pos, theta, n_rot):
+    """x [..., S, H, d] float64, pos [..., S]: rotate pairs t < n_rot."""
+    d = x.shape[-1]
+    z = x[..., 0::2] + 1j * x[..., 1::2]
+    t = np.arange(d // 2)
+    freq = np.where(t < n_rot, np.power(float(theta), -2.0 * t / d), 0.0)
+    ph = np.exp(1j * pos[..., :, None, None].astype(np.float64) * freq)
+    z = z * ph
+    y = np.empty_like(x)
+    y[..., 0::2] = z.real
+    y[..., 1::2] = z.imag
+    return y
+
+
+def mask_matrix(S, window):
+    i = np.arange(S)[:, None]
+    j = np.arange(S)[None, :]
+    m = j <= i
+    if window > 0:
+        m &= (i - j) < window
+    return m
+
+
+def attention(q, k, v, pos, window, theta, n_rot):
+    """q [B,S,Hq,d], k/v [B,S,Hkv,d] float64; returns [B,S,Hq,d]."""
+    B, S, Hq, d = q.shape
+    Hkv = k.shape[2]
+    G = Hq // Hkv
+    qr = rotate(q, pos, theta, n_rot)
+    kr = rotate(k, pos, theta, n_rot)
+    kr = np.repeat(kr, G, axis=2)
+    vv = np.repeat(v, G, axis=2)
+    sc = np.einsum("bihd,bjhd->bhij", qr, kr) / np.sqrt(d)
+    m = mask_matrix(S, window)
+    sc = np.where(m[None, None], sc, -np.inf)
+    sc = sc - sc.max(axis=-1, keepdims=True)
+    w = np.exp(sc)
+    w = w / w.sum(axis=-1, keepdims=True)
+    return np.einsum("bhij,bjhd->bihd", w, vv)

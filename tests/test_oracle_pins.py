@@ -1,0 +1,347 @@
+"""Pins of the fp64 oracle against things other than itself (CPU only).
+
+- brute force: a dense numpy formulation (complex rotation, explicit mask matrix,
+  repeated KV heads) on tiny inputs, atol 1e-12;
+- closed forms: q = 0 gives the sliding-window mean of v; S = 1 gives v0;
+  hand-derived rotation angles (tests/golden/rope_hand.json);
+- library routine: p = 0 reduces to plain causal softmax attention, compared with
+  torch's scaled_dot_product_attention in float64;
+- invariants: W >= S equals W = 0; GQA equals MHA with repeated KV heads;
+  K=V equals the standard path fed v := k; p = 1 rotates every pair; the
+  rotation is orthogonal and additive in the position; outputs are invariant
+  under a common position shift; probability rows sum to 1 with exactly the
+  window's keys non-zero; decode equals the last prefill row; a ring cache
+  equals a linear one;
+- mutants: plausible mistakes planted in a copy of oracle.c must fail a pin.
+"""
+import json
+import math
+import os
+import shutil
+import subprocess
+
+import numpy as np
+import pytest
+
+import oracle
+from tests import brute
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def rnd(shape, seed, dtype=np.float32):
+    return np.random.default_rng(seed).standard_normal(shape).astype(dtype)
+
+
+def to_bf16_bits(x):
+    """Round-to-nearest-even float32 -> bf16 bit patterns (uint16)."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    r = ((u >> 16) & 1) + 0x7FFF
+    return ((u + r) >> 16).astype(np.uint16)
+
+
+def bf16_to_f64(bits):
+    return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+CASES = [
+    # B, S, Hq, Hkv, d, window, theta, p
+    (1, 9, 2, 1, 8, 0, 1e4, 1.0),
+    (2, 13, 4, 2, 16, 4, 1e4, 1.0),
+    (1, 17, 8, 1, 32, 0, 1e6, 0.25),
+    (2, 11, 4, 4, 8, 1, 1e4, 1.0),
+    (1, 12, 8, 2, 16, 5, 1e6, 0.5),
+    (1, 10, 2, 2, 8, 3, 1e4, 0.0),
+    (1, 16, 8, 1, 64, 7, 1e6, 0.25),
+]
+
+
+@pytest.mark.parametrize("case", CASES)
+@pytest.mark.parametrize("offset", [0, 1000])
+def test_brute_force_prefill(case, offset):
+    B, S, Hq, Hkv, d, W, theta, p = case
+    q, k, v = rnd((B, S, Hq, d), 1), rnd((B, S, Hkv, d), 2), rnd((B, S, Hkv, d), 3)
+    pos = (np.arange(S, dtype=np.int32) + offset)[None].repeat(B, 0)
+    got = oracle.prefill(q, k, v, pos, W, theta, p)
+    n_rot = int(math.floor(p * d / 2))
+    want = brute.attention(q.astype(np.float64), k.astype(np.float64), v.astype(np.float64),
+                           pos, W, theta, n_rot)
+    np.testing.assert_allclose(got, want, rtol=0, atol=1e-12)
+
+
+def test_brute_force_bf16_inputs_and_random_positions():
+    B, S, Hq, Hkv, d, W = 2, 15, 4, 2, 16, 6
+    q, k, v = (to_bf16_bits(rnd(s, i)) for i, s in enumerate([(B, S, Hq, d), (B, S, Hkv, d),
+                                                               (B, S, Hkv, d)]))
+    pos = np.random.default_rng(5).integers(0, 262144, size=(B, S)).astype(np.int32)
+    got = oracle.prefill(q, k, v, pos, W, 1e4, 1.0)
+    want = brute.attention(bf16_to_f64(q), bf16_to_f64(k), bf16_to_f64(v), pos, W, 1e4, d // 2)
+    np.testing.assert_allclose(got, want, rtol=0, atol=1e-11)
+
+
+def test_row_subset_matches_full():
+    B, S, Hq, Hkv, d, W = 2, 20, 4, 2, 16, 5
+    q, k, v = rnd((B, S, Hq, d), 7), rnd((B, S, Hkv, d), 8), rnd((B, S, Hkv, d), 9)
+    pos = np.arange(S, dtype=np.int32)[None].repeat(B, 0)
+    full = oracle.prefill(q, k, v, pos, W, 1e4, 1.0)
+    rows = np.array([0, 3, 19, 20, 27, 39])
+    sub = oracle.prefill(q, k, v, pos, W, 1e4, 1.0, rows=rows)
+    np.testing.assert_array_equal(sub, full.reshape(B * S, Hq, d)[rows])
+
+
+@pytest.mark.parametrize("W", [1, 2, 5, 0])
+def test_zero_query_gives_window_mean(W):
+    """q = 0 makes every visible score 0, so each output is the plain mean of
+    the visible values: a sliding-window mean, computed here with cumsum."""
+    B, S, Hq, Hkv, d = 1, 23, 4, 2, 8
+    q = np.zeros((B, S, Hq, d), np.float32)
+    k, v = rnd((B, S, Hkv, d), 11), rnd((B, S, Hkv, d), 12)
+    pos = np.arange(S, dtype=np.int32)[None]
+    got = oracle.prefill(q, k, v, pos, W, 1e4, 1.0)
+    c = np.concatenate([np.zeros((1, Hkv, d)), np.cumsum(v[0].astype(np.float64), axis=0)])
+    for i in range(S):
+        lo = 0 if W == 0 else max(0, i - W + 1)
+        mean = (c[i + 1] - c[lo]) / (i + 1 - lo)
+        for h in range(Hq):
+            np.testing.assert_allclose(got[0, i, h], mean[h // (Hq // Hkv)], rtol=0, atol=1e-12)
+
+
+def test_single_token_returns_v0():
+    q, k, v = rnd((3, 1, 8, 32), 1), rnd((3, 1, 1, 32), 2), rnd((3, 1, 1, 32), 3)
+    pos = np.array([[5], [0], [262143]], np.int32)
+    got = oracle.prefill(q, k, v, pos, 0, 1e6, 0.25)
+    np.testing.assert_array_equal(got, np.repeat(v.astype(np.float64), 8, axis=2))
+
+
+def test_window_at_least_seq_equals_global():
+    B, S, Hq, Hkv, d = 1, 19, 4, 2, 16
+    q, k, v = rnd((B, S, Hq, d), 21), rnd((B, S, Hkv, d), 22), rnd((B, S, Hkv, d), 23)
+    pos = np.arange(S, dtype=np.int32)[None]
+    g = oracle.prefill(q, k, v, pos, 0, 1e4, 1.0)
+    for W in (S, S + 1, 1000):
+        np.testing.assert_array_equal(oracle.prefill(q, k, v, pos, W, 1e4, 1.0), g)
+    assert not np.allclose(oracle.prefill(q, k, v, pos, S - 1, 1e4, 1.0), g)
+
+
+def test_gqa_equals_mha_with_repeated_heads():
+    B, S, Hq, Hkv, d, W = 2, 14, 8, 2, 16, 6
+    q, k, v = rnd((B, S, Hq, d), 31), rnd((B, S, Hkv, d), 32), rnd((B, S, Hkv, d), 33)
+    pos = np.arange(S, dtype=np.int32)[None].repeat(B, 0)
+    gqa = oracle.prefill(q, k, v, pos, W, 1e4, 1.0)
+    mha = oracle.prefill(q, np.repeat(k, 4, axis=2), np.repeat(v, 4, axis=2), pos, W, 1e4, 1.0)
+    np.testing.assert_allclose(gqa, mha, rtol=0, atol=1e-13)
+
+
+def test_k_equals_v_is_standard_attention_fed_v_is_k():
+    B, S, Hq, Hkv, d = 1, 16, 8, 1, 64
+    q, kv = rnd((B, S, Hq, d), 41), rnd((B, S, Hkv, d), 42)
+    pos = np.arange(S, dtype=np.int32)[None]
+    got = oracle.prefill(q, kv, kv, pos, 0, 1e6, 0.25)
+    want = brute.attention(q.astype(np.float64), kv.astype(np.float64), kv.astype(np.float64),
+                           pos, 0, 1e6, 8)
+    np.testing.assert_allclose(got, want, rtol=0, atol=1e-12)
+    # values are the raw tensor, not the rotated one
+    rot_v = brute.rotate(kv.astype(np.float64), pos, 1e6, 8)
+    wrong = brute.attention(q.astype(np.float64), kv.astype(np.float64), rot_v, pos, 0, 1e6, 8)
+    assert np.abs(got - wrong).max() > 1e-3
+
+
+@pytest.mark.parametrize("W", [0, 4])
+def test_p0_is_plain_causal_attention_library_routine(W):
+    torch = pytest.importorskip("torch")
+    B, S, Hq, Hkv, d = 2, 12, 4, 4, 16
+    q, k, v = rnd((B, S, Hq, d), 51), rnd((B, S, Hkv, d), 52), rnd((B, S, Hkv, d), 53)
+    pos = np.arange(S, dtype=np.int32)[None].repeat(B, 0) + 777
+    got = oracle.prefill(q, k, v, pos, W, 1e4, 0.0)
+    tq, tk, tv = (torch.from_numpy(x.astype(np.float64)).transpose(1, 2) for x in (q, k, v))
+    i = torch.arange(S)[:, None]
+    j = torch.arange(S)[None, :]
+    allowed = (j <= i) & (((i - j) < W) if W > 0 else torch.ones_like(j <= i))
+    ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=allowed)
+    np.testing.assert_allclose(got, ref.transpose(1, 2).numpy(), rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("p,n_rot", [(1.0, 8), (0.25, 2), (0.5, 4)])
+def test_p_rotates_exactly_the_first_pairs(p, n_rot):
+    """attention(q, k; p) == attention(R_p q, R_p k; p = 0), where R_p rotates the
+    first n_rot pairs in numpy: p = 1 is full RoPE, p = 0.25 the first quarter."""
+    B, S, Hq, Hkv, d = 1, 10, 2, 1, 16
+    q, k, v = rnd((B, S, Hq, d), 61), rnd((B, S, Hkv, d), 62), rnd((B, S, Hkv, d), 63)
+    pos = np.arange(S, dtype=np.int32)[None] + 3
+    got = oracle.prefill(q, k, v, pos, 0, 1e4, p)
+    qr = brute.rotate(q.astype(np.float64), pos, 1e4, n_rot).astype(np.float32)
+    kr = brute.rotate(k.astype(np.float64), pos, 1e4, n_rot).astype(np.float32)
+    # fp32 storage of the pre-rotated operands costs ~1e-7
+    np.testing.assert_allclose(got, oracle.prefill(qr, kr, v, pos, 0, 1e4, 0.0), atol=2e-6)
+    assert oracle.nrot(d, p) == n_rot
+
+
+def test_p0_is_identity_rotation():
+    x = rnd(64, 70).astype(np.float64)
+    np.testing.assert_array_equal(oracle.rope(x, 1e4, 0.0, 12345), x)
+
+
+def test_rotation_orthogonal_norm_preserving_and_additive():
+    d = 32
+    for p, theta in ((1.0, 1e4), (0.25, 1e6)):
+        R = np.stack([oracle.rope(np.eye(d)[c], theta, p, 977) for c in range(d)], axis=1)
+        np.testing.assert_allclose(R.T @ R, np.eye(d), atol=1e-14)
+        x = rnd(d, 71).astype(np.float64)
+        np.testing.assert_allclose(np.linalg.norm(R @ x), np.linalg.norm(x), rtol=1e-14)
+        # R(a) R(b) = R(a + b)
+        y = oracle.rope(oracle.rope(x, theta, p, 1234), theta, p, 4321)
+        np.testing.assert_allclose(y, oracle.rope(x, theta, p, 5555), atol=1e-11)
+
+
+def test_hand_derived_angles():
+    g = json.load(open(os.path.join(GOLDEN, "rope_hand.json")))
+    for c in g["cases"]:
+        d, t = c["d"], c["pair"]
+        x = np.zeros(d)
+        x[2 * t] = 1.0
+        y = oracle.rope(x, c["theta"], c["p"], c["pos"])
+        want = np.zeros(d)
+        want[2 * t] = math.cos(c["angle"])
+        want[2 * t + 1] = math.sin(c["angle"])
+        np.testing.assert_allclose(y, want, rtol=0, atol=1e-12, err_msg=str(c))
+        x = np.zeros(d)
+        x[2 * t + 1] = 1.0
+        y = oracle.rope(x, c["theta"], c["p"], c["pos"])
+        want = np.zeros(d)
+        want[2 * t] = -math.sin(c["angle"])
+        want[2 * t + 1] = math.cos(c["angle"])
+        np.testing.assert_allclose(y, want, rtol=0, atol=1e-12, err_msg=str(c))
+
+
+def test_relative_position_invariance():
+    B, S, Hq, Hkv, d, W = 1, 18, 4, 2, 32, 7
+    q, k, v = rnd((B, S, Hq, d), 81), rnd((B, S, Hkv, d), 82), rnd((B, S, Hkv, d), 83)
+    pos = np.arange(S, dtype=np.int32)[None]
+    a = oracle.prefill(q, k, v, pos, W, 1e4, 1.0)
+    b = oracle.prefill(q, k, v, pos + 200000, W, 1e4, 1.0)
+    np.testing.assert_allclose(a, b, rtol=0, atol=1e-9)
+
+
+def test_probability_rows_sum_to_one_over_the_window():
+    B, S, Hq, Hkv, d = 1, 30, 4, 2, 16
+    q, k = rnd((B, S, Hq, d), 91), rnd((B, S, Hkv, d), 92)
+    pos = np.arange(S, dtype=np.int32)[None]
+    for W in (0, 1, 4, 29):
+        for i in (0, 3, 4, 17, 29):
+            for h in (0, 3):
+                pr = oracle.probs(q, k, pos, W, 1e4, 1.0, 0, i, h)
+                assert abs(pr.sum() - 1.0) < 1e-14
+                lo = 0 if W == 0 else max(0, i - W + 1)
+                nz = np.nonzero(pr)[0]
+                assert nz.min() == lo and nz.max() == i and nz.size == i - lo + 1
+
+
+def _sequence(B, L, Hq, Hkv, d, seed):
+    return rnd((B, L, Hq, d), seed), rnd((B, L, Hkv, d), seed + 1), rnd((B, L, Hkv, d), seed + 2)
+
+
+def test_decode_linear_equals_last_prefill_row():
+    B, L, Hq, Hkv, d, C = 2, 21, 8, 1, 32, 40
+    q, k, _ = _sequence(B, L, Hq, Hkv, d, 100)
+    pos = np.arange(L, dtype=np.int32)[None].repeat(B, 0)
+    pre = oracle.prefill(q, k, k, pos, 0, 1e6, 0.25)
+    cache = np.full((B, Hkv, C, d), np.nan, np.float32)  # unread rows stay NaN
+    cache[:, :, :L] = k.transpose(0, 2, 1, 3)
+    out = oracle.decode(q[:, L - 1], cache, None, np.full(B, L - 1, np.int32), 0, 1e6, 0.25)
+    np.testing.assert_allclose(out, pre[:, L - 1], rtol=0, atol=1e-13)
+
+
+def test_decode_ring_equals_linear_and_prefill():
+    B, L, Hq, Hkv, d, W = 2, 29, 4, 2, 16, 8
+    q, k, v = _sequence(B, L, Hq, Hkv, d, 200)
+    pos = np.arange(L, dtype=np.int32)[None].repeat(B, 0)
+    pre = oracle.prefill(q, k, v, pos, W, 1e4, 1.0)
+    P = L - 1
+    ring_k = np.empty((B, Hkv, W, d), np.float32)
+    ring_v = np.empty((B, Hkv, W, d), np.float32)
+    for s in range(W):
+        t = P - ((P - s) % W)  # the position slot s holds
+        ring_k[:, :, s] = k[:, t]
+        ring_v[:, :, s] = v[:, t]
+    lin_k = np.ascontiguousarray(k.transpose(0, 2, 1, 3))
+    lin_v = np.ascontiguousarray(v.transpose(0, 2, 1, 3))
+    qP = q[:, P]
+    ring = oracle.decode(qP, ring_k, ring_v, np.full(B, P, np.int32), W, 1e4, 1.0)
+    np.testing.assert_allclose(ring, pre[:, P], rtol=0, atol=1e-13)
+    # linear cache with no window sees everything: equals the global prefill row
+    lin = oracle.decode(qP, lin_k, lin_v, np.full(B, P, np.int32), 0, 1e4, 1.0)
+    glob = oracle.prefill(q, k, v, pos, 0, 1e4, 1.0)
+    np.testing.assert_allclose(lin, glob[:, P], rtol=0, atol=1e-13)
+
+
+def test_decode_bad_positions_give_nan_rows():
+    B, Hq, Hkv, d, C = 3, 4, 2, 8, 10
+    q = rnd((B, Hq, d), 1)
+    kc = rnd((B, Hkv, C, d), 2)
+    out = oracle.decode(q, kc, None, np.array([-1, 10, 9], np.int32), 0, 1e4, 1.0)
+    assert np.isnan(out[0]).all() and np.isnan(out[1]).all() and np.isfinite(out[2]).all()
+
+
+def test_invalid_arguments_rejected():
+    q, k = rnd((1, 4, 3, 8), 1), rnd((1, 4, 2, 8), 2)
+    pos = np.arange(4, dtype=np.int32)[None]
+    with pytest.raises(ValueError):
+        oracle.prefill(q, k, k, pos, 0, 1e4, 1.0)  # Hq % Hkv != 0
+    q = rnd((1, 4, 2, 8), 1)
+    for W, theta, p in ((-1, 1e4, 1.0), (0, 0.0, 1.0), (0, 1e4, 1.5), (0, 1e4, -0.1)):
+        with pytest.raises(ValueError):
+            oracle.prefill(q, k, k, pos, W, theta, p)
+
+
+# --- mutants: plausible mistakes must fail a pin ---------------------------------
+
+MUTANTS = {
+    "rotation_sign": ("x[2 * t] = x0 * c - x1 * s;", "x[2 * t] = x0 * c + x1 * s;"),
+    "dropped_scale": ("sc[(size_t)hh * nk + jj] = s * scale;", "sc[(size_t)hh * nk + jj] = s;"),
+    "window_off_by_one": ("int64_t lo = i - window + 1;", "int64_t lo = i - window;"),
+    "gqa_mapping": ("const int h = g * G + hh;\n          const size_t qoff",
+                    "const int h = hh * Hkv + g;\n          const size_t qoff"),
+    "freq_over_rotated_dims": ("return pos * pow(theta, -2.0 * (double)t / (double)d);",
+                               "return pos * pow(theta, -2.0 * (double)t / (double)(d / 4));"),
+    "key_rotated_with_table_sign": ("kr[2 * t + 1] = x0 * c[2 * t + 1] + x1 * c[2 * t];",
+                                    "kr[2 * t + 1] = -x0 * c[2 * t + 1] + x1 * c[2 * t];"),
+    "rotated_values": ("o[e] += w * g4o_in(v, dtype, voff + e);", "o[e] += w * kr[e];"),
+}
+
+
+@pytest.fixture(scope="module")
+def mutant_dir(tmp_path_factory):
+    if shutil.which("gcc") is None:
+        pytest.skip("gcc not available")
+    return tmp_path_factory.mktemp("mutants")
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, mutant_dir):
+    src = open(os.path.join(os.path.dirname(oracle.__file__), "oracle.c")).read()
+    old, new = MUTANTS[name]
+    assert src.count(old) >= 1, name
+    path = mutant_dir / f"{name}.c"
+    path.write_text(src.replace(old, new, 1))
+    lib_path = mutant_dir / f"lib{name}.so"
+    subprocess.run(["gcc", "-O1", "-fopenmp", "-fPIC", "-shared", str(path), "-o", str(lib_path),
+                    "-lm"], check=True)
+    lib = oracle.load(str(lib_path))
+    # the brute-force pin over the prefill cases (one with G = 4, window, K=V)
+    B, S, Hq, Hkv, d, W, theta, p = 1, 12, 8, 2, 16, 5, 1e4, 1.0
+    q, k, v = rnd((B, S, Hq, d), 1), rnd((B, S, Hkv, d), 2), rnd((B, S, Hkv, d), 3)
+    pos = np.arange(S, dtype=np.int32)[None] + 11
+    got = oracle.prefill(q, k, v, pos, W, theta, p, lib=lib)
+    want = brute.attention(q.astype(np.float64), k.astype(np.float64), v.astype(np.float64),
+                           pos, W, theta, d // 2)
+    caught = not np.allclose(got, want, rtol=0, atol=1e-12)
+    # rotation mistakes that only touch oracle.rope are caught by the hand angles
+    x = np.zeros(8)
+    x[2] = 1.0
+    y = oracle.rope(x, 1e4, 1.0, 1, lib=lib)
+    caught |= not np.allclose(y[2:4], [math.cos(0.1), math.sin(0.1)], atol=1e-12)
+    x = np.zeros(8)
+    x[3] = 1.0
+    y = oracle.rope(x, 1e4, 1.0, 1, lib=lib)
+    caught |= not np.allclose(y[2:4], [-math.sin(0.1), math.cos(0.1)], atol=1e-12)
+    assert caught, f"mutant {name} survived the pins"
