@@ -1,0 +1,126 @@
+"""libg4attn: Gemma 4 interleaved attention (sliding-window local layers and
+K=V / p-RoPE global layers) on AMD MI355X (gfx950).
+
+Thin Python binding over the C ABI in include/g4attn.h.  It only checks and
+marshals torch tensors (device memory) and passes torch's current HIP stream;
+every step of the computation runs in the library's HIP kernels.  There is no
+CPU or PyTorch fallback: if the library is missing, calls raise.
+
+Layouts (contiguous): prefill q/out [B,S,Hq,d], k/v/kv [B,S,Hkv,d], pos [B,S]
+int32; decode q/out [B,Hq,d], caches [B,Hkv,capacity,d], pos [B] int32.
+"""
+from ._lib import lib as _g4lib
+
+F32, BF16 = 0, 1
+STATUS = {0: "G4A_OK", -1: "G4A_EINVAL", -2: "G4A_EUNSUPPORTED", -3: "G4A_EALIGN",
+          -4: "G4A_EWORKSPACE", -5: "G4A_EHIP"}
+
+
+class G4AttnError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        msg = _g4lib().g4attn_strerror(status).decode()
+        if status == -5:
+            msg += f" (hipError {_g4lib().g4attn_last_hip_error()})"
+        super().__init__(f"{where}: {STATUS.get(status, status)}: {msg}")
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _code(t):
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _dev(*ts):
+    for t in ts:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("tensors must live in GPU memory")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+
+
+def _ptr(t):
+    return t.data_ptr() if t is not None else None
+
+
+def _stream():
+    return _torch().cuda.current_stream().cuda_stream
+
+
+def _out(like_shape, out, out_dtype, device):
+    torch = _torch()
+    if out is not None:
+        return out
+    dt = torch.float32 if out_dtype in (None, F32, torch.float32) else torch.bfloat16
+    return torch.empty(like_shape, dtype=dt, device=device)
+
+
+def _check(rc, where):
+    if rc != 0:
+        raise G4AttnError(rc, where)
+
+
+def local_prefill(q, k, v, pos, window, theta=1e4, p=1.0, out=None, out_dtype=None):
+    """Causal sliding-window attention, separate K and V (g4attn_local_prefill)."""
+    _dev(q, k, v, pos, out)
+    B, S, Hq, d = q.shape
+    Hkv = k.shape[2]
+    out = _out((B, S, Hq, d), out, out_dtype, q.device)
+    rc = _g4lib().g4attn_local_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(pos), B, S, Hq,
+                                     Hkv, d, int(window), float(theta), float(p), _code(q),
+                                     _code(out), _stream())
+    _check(rc, "g4attn_local_prefill")
+    return out
+
+
+def global_prefill(q, kv, pos, window=0, theta=1e6, p=0.25, out=None, out_dtype=None):
+    """Causal attention with keys identical to values (g4attn_global_prefill)."""
+    _dev(q, kv, pos, out)
+    B, S, Hq, d = q.shape
+    Hkv = kv.shape[2]
+    out = _out((B, S, Hq, d), out, out_dtype, q.device)
+    rc = _g4lib().g4attn_global_prefill(_ptr(q), _ptr(kv), _ptr(out), _ptr(pos), B, S, Hq, Hkv, d,
+                                      int(window), float(theta), float(p), _code(q), _code(out),
+                                      _stream())
+    _check(rc, "g4attn_global_prefill")
+    return out
+
+
+def decode_workspace_bytes(B, Hq, Hkv, d, capacity, window):
+    return int(_g4lib().g4attn_decode_workspace_bytes(B, Hq, Hkv, d, capacity, window))
+
+
+def decode(q, k_cache, v_cache, pos, window, theta, p, out=None, workspace=None,
+           out_dtype=None):
+    """One query token per sequence against a raw KV cache (g4attn_decode).
+
+    v_cache None means K=V; window > 0 is a ring cache of `window` slots.
+    """
+    torch = _torch()
+    _dev(q, k_cache, v_cache, pos, out, workspace)
+    B, Hq, d = q.shape
+    _, Hkv, C, _ = k_cache.shape
+    out = _out((B, Hq, d), out, out_dtype, q.device)
+    need = decode_workspace_bytes(B, Hq, Hkv, d, C, window)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    nbytes = workspace.numel() * workspace.element_size()
+    rc = _g4lib().g4attn_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out), _ptr(pos), B, Hq,
+                              Hkv, d, C, int(window), float(theta), float(p), _code(q),
+                              _code(out), _ptr(workspace), nbytes, _stream())
+    _check(rc, "g4attn_decode")
+    return out
+
+
+def strerror(status):
+    return _g4lib().g4attn_strerror(int(status)).decode()

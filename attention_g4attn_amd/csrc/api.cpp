@@ -1,0 +1,168 @@
+// C ABI of libg4attn: argument validation and dispatch to the gfx950 kernels.
+// Every check runs on the host before anything is launched; the library keeps
+// no state between calls apart from a per-thread copy of the last launch
+// error.  See include/g4attn.h for the contract of each call.
+#include "../../include/g4attn.h"
+
+#include <math.h>
+
+#include "kernels.hpp"
+
+#define G4A_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
+
+bool valid_group(int G) { return G == 1 || G == 2 || G == 4 || G == 8; }
+
+// n_rot = floor(p * d / 2), the number of rotated pairs
+int rotated_pairs(int d, float p) {
+  int n = (int)floor((double)p * (double)d / 2.0);
+  if (n < 0) n = 0;
+  if (n > d / 2) n = d / 2;
+  return n;
+}
+
+// Shared checks of head layout, rotary parameters and dtypes.
+int check_common(int Hq, int Hkv, int d, int window, float theta, float p, int in_dtype,
+                 int out_dtype) {
+  if (Hq <= 0 || Hkv <= 0 || d <= 0 || (d & 1) || window < 0) return G4A_EINVAL;
+  if (Hq % Hkv) return G4A_EINVAL;
+  if (!(theta > 0.f) || isinf(theta)) return G4A_EINVAL;
+  if (!(p >= 0.f && p <= 1.f)) return G4A_EINVAL;
+  if ((in_dtype != G4A_F32 && in_dtype != G4A_BF16) ||
+      (out_dtype != G4A_F32 && out_dtype != G4A_BF16))
+    return G4A_EINVAL;
+  if (in_dtype == G4A_F32 && out_dtype != G4A_F32) return G4A_EUNSUPPORTED;
+  if (!valid_group(Hq / Hkv)) return G4A_EUNSUPPORTED;
+  if (in_dtype == G4A_BF16 && d != 256 && d != 512) return G4A_EUNSUPPORTED;
+  if (in_dtype == G4A_F32 && d != 64 && d != 128 && d != 256 && d != 512) return G4A_EUNSUPPORTED;
+  return G4A_OK;
+}
+
+int finish(hipError_t e) {
+  if (e == hipSuccess) return G4A_OK;
+  g_last_hip_error = (int)e;
+  return G4A_EHIP;
+}
+
+int prefill(const void* q, const void* k, const void* v, void* out, const int32_t* pos, int B,
+            int S, int Hq, int Hkv, int d, int window, float theta, float p, int in_dtype,
+            int out_dtype, void* stream, bool kv_shared) {
+  if (B < 0 || S < 0) return G4A_EINVAL;
+  int rc = check_common(Hq, Hkv, d, window, theta, p, in_dtype, out_dtype);
+  if (rc) return rc;
+  if (B == 0 || S == 0) return G4A_OK;
+  if (!q || !k || !v || !out || !pos) return G4A_EINVAL;
+  if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(out) || misaligned(pos))
+    return G4A_EALIGN;
+  // element counts must stay addressable; the grid must fit in 2^31 workgroups
+  if ((double)B * S * Hq * d > 9.0e18 || (double)B * S * Hkv > 2.0e9) return G4A_EINVAL;
+  g4a::PrefillArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.out = out;
+  a.pos = pos;
+  a.B = B;
+  a.S = S;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.D = d;
+  a.window = window;
+  a.n_rot = rotated_pairs(d, p);
+  a.log2_theta = log2((double)theta);
+  a.scale = (float)(1.0 / sqrt((double)d));
+  a.scale_log2e = (float)(1.4426950408889634 / sqrt((double)d));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (in_dtype == G4A_F32) return finish(g4a::launch_prefill_f32(a, st));
+  return finish(g4a::launch_prefill_bf16(a, kv_shared, out_dtype == G4A_BF16, st));
+}
+
+}  // namespace
+
+G4A_API int g4attn_local_prefill(const void* q, const void* k, const void* v, void* out,
+                                 const int32_t* pos, int B, int S, int Hq, int Hkv, int d,
+                                 int window, float theta, float p, int in_dtype, int out_dtype,
+                                 void* stream) {
+  return prefill(q, k, v, out, pos, B, S, Hq, Hkv, d, window, theta, p, in_dtype, out_dtype,
+                 stream, k == v);
+}
+
+G4A_API int g4attn_global_prefill(const void* q, const void* kv, void* out, const int32_t* pos,
+                                  int B, int S, int Hq, int Hkv, int d, int window, float theta,
+                                  float p, int in_dtype, int out_dtype, void* stream) {
+  return prefill(q, kv, kv, out, pos, B, S, Hq, Hkv, d, window, theta, p, in_dtype, out_dtype,
+                 stream, true);
+}
+
+G4A_API size_t g4attn_decode_workspace_bytes(int B, int Hq, int Hkv, int d, int capacity,
+                                             int window) {
+  if (B < 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || capacity <= 0 || window < 0) return 0;
+  if (window > 0 && capacity != window) return 0;
+  const size_t nch = (size_t)g4a::decode_num_chunks(d, capacity, window, false);
+  const size_t bytes = (size_t)B * Hq * nch * ((size_t)d + 2) * sizeof(float);
+  return bytes > 0 ? bytes : 16;
+}
+
+G4A_API int g4attn_decode(const void* q, const void* k_cache, const void* v_cache, void* out,
+                          const int32_t* pos, int B, int Hq, int Hkv, int d, int capacity,
+                          int window, float theta, float p, int in_dtype, int out_dtype,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  if (B < 0 || capacity <= 0) return G4A_EINVAL;
+  if (window > 0 && capacity != window) return G4A_EINVAL;
+  int rc = check_common(Hq, Hkv, d, window, theta, p, in_dtype, out_dtype);
+  if (rc) return rc;
+  if (B == 0) return G4A_OK;
+  if (!q || !k_cache || !out || !pos) return G4A_EINVAL;
+  if (misaligned(q) || misaligned(k_cache) || (v_cache && misaligned(v_cache)) ||
+      misaligned(out) || misaligned(pos))
+    return G4A_EALIGN;
+  if ((double)B * Hkv * capacity * d > 9.0e18) return G4A_EINVAL;
+  const bool f32 = in_dtype == G4A_F32;
+  g4a::DecodeArgs a{};
+  a.q = q;
+  a.k = k_cache;
+  a.v = v_cache ? v_cache : k_cache;
+  a.out = out;
+  a.pos = pos;
+  a.B = B;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.D = d;
+  a.capacity = capacity;
+  a.window = window;
+  a.n_rot = rotated_pairs(d, p);
+  a.log2_theta = log2((double)theta);
+  a.scale = (float)(1.0 / sqrt((double)d));
+  a.scale_log2e = (float)(1.4426950408889634 / sqrt((double)d));
+  a.chunk = g4a::decode_chunk_rows(d, capacity, window, f32);
+  a.nchunk = g4a::decode_num_chunks(d, capacity, window, f32);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (f32) return finish(g4a::launch_decode_f32(a, st));
+  const size_t need = g4attn_decode_workspace_bytes(B, Hq, Hkv, d, capacity, window);
+  if (!workspace || workspace_bytes < need) return G4A_EWORKSPACE;
+  if (misaligned(workspace)) return G4A_EALIGN;
+  if ((double)B * Hkv * a.nchunk > 2.0e9) return G4A_EINVAL;
+  a.part_o = static_cast<float*>(workspace);
+  a.part_ml = a.part_o + (size_t)B * Hq * a.nchunk * d;
+  return finish(g4a::launch_decode_bf16(a, v_cache == nullptr || v_cache == k_cache,
+                                        out_dtype == G4A_BF16, st));
+}
+
+G4A_API const char* g4attn_strerror(int status) {
+  switch (status) {
+    case G4A_OK: return "ok";
+    case G4A_EINVAL: return "invalid argument";
+    case G4A_EUNSUPPORTED: return "unsupported head dim, group size or dtype pair";
+    case G4A_EALIGN: return "tensor pointer not 16-byte aligned";
+    case G4A_EWORKSPACE: return "decode workspace missing or too small";
+    case G4A_EHIP: return "HIP launch failed (see g4attn_last_hip_error)";
+  }
+  return "unknown status";
+}
+
+G4A_API int g4attn_last_hip_error(void) { return g_last_hip_error; }

@@ -1,0 +1,54 @@
+// Launch entry points of the gfx950 kernels, called by the C ABI layer (api.cpp)
+// after it has validated every argument.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace g4a {
+
+struct PrefillArgs {
+  const void* q;
+  const void* k;
+  const void* v;  // equals k for the K=V layer
+  void* out;
+  const int32_t* pos;
+  int B, S, Hq, Hkv, D, window, n_rot;
+  double log2_theta;
+  float scale_log2e;  // log2(e) / sqrt(D)
+  float scale;        // 1 / sqrt(D)
+  int nq, nheads;     // filled in by the launcher
+};
+
+struct DecodeArgs {
+  const void* q;
+  const void* k;
+  const void* v;  // equals k for K=V
+  void* out;
+  const int32_t* pos;
+  int B, Hq, Hkv, D, capacity, window, n_rot;
+  double log2_theta;
+  float scale_log2e;
+  float scale;
+  int chunk;    // cache rows per workgroup
+  int nchunk;   // chunks per (b, kv head)
+  float* part_o;   // [B, Hq, nchunk, D]
+  float* part_ml;  // [B, Hq, nchunk, 2]
+};
+
+// bf16 inputs, matrix-core path; D in {256, 512}, G in {1, 2, 4, 8}
+hipError_t launch_prefill_bf16(const PrefillArgs& a, bool kv_shared, bool out_bf16,
+                               hipStream_t st);
+// f32 inputs, fp32 vector path; D in {64, 128, 256, 512}, G in {1, 2, 4, 8}
+hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t st);
+
+// split + merge decode
+hipError_t launch_decode_bf16(const DecodeArgs& a, bool kv_shared, bool out_bf16,
+                              hipStream_t st);
+hipError_t launch_decode_f32(const DecodeArgs& a, hipStream_t st);
+
+// rows of the cache one decode workgroup covers, and chunks per (b, kv head)
+int decode_chunk_rows(int D, int capacity, int window, bool f32);
+int decode_num_chunks(int D, int capacity, int window, bool f32);
+
+}  // namespace g4a

@@ -1,0 +1,122 @@
+"""Seeded synthetic inputs and workload shapes.
+
+Shared by the tests, the benchmark and the oracle side alike; holds none of
+the attention arithmetic.  Every tensor is N(0, 1) drawn with a torch.Generator
+on the device that will hold it, seeded 1000*workload + 10*layer + tensor
+(q = 1, k or kv = 2, v = 3), then rounded to the input dtype.  Positions are
+0..S-1.  The shapes follow the layer geometry the pages give for Gemma 4:
+local layers with a 512/1024 window, 2 query heads per KV head and head dim
+256; global layers with 8 query heads per KV head, head dim 512, K=V and
+p = 0.25 ("Guia visual do Gemma 4", sections "Intercalacao de camadas de
+atencao", "GQA", "Tecnica K=V", "p-RoPE"; techtoday page, attention section);
+contexts up to 256K ("Visao geral do modelo Gemma 4", section "Recursos").
+"""
+from dataclasses import dataclass
+
+import torch
+
+LOCAL_THETA, GLOBAL_THETA = 1.0e4, 1.0e6
+
+
+@dataclass(frozen=True)
+class Layer:
+    kind: str  # "local" (separate K, V) or "global" (K = V)
+    B: int
+    S: int
+    Hq: int
+    Hkv: int
+    d: int
+    window: int
+    theta: float
+    p: float
+
+
+def local(B, S, Hq=16, Hkv=8, d=256, window=1024):
+    return Layer("local", B, S, Hq, Hkv, d, window, LOCAL_THETA, 1.0)
+
+
+def global_(B, S, Hq=16, Hkv=2, d=512):
+    return Layer("global", B, S, Hq, Hkv, d, 0, GLOBAL_THETA, 0.25)
+
+
+# Workloads (sizes of one GPU's share at the model's real shapes).
+TINY_LOCAL = Layer("local", 1, 128, 4, 2, 256, 32, LOCAL_THETA, 1.0)  # fp32 inputs
+TINY_GLOBAL = Layer("global", 1, 128, 8, 1, 512, 0, GLOBAL_THETA, 0.25)  # fp32 inputs
+LOCAL_PREFILL = local(4, 8192)                                        # bf16
+GLOBAL_PREFILL = Layer("global", 1, 32768, 32, 4, 512, 0, GLOBAL_THETA, 0.25)
+GROUP_S = 262144
+GROUP_LOCAL = local(1, GROUP_S)      # x5 per group
+GROUP_GLOBAL = global_(1, GROUP_S)   # x1 per group
+
+
+@dataclass(frozen=True)
+class DecodeLayer:
+    kind: str
+    B: int
+    Hq: int
+    Hkv: int
+    d: int
+    capacity: int
+    window: int  # > 0: ring cache of `window` slots
+    theta: float
+    p: float
+
+
+DECODE_LOCAL = DecodeLayer("local", 64, 16, 8, 256, 512, 512, LOCAL_THETA, 1.0)
+DECODE_GLOBAL = DecodeLayer("global", 64, 16, 2, 512, 65536, 0, GLOBAL_THETA, 0.25)
+DECODE_LEN_RANGE = (4096, 65536)  # cache lengths, uniform, inclusive
+
+
+def seed(workload, layer, tensor):
+    return 1000 * workload + 10 * layer + tensor
+
+
+def randn(shape, seed_, dtype, device):
+    g = torch.Generator(device=device)
+    g.manual_seed(seed_)
+    return torch.randn(shape, generator=g, device=device, dtype=torch.float32).to(dtype)
+
+
+def positions(B, S, device, offset=0):
+    return (torch.arange(S, dtype=torch.int32, device=device) + offset).repeat(B, 1).contiguous()
+
+
+def prefill_inputs(layer: Layer, workload, index, dtype, device, offset=0):
+    """q, k, v (v is k for a global layer), pos."""
+    q = randn((layer.B, layer.S, layer.Hq, layer.d), seed(workload, index, 1), dtype, device)
+    k = randn((layer.B, layer.S, layer.Hkv, layer.d), seed(workload, index, 2), dtype, device)
+    v = k if layer.kind == "global" else randn((layer.B, layer.S, layer.Hkv, layer.d),
+                                               seed(workload, index, 3), dtype, device)
+    return q, k, v, positions(layer.B, layer.S, device, offset)
+
+
+def decode_lengths(B, seed_=4009, lo=DECODE_LEN_RANGE[0], hi=DECODE_LEN_RANGE[1]):
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed_)
+    return torch.randint(lo, hi + 1, (B,), generator=g, dtype=torch.int64)
+
+
+def decode_inputs(layer: DecodeLayer, workload, index, dtype, device, lengths=None):
+    """q [B,Hq,d], k_cache, v_cache (None for K=V), pos [B] int32, lengths [B].
+
+    Ring caches are full: every slot holds a token.  A linear cache holds
+    lengths[b] tokens; the rows beyond are filled with NaN, which the kernels
+    must never read.  The query token is the last cached one: pos = length - 1.
+    """
+    B = layer.B
+    if lengths is None:
+        lengths = decode_lengths(B)
+    lengths = lengths.to(torch.int64)
+    q = randn((B, layer.Hq, layer.d), seed(workload, index, 1), dtype, device)
+    shape = (B, layer.Hkv, layer.capacity, layer.d)
+    k = torch.empty(shape, dtype=dtype, device=device)
+    v = None if layer.kind == "global" else torch.empty(shape, dtype=dtype, device=device)
+    for b in range(B):  # per-sequence draws keep the temporary small
+        k[b] = randn(shape[1:], seed(workload, index, 2) * 100003 + b, dtype, device)
+        if v is not None:
+            v[b] = randn(shape[1:], seed(workload, index, 3) * 100003 + b, dtype, device)
+        if layer.window == 0:
+            L = int(lengths[b])
+            k[b, :, L:] = float("nan")
+    pos = (lengths - 1).to(torch.int32).to(device)
+    return q, k, v, pos, lengths

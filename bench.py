@@ -1,0 +1,282 @@
+#!/usr/bin/env python3
+"""Benchmark of the Gemma 4 interleaved attention block on one MI355X.
+
+One step = the whole hot path once over synthetic, seeded bf16 inputs already
+resident in HBM:
+  - prefill of one 5:1 interleave group at long context (B=1, S=262144):
+    5 sliding-window local layers (Hq=16, Hkv=8, d=256, window 1024, full
+    RoPE) then 1 global layer (Hq=16, Hkv=2, d=512, K=V, p-RoPE p=0.25);
+  - one decode step of the same 5:1 group for a batch of 64 sequences with
+    cache lengths uniform in [4096, 65536]: 5 local layers (Hq=16, Hkv=8,
+    d=256, 512-slot ring cache) then 1 global layer (Hq=16, Hkv=2, d=512, K=V
+    linear cache).
+value = algorithmic attention FLOPs of the step / step time (TFLOP/s); only
+(query, key) pairs the mask keeps are counted.  Per-kind times come from HIP
+events recorded on the stream the kernels run on.  Prints one JSON line.
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E peak
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target CPU time of the oracle baseline sample")
+    ap.add_argument("--only", choices=["all", "local", "global", "decode"], default="all",
+                    help="restrict the step to one kernel kind (profiling runs)")
+    ap.add_argument("--seq", type=int, default=None, help="override the prefill length")
+    return ap.parse_args()
+
+
+def prefill_flops(layer):
+    """4 * d * Hq * B * sum_i n_i, n_i = keys row i sees."""
+    S, W = layer.S, layer.window
+    if W == 0 or W >= S:
+        pairs = S * (S + 1) // 2
+    else:
+        pairs = W * (W + 1) // 2 + (S - W) * W
+    return 4.0 * layer.d * layer.Hq * layer.B * pairs
+
+
+def decode_cost(layer, lengths):
+    """(FLOPs, bytes): cache rows read once (K and V, or one tensor for K=V),
+    plus q and out."""
+    n = [min(int(L), layer.window) if layer.window > 0 else int(L) for L in lengths]
+    rows = sum(n)
+    tensors = 1 if layer.kind == "global" else 2
+    byts = rows * layer.Hkv * layer.d * 2 * tensors + layer.B * layer.Hq * layer.d * (2 + 4)
+    flops = 4.0 * layer.d * sum(n) * layer.Hq
+    return flops, byts
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; "
+                          "sharding across GPUs is not implemented", "n_gpus": args.gpus}))
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import attention_g4attn_amd as g4
+    from attention_g4attn_amd import inputs
+
+    dev = "cuda"
+    torch.cuda.set_device(0)
+    S = args.seq or inputs.GROUP_S
+    loc = inputs.local(1, S)
+    glo = inputs.global_(1, S)
+    dloc, dglo = inputs.DECODE_LOCAL, inputs.DECODE_GLOBAL
+    lengths = inputs.decode_lengths(dloc.B)
+    bf = torch.bfloat16
+    run_local = args.only in ("all", "local")
+    run_global = args.only in ("all", "global")
+    run_decode = args.only in ("all", "decode")
+
+    t_setup = time.time()
+    L_in = [inputs.prefill_inputs(loc, 5, i, bf, dev) for i in range(5)] if run_local else []
+    L_out = [torch.empty((1, S, loc.Hq, loc.d), dtype=torch.float32, device=dev) for _ in L_in]
+    G_in = inputs.prefill_inputs(glo, 5, 5, bf, dev) if run_global else None
+    G_out = torch.empty((1, S, glo.Hq, glo.d), dtype=torch.float32, device=dev) if run_global else None
+    D_loc = [inputs.decode_inputs(dloc, 4, i, bf, dev, lengths) for i in range(5)] if run_decode else []
+    D_glo = inputs.decode_inputs(dglo, 4, 5, bf, dev, lengths) if run_decode else None
+    D_out_l = [torch.empty((dloc.B, dloc.Hq, dloc.d), dtype=torch.float32, device=dev) for _ in D_loc]
+    D_out_g = torch.empty((dglo.B, dglo.Hq, dglo.d), dtype=torch.float32, device=dev) if run_decode else None
+    ws_l = torch.empty(g4.decode_workspace_bytes(dloc.B, dloc.Hq, dloc.Hkv, dloc.d, dloc.capacity,
+                                                 dloc.window), dtype=torch.uint8, device=dev)
+    ws_g = torch.empty(g4.decode_workspace_bytes(dglo.B, dglo.Hq, dglo.Hkv, dglo.d, dglo.capacity,
+                                                 dglo.window), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    print(f"# setup {time.time() - t_setup:.1f}s", file=sys.stderr, flush=True)
+
+    stream = torch.cuda.current_stream()
+    kinds = ["local_prefill", "global_prefill", "local_decode", "global_decode"]
+
+    def step(record):
+        ev = []
+        def mark():
+            if record:
+                e = torch.cuda.Event(enable_timing=True)
+                e.record(stream)
+                ev.append(e)
+        for (q, k, v, pos), out in zip(L_in, L_out):
+            mark()
+            g4.local_prefill(q, k, v, pos, loc.window, loc.theta, loc.p, out=out)
+            mark()
+        if G_in is not None:
+            q, kv, _, pos = G_in
+            mark()
+            g4.global_prefill(q, kv, pos, 0, glo.theta, glo.p, out=G_out)
+            mark()
+        for (q, kc, vc, pos, _), out in zip(D_loc, D_out_l):
+            mark()
+            g4.decode(q, kc, vc, pos, dloc.window, dloc.theta, dloc.p, out=out, workspace=ws_l)
+            mark()
+        if D_glo is not None:
+            q, kc, _, pos, _ = D_glo
+            mark()
+            g4.decode(q, kc, None, pos, 0, dglo.theta, dglo.p, out=D_out_g, workspace=ws_g)
+            mark()
+        return ev
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    per_kind = {k: [] for k in kinds}
+    t0 = time.perf_counter()
+    all_ev = []
+    for _ in range(args.steps):
+        all_ev.append(step(True))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    for ev in all_ev:
+        pairs = [ev[i].elapsed_time(ev[i + 1]) for i in range(0, len(ev), 2)]
+        it = iter(pairs)
+        for _ in L_in:
+            per_kind["local_prefill"].append(next(it))
+        if G_in is not None:
+            per_kind["global_prefill"].append(next(it))
+        for _ in D_loc:
+            per_kind["local_decode"].append(next(it))
+        if D_glo is not None:
+            per_kind["global_decode"].append(next(it))
+    print(f"# timed {args.steps} steps in {wall:.2f}s", file=sys.stderr, flush=True)
+
+    fl_loc, fl_glo = prefill_flops(loc), prefill_flops(glo)
+    (fdl, bdl), (fdg, bdg) = decode_cost(dloc, lengths), decode_cost(dglo, lengths)
+    step_flops = 5 * fl_loc * run_local + fl_glo * run_global + (5 * fdl + fdg) * run_decode
+    ms_step = wall * 1e3 / args.steps
+
+    def mean(x):
+        return float(np.mean(x)) if x else None
+
+    kind_rep = {}
+    if run_local:
+        t = mean(per_kind["local_prefill"])
+        kind_rep["local_prefill"] = {"ms": t, "tflops": fl_loc / t / 1e9,
+                                     "frac_mfma": fl_loc / t / 1e9 / MFMA_BF16_PEAK_TFLOPS}
+    if run_global:
+        t = mean(per_kind["global_prefill"])
+        kind_rep["global_prefill"] = {"ms": t, "tflops": fl_glo / t / 1e9,
+                                      "frac_mfma": fl_glo / t / 1e9 / MFMA_BF16_PEAK_TFLOPS}
+    if run_decode:
+        tl, tg = mean(per_kind["local_decode"]), mean(per_kind["global_decode"])
+        kind_rep["local_decode"] = {"us": tl * 1e3, "GBps": bdl / tl / 1e6,
+                                    "frac_hbm": bdl / tl / 1e6 / HBM_PEAK_GBS,
+                                    "tok_per_s": dloc.B / tl * 1e3}
+        kind_rep["global_decode"] = {"us": tg * 1e3, "GBps": bdg / tg / 1e6,
+                                     "frac_hbm": bdg / tg / 1e6 / HBM_PEAK_GBS,
+                                     "tok_per_s": dglo.B / tg * 1e3}
+        kind_rep["group_decode_tok_per_s"] = dloc.B / (5 * tl + tg) * 1e3
+
+    roof = None
+    if run_global:
+        t = mean(per_kind["global_prefill"])
+        ach = fl_glo / t / 1e9
+        roof = {"bound": "mfma", "achieved": ach, "peak": MFMA_BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": ach / MFMA_BF16_PEAK_TFLOPS, "traffic": None,
+                "kernel": "prefill_bf16_kernel<512,8,KV=V>", "flops_per_launch": fl_glo}
+    roof_dec = None
+    if run_decode:
+        tg = mean(per_kind["global_decode"])
+        ach = bdg / tg / 1e6
+        roof_dec = {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": ach / HBM_PEAK_GBS, "bytes_per_launch": bdg,
+                    "kernel": "decode_split_kernel<512,8,KV=V> + merge"}
+
+    cpu = None
+    if not args.no_cpu_baseline and run_global and run_local:
+        cpu = cpu_baseline(args, loc, glo, L_in[0], G_in, L_out[0], G_out)
+
+    rec = {
+        "metric": "attention TFLOP/s (prefill) + decode tok/s, as % of MFMA / HBM roofline",
+        "value": step_flops / (ms_step * 1e-3) / 1e12,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"gemma4 5:1 interleave group prefill S={S} (5 local W=1024 "
+                               f"Hq16/Hkv8/d256 + 1 global K=V p=0.25 Hq16/Hkv2/d512) + "
+                               f"batch-64 decode of the group (cache 4096..65536)",
+                   "global_batch": 1, "seq_len": S, "parallelism": "none (1 GPU)",
+                   "only": args.only},
+        "kinds": kind_rep,
+        "roofline": roof,
+        "roofline_decode": roof_dec,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+def cpu_baseline(args, loc, glo, L0, G0, Lout, Gout):
+    """The fp64 oracle, untuned, on a bounded sample of rows of the same
+    workload (first local layer and the global layer); also reports the
+    parity of those rows against the GPU outputs of the run."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from tests.helpers import to_oracle
+
+    S = loc.S
+    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    qg, kvg, _, posg = G0
+    ql, kl, vl, posl = L0
+    t0 = time.time()
+    kvg_h, kl_h, vl_h = to_oracle(kvg), to_oracle(kl), to_oracle(vl)
+    posg_h, posl_h = posg.cpu().numpy(), posl.cpu().numpy()
+    qg_h, ql_h = to_oracle(qg), to_oracle(ql)
+    print(f"# host copies {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+
+    def run(rows_g, rows_l):
+        t = time.time()
+        og = oracle.prefill(qg_h, kvg_h, kvg_h, posg_h, 0, glo.theta, glo.p, rows=rows_g)
+        ol = oracle.prefill(ql_h, kl_h, vl_h, posl_h, loc.window, loc.theta, loc.p, rows=rows_l)
+        return time.time() - t, og, ol
+
+    def flops(rows_g, rows_l):
+        f = sum(4.0 * glo.d * glo.Hq * (int(r) + 1) for r in rows_g)
+        f += sum(4.0 * loc.d * loc.Hq * min(int(r) + 1, loc.window) for r in rows_l)
+        return f
+
+    rng = np.random.default_rng(7)
+    # calibration: 2 global rows near the end, 64 local rows
+    rg = np.array([S - 1, S - 2])
+    rl = rng.choice(S, 64, replace=False)
+    tc, _, _ = run(rg, rl)
+    n_g = max(2, min(64, int(2 * args.cpu_seconds / max(tc, 1e-3))))
+    rows_g = np.unique(np.concatenate([[0, 1, S - 1], rng.choice(S, n_g, replace=False)]))
+    rows_l = np.unique(np.concatenate([[0, 1, 1023, 1024, S - 1], rng.choice(S, 8 * n_g, replace=False)]))
+    t, og, ol = run(rows_g, rows_l)
+    f = flops(rows_g, rows_l)
+    got_g = Gout.view(S, glo.Hq, glo.d)[torch.as_tensor(rows_g, device=Gout.device)]
+    got_l = Lout.view(S, loc.Hq, loc.d)[torch.as_tensor(rows_l, device=Lout.device)]
+    eg = np.abs(got_g.double().cpu().numpy() - og)
+    el = np.abs(got_l.double().cpu().numpy() - ol)
+    return {"value": f / t / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "seconds": t,
+            "sample": f"{len(rows_g)} query rows (all 16 heads) of the global layer and "
+                      f"{len(rows_l)} rows of the first local layer, S={S}; fp64, OpenMP",
+            "parity_sample": {"global_max_abs": float(eg.max()), "global_mean_abs": float(eg.mean()),
+                              "local_max_abs": float(el.max()), "local_mean_abs": float(el.mean())}}
+
+
+if __name__ == "__main__":
+    main()

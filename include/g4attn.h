@@ -1,0 +1,140 @@
+/*
+ * g4attn.h -- C ABI of libg4attn: the attention block of Gemma 4 on AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The block interleaves two attention layer kinds:
+ *   - local layers: causal sliding-window attention (window 512 or 1024 keys),
+ *     2 query heads per KV head, head dim 256, rotary encoding on every pair;
+ *   - global layers: causal attention over the whole preceding sequence,
+ *     8 query heads per KV head, head dim 512, keys identical to values (one
+ *     tensor serves both), and p-RoPE rotating only the first quarter of the
+ *     rotary pairs.
+ * Sources: "Guia visual do Gemma 4" (pt.news.hada.io), sections "Intercalacao
+ * de camadas de atencao", "GQA (Grouped Query Attention)", "Tecnica K=V" and
+ * "p-RoPE"; "Gemma 4: yak Google DeepMind pereosmyslyuye vidkryti modeli ..."
+ * (techtoday.in.ua), section "Optymizovana uvaha: lokalni y hlobalni shary"
+ * (local GQA ratio, 512 vs 256 head dims); "Visao geral do modelo Gemma 4"
+ * (ai.google.dev), section "Principais Consideracoes para o planejamento de
+ * memoria" (the KV cache grows with prompt and generated tokens).
+ *
+ * What every call computes, for query row (b, i, h) with G = Hq / Hkv:
+ *     out[b,i,h] = sum_j softmax_j(s_j) * v[b,j,h/G]
+ *     s_j = < R(pos_i) q[b,i,h], R(pos_j) k[b,j,h/G] > / sqrt(d)
+ * over the keys j with 0 <= i - j < window (window 0: every j <= i).  R(P)
+ * turns pair t = (dims 2t, 2t+1), for t < n_rot = floor(p * d / 2), by the
+ * angle P * theta^(-2t/d), counter-clockwise; the other pairs are not turned.
+ * Values are never rotated (for K=V the one tensor is rotated for the scores
+ * and read raw as the values).  The mask uses the sequence index; positions
+ * only set the rotation angles.
+ *
+ * Conventions shared by every call
+ *   - All tensors are dense, row-major, in device memory (hipMalloc or any
+ *     allocator of device memory).  The caller owns every buffer; the library
+ *     allocates, frees and synchronises nothing, keeps no state between calls
+ *     and is safe to call from several host threads.
+ *   - Calls are asynchronous and ordered on `stream` (a hipStream_t; NULL is
+ *     the null stream).  A return of G4A_OK means the work was enqueued.
+ *   - Argument errors are reported synchronously, before anything is
+ *     launched, as a negative status.  Faults inside a kernel surface at the
+ *     caller's next synchronisation of the stream.
+ *   - Every tensor pointer must be 16-byte aligned.
+ *   - dtype codes: G4A_F32 = 0 (float32), G4A_BF16 = 1 (bfloat16).
+ *     Supported (in_dtype, out_dtype): (F32, F32), (BF16, F32), (BF16, BF16).
+ *     Inside the kernels bf16 inputs are multiplied on the matrix cores with
+ *     fp32 accumulation; f32 inputs are computed in fp32 throughout.
+ *   - Supported shapes: d in {256, 512} for bf16 inputs, d in {64, 128, 256,
+ *     512} for f32 inputs; G = Hq / Hkv in {1, 2, 4, 8}.
+ */
+#ifndef G4ATTN_H
+#define G4ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define G4A_OK 0
+#define G4A_EINVAL (-1)      /* null pointer, bad size, Hq % Hkv != 0, p outside [0,1],
+                                theta <= 0, window < 0, ring capacity != window */
+#define G4A_EUNSUPPORTED (-2) /* head dim, group size or dtype pair not built */
+#define G4A_EALIGN (-3)      /* a tensor pointer is not 16-byte aligned */
+#define G4A_EWORKSPACE (-4)  /* decode workspace missing or too small */
+#define G4A_EHIP (-5)        /* the HIP runtime refused a launch; see g4attn_last_hip_error */
+
+/* dtype codes */
+#define G4A_F32 0
+#define G4A_BF16 1
+
+/*
+ * Sliding-window (local) causal prefill with separate keys and values.
+ *   q    [B, S, Hq,  d]  in_dtype        k, v [B, S, Hkv, d]  in_dtype
+ *   out  [B, S, Hq,  d]  out_dtype       pos  [B, S] int32 token positions
+ *   window: keys per query including itself (0 = unbounded, i.e. global).
+ *   theta: rotary base; p: rotated fraction of the pairs (1 = full RoPE).
+ * Local layers: window 512/1024, G = 2, d = 256, theta 1e4, p = 1
+ * ("Guia visual do Gemma 4", section "Intercalacao de camadas de atencao";
+ * techtoday page, attention section, for G = 2 and d = 256).
+ * Returns G4A_OK or a negative status; out is written in full.
+ */
+int g4attn_local_prefill(const void* q, const void* k, const void* v, void* out,
+                         const int32_t* pos, int B, int S, int Hq, int Hkv, int d, int window,
+                         float theta, float p, int in_dtype, int out_dtype, void* stream);
+
+/*
+ * Global causal prefill with keys identical to values (K=V): one tensor kv
+ * is rotated for the scores and read raw as the values, so it is loaded once
+ * for both products ("Guia visual do Gemma 4", sections "GQA", "Tecnica K=V",
+ * "p-RoPE": G = 8, d = 512, p = 0.25).
+ *   q   [B, S, Hq, d]   kv [B, S, Hkv, d]   out [B, S, Hq, d]   pos [B, S]
+ *   window: 0 for global layers (a positive window also works).
+ * Returns G4A_OK or a negative status; out is written in full.
+ */
+int g4attn_global_prefill(const void* q, const void* kv, void* out, const int32_t* pos, int B,
+                          int S, int Hq, int Hkv, int d, int window, float theta, float p,
+                          int in_dtype, int out_dtype, void* stream);
+
+/*
+ * Decode: one query token per sequence against a cache of raw (unrotated)
+ * keys and values; the rotation of every cached key is applied on the fly at
+ * the position that key holds.
+ *   q        [B, Hq, d]              in_dtype
+ *   k_cache  [B, Hkv, capacity, d]   in_dtype
+ *   v_cache  [B, Hkv, capacity, d]   in_dtype, or NULL for K=V (k_cache is
+ *                                    read raw as the values)
+ *   out      [B, Hq, d]              out_dtype
+ *   pos      [B] int32: position P of each query token; its own key/value
+ *            must already be in the cache.
+ *   window > 0: ring cache, capacity == window; position t lives in slot
+ *            t mod window and the query sees positions max(0, P-window+1)..P.
+ *   window == 0: linear cache, row t holds position t; the query sees 0..P.
+ *   Cache rows the query does not see are never read (they may hold NaN).
+ *   A sequence with P < 0, or P >= capacity for a linear cache, gets an
+ *   all-NaN output row.
+ *   workspace: device memory of at least g4attn_decode_workspace_bytes(...)
+ *   bytes for split partial results; its contents need no initialisation
+ *   and are garbage afterwards.  Calls that share one workspace must be
+ *   ordered on one stream.
+ * Returns G4A_OK or a negative status.
+ */
+int g4attn_decode(const void* q, const void* k_cache, const void* v_cache, void* out,
+                  const int32_t* pos, int B, int Hq, int Hkv, int d, int capacity, int window,
+                  float theta, float p, int in_dtype, int out_dtype, void* workspace,
+                  size_t workspace_bytes, void* stream);
+
+/* Workspace bytes g4attn_decode needs for these sizes (0 on invalid sizes). */
+size_t g4attn_decode_workspace_bytes(int B, int Hq, int Hkv, int d, int capacity, int window);
+
+/* Static text for a status code. */
+const char* g4attn_strerror(int status);
+
+/* hipError_t of the last failed launch on this host thread (0 if none). */
+int g4attn_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* G4ATTN_H */

@@ -1,0 +1,116 @@
+"""The C-ABI library: it loads without a GPU, exports every symbol the header
+declares, and rejects bad arguments on the host before any launch."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import attention_g4attn_amd._lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "g4attn.h")
+
+
+def header_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(g4attn_\w+)\s*\(", text)))
+
+
+def test_header_lists_the_binding_signatures():
+    assert header_functions() == sorted(L.SIGNATURES)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = L.lib()
+    out = subprocess.run(["nm", "-D", "--defined-only", L.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (g4attn_\w+)", out))
+    for name in header_functions():
+        assert name in exported, name
+        assert getattr(lib, name) is not None
+    # nothing else leaks out of the C ABI
+    assert exported == set(header_functions())
+
+
+def test_strerror_and_codes():
+    lib = L.lib()
+    for code in (0, -1, -2, -3, -4, -5):
+        assert lib.g4attn_strerror(code)
+    assert lib.g4attn_strerror(7) == b"unknown status"
+    assert lib.g4attn_last_hip_error() == 0
+
+
+# Fake, aligned, never dereferenced device addresses: every call below must
+# fail validation before touching memory or the HIP runtime.
+A = 1 << 20
+
+
+def local(**kw):
+    args = dict(q=A, k=2 * A, v=3 * A, out=4 * A, pos=5 * A, B=1, S=8, Hq=4, Hkv=2, d=256,
+                window=4, theta=1e4, p=1.0, i=1, o=0, stream=None)
+    args.update(kw)
+    return L.lib().g4attn_local_prefill(*args.values())
+
+
+def glob(**kw):
+    args = dict(q=A, kv=2 * A, out=4 * A, pos=5 * A, B=1, S=8, Hq=8, Hkv=1, d=512, window=0,
+                theta=1e6, p=0.25, i=1, o=0, stream=None)
+    args.update(kw)
+    return L.lib().g4attn_global_prefill(*args.values())
+
+
+def dec(**kw):
+    args = dict(q=A, k=2 * A, v=None, out=4 * A, pos=5 * A, B=2, Hq=16, Hkv=2, d=512,
+                capacity=1024, window=0, theta=1e6, p=0.25, i=1, o=0, ws=6 * A,
+                ws_bytes=1 << 30, stream=None)
+    args.update(kw)
+    return L.lib().g4attn_decode(*args.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), -1), (dict(k=None), -1), (dict(v=None), -1), (dict(out=None), -1),
+    (dict(pos=None), -1), (dict(B=-1), -1), (dict(S=-2), -1), (dict(Hq=0), -1),
+    (dict(Hkv=0), -1), (dict(Hq=5), -1), (dict(d=255), -1), (dict(window=-1), -1),
+    (dict(theta=0.0), -1), (dict(theta=float("nan")), -1), (dict(p=1.5), -1),
+    (dict(p=-0.1), -1), (dict(p=float("nan")), -1), (dict(i=2), -1), (dict(o=3), -1),
+    (dict(d=128), -2), (dict(Hq=6, Hkv=2), -2), (dict(Hq=32, Hkv=2), -2), (dict(i=0, o=1), -2),
+    (dict(q=A + 8), -3), (dict(out=4 * A + 4), -3), (dict(pos=5 * A + 2), -3),
+])
+def test_local_prefill_validation(kw, code):
+    assert local(**kw) == code
+
+
+def test_empty_inputs_are_noops():
+    assert local(B=0, q=None, k=None, v=None, out=None, pos=None) == 0
+    assert local(S=0, q=None, k=None, v=None, out=None, pos=None) == 0
+    assert glob(S=0, q=None, kv=None, out=None, pos=None) == 0
+    assert dec(B=0, q=None, k=None, out=None, pos=None, ws=None) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(kv=None), -1), (dict(d=384), -2), (dict(Hq=24, Hkv=1), -2), (dict(kv=2 * A + 1), -3),
+])
+def test_global_prefill_validation(kw, code):
+    assert glob(**kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(capacity=0), -1), (dict(window=512, capacity=1024), -1), (dict(q=None), -1),
+    (dict(k=None), -1), (dict(pos=None), -1), (dict(B=-1), -1), (dict(d=100), -1 + 0 * 2),
+    (dict(d=96), -2), (dict(ws=None), -4), (dict(ws_bytes=100), -4), (dict(ws=6 * A + 4), -3),
+    (dict(v=3 * A + 2), -3),
+])
+def test_decode_validation(kw, code):
+    if kw.get("d") == 100:
+        code = -2  # even but not a supported head dim
+    assert dec(**kw) == code
+
+
+def test_workspace_size():
+    f = L.lib().g4attn_decode_workspace_bytes
+    assert f(64, 16, 2, 512, 65536, 0) == 64 * 16 * 32 * (512 + 2) * 4
+    assert f(64, 16, 8, 256, 512, 512) == 64 * 16 * 4 * (256 + 2) * 4
+    assert f(1, 16, 8, 256, 1024, 512) == 0  # ring capacity must equal the window
+    assert f(1, 0, 8, 256, 512, 512) == 0

@@ -1,0 +1,171 @@
+"""HIP kernels vs the fp64 oracle, element by element, through the C ABI.
+
+Sizes keep the oracle to seconds while spanning several query tiles (16 tokens
+for d=512/G=8 ... 128 tokens for G=1), several 32-key KV tiles and ragged
+tails.  Tolerances: fp32 inputs max |err| <= 1e-4; bf16 inputs max |err| <=
+1e-2 and mean |err| <= 1e-3, measured on fp32 outputs.
+"""
+import numpy as np
+import pytest
+import torch
+
+import attention_g4attn_amd as g4
+import oracle
+from attention_g4attn_amd import inputs
+from tests.helpers import assert_parity, to_oracle
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def run_prefill(layer, dtype, offset=0, window=None, out_dtype=None, wl=90, idx=0):
+    q, k, v, pos = inputs.prefill_inputs(layer, wl, idx, dtype, DEV, offset)
+    W = layer.window if window is None else window
+    print(f"prefill {layer} {dtype} W={W} offset={offset}", flush=True)
+    if layer.kind == "global":
+        out = g4.global_prefill(q, k, pos, W, layer.theta, layer.p, out_dtype=out_dtype)
+    else:
+        out = g4.local_prefill(q, k, v, pos, W, layer.theta, layer.p, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    return out, (q, k, v, pos, W)
+
+
+def oracle_prefill(layer, q, k, v, pos, W, rows=None):
+    return oracle.prefill(to_oracle(q), to_oracle(k), to_oracle(v), pos.cpu().numpy(), W,
+                          layer.theta, layer.p, rows=rows)
+
+
+def test_tiny_fp32_local_and_global():
+    for layer in (inputs.TINY_LOCAL, inputs.TINY_GLOBAL):
+        out, (q, k, v, pos, W) = run_prefill(layer, torch.float32, wl=1)
+        ref = oracle_prefill(layer, q, k, v, pos, W)
+        assert_parity(out, ref, torch.float32, str(layer))
+
+
+SMALL = [
+    # kind, B, S, Hq, Hkv, d, window, theta, p
+    inputs.Layer("global", 1, 300, 8, 1, 512, 0, 1e6, 0.25),
+    inputs.Layer("global", 2, 77, 16, 2, 512, 0, 1e6, 0.25),
+    inputs.Layer("local", 2, 333, 4, 2, 256, 64, 1e4, 1.0),
+    inputs.Layer("local", 1, 700, 16, 8, 256, 256, 1e4, 1.0),
+    inputs.Layer("local", 1, 200, 2, 2, 256, 1, 1e4, 1.0),
+    inputs.Layer("global", 1, 150, 4, 1, 256, 0, 1e6, 0.5),
+    inputs.Layer("local", 1, 190, 8, 2, 512, 40, 1e4, 1.0),
+    inputs.Layer("global", 1, 129, 2, 1, 512, 0, 1e4, 0.0),
+    inputs.Layer("local", 1, 100, 4, 4, 256, 0, 1e4, 0.25),
+]
+
+
+@pytest.mark.parametrize("layer", SMALL, ids=lambda l: f"{l.kind}-S{l.S}-G{l.Hq // l.Hkv}-d{l.d}-W{l.window}-p{l.p}")
+def test_bf16_prefill_small(layer):
+    out, (q, k, v, pos, W) = run_prefill(layer, torch.bfloat16)
+    ref = oracle_prefill(layer, q, k, v, pos, W)
+    assert_parity(out, ref, torch.bfloat16, str(layer))
+
+
+@pytest.mark.parametrize("layer", [SMALL[0], SMALL[2]], ids=["global", "local"])
+def test_bf16_prefill_fp32_path_for_f32_inputs_small(layer):
+    out, (q, k, v, pos, W) = run_prefill(layer, torch.float32)
+    ref = oracle_prefill(layer, q, k, v, pos, W)
+    assert_parity(out, ref, torch.float32, str(layer))
+
+
+def test_large_positions_offset():
+    """Positions near 2^18: rotation angles must stay accurate."""
+    layer = inputs.Layer("global", 1, 160, 8, 1, 512, 0, 1e6, 0.25)
+    out, (q, k, v, pos, W) = run_prefill(layer, torch.bfloat16, offset=200000)
+    assert_parity(out, oracle_prefill(layer, q, k, v, pos, W), torch.bfloat16, "offset global")
+    layer = inputs.Layer("local", 1, 160, 4, 2, 256, 48, 1e4, 1.0)
+    out, (q, k, v, pos, W) = run_prefill(layer, torch.bfloat16, offset=261000)
+    assert_parity(out, oracle_prefill(layer, q, k, v, pos, W), torch.bfloat16, "offset local")
+
+
+def test_bf16_output():
+    layer = SMALL[0]
+    out, (q, k, v, pos, W) = run_prefill(layer, torch.bfloat16, out_dtype=torch.bfloat16)
+    assert out.dtype == torch.bfloat16
+    ref = oracle_prefill(layer, q, k, v, pos, W)
+    got = out.float().cpu().double().numpy()
+    # bf16 storage adds at most half an ulp of the output: 2^-9 relative
+    assert np.all(np.abs(got - ref) <= 1e-2 + 2.0 ** -8 * np.abs(ref))
+
+
+def test_window_ge_seq_equals_global_and_k_equals_v_paths():
+    layer = inputs.Layer("local", 1, 260, 8, 1, 512, 0, 1e6, 0.25)
+    q, k, v, pos = inputs.prefill_inputs(layer, 91, 0, torch.bfloat16, DEV)
+    a = g4.global_prefill(q, k, pos, 0, 1e6, 0.25)
+    b = g4.global_prefill(q, k, pos, 260, 1e6, 0.25)
+    c = g4.local_prefill(q, k, k.clone(), pos, 0, 1e6, 0.25)  # separate-V path fed v := k
+    d = g4.global_prefill(q, k, pos, 0, 1e6, 0.25)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    assert torch.equal(a, d), "not deterministic"
+    assert (a - c).abs().max().item() <= 1e-6
+
+
+def test_unread_tail_and_guard_band():
+    """Output rows are written exactly; memory past the output stays untouched."""
+    layer = inputs.Layer("global", 1, 45, 8, 1, 512, 0, 1e6, 0.25)
+    q, k, v, pos = inputs.prefill_inputs(layer, 92, 0, torch.bfloat16, DEV)
+    n = 1 * 45 * 8 * 512
+    buf = torch.full((n + 4096,), float("nan"), device=DEV)
+    out = buf[:n].view(1, 45, 8, 512)
+    g4.global_prefill(q, k, pos, 0, 1e6, 0.25, out=out)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all()
+    assert torch.isnan(buf[n:]).all()
+
+
+# ---------------------------------------------------------------- decode ----
+
+def run_decode(layer, dtype, lengths, wl=95):
+    q, kc, vc, pos, lengths = inputs.decode_inputs(layer, wl, 0, dtype, DEV, lengths)
+    print(f"decode {layer} {dtype} lengths={lengths.tolist()[:8]}", flush=True)
+    out = g4.decode(q, kc, vc, pos, layer.window, layer.theta, layer.p)
+    torch.cuda.synchronize()
+    ref = oracle.decode(to_oracle(q), to_oracle(kc), None if vc is None else to_oracle(vc),
+                        pos.cpu().numpy(), layer.window, layer.theta, layer.p)
+    return out, ref
+
+
+DEC = [
+    inputs.DecodeLayer("global", 4, 16, 2, 512, 3000, 0, 1e6, 0.25),
+    inputs.DecodeLayer("local", 4, 16, 8, 256, 512, 512, 1e4, 1.0),
+    inputs.DecodeLayer("local", 3, 8, 4, 256, 96, 96, 1e4, 1.0),
+    inputs.DecodeLayer("global", 3, 8, 1, 512, 700, 0, 1e6, 0.25),
+]
+
+
+@pytest.mark.parametrize("layer", DEC, ids=lambda l: f"{l.kind}-C{l.capacity}-G{l.Hq // l.Hkv}")
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
+def test_decode_small(layer, dtype):
+    if layer.window > 0:
+        lengths = torch.tensor([1, layer.window - 1, layer.window, 5 * layer.window + 3][:layer.B])
+    else:
+        C = layer.capacity
+        lengths = torch.tensor([1, min(2049, C // 2 + 1), C, min(1500, C - 3)][:layer.B])
+    out, ref = run_decode(layer, dtype, lengths)
+    assert_parity(out, ref, dtype, str(layer))
+
+
+def test_decode_bad_positions_nan():
+    layer = inputs.DecodeLayer("global", 3, 8, 1, 512, 64, 0, 1e6, 0.25)
+    q, kc, vc, pos, _ = inputs.decode_inputs(layer, 96, 0, torch.bfloat16, DEV,
+                                             torch.tensor([10, 10, 10]))
+    pos = torch.tensor([-1, 64, 5], dtype=torch.int32, device=DEV)
+    out = g4.decode(q, kc, None, pos, 0, 1e6, 0.25)
+    torch.cuda.synchronize()
+    assert torch.isnan(out[0]).all() and torch.isnan(out[1]).all() and torch.isfinite(out[2]).all()
+
+
+def test_decode_equals_last_prefill_row():
+    S = 517
+    layer = inputs.Layer("global", 1, S, 16, 2, 512, 0, 1e6, 0.25)
+    q, k, v, pos = inputs.prefill_inputs(layer, 97, 0, torch.bfloat16, DEV)
+    pre = g4.global_prefill(q, k, pos, 0, 1e6, 0.25)
+    cache = k.permute(0, 2, 1, 3).contiguous()
+    dec = g4.decode(q[:, S - 1].contiguous(), cache, None,
+                    torch.tensor([S - 1], dtype=torch.int32, device=DEV), 0, 1e6, 0.25)
+    torch.cuda.synchronize()
+    assert (dec - pre[:, S - 1]).abs().max().item() <= 1e-2
