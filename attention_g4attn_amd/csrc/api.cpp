@@ -74,11 +74,18 @@ int prefill(const void* q, const void* k, const void* v, void* out, const int32_
   a.D = d;
   a.window = window;
   a.n_rot = rotated_pairs(d, p);
+  {
+    const int nrc = (a.n_rot + 3) / 4;  // 16-byte chunks holding rotated pairs
+    int l2 = 0;
+    while ((1 << l2) < nrc) ++l2;
+    a.nrc_log2 = l2;
+  }
   a.log2_theta = log2((double)theta);
   a.scale = (float)(1.0 / sqrt((double)d));
   a.scale_log2e = (float)(1.4426950408889634 / sqrt((double)d));
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (in_dtype == G4A_F32) return finish(g4a::launch_prefill_f32(a, st));
+  if (!g4a::prefill_supported(d, kv_shared, a.n_rot)) return G4A_EUNSUPPORTED;
   return finish(g4a::launch_prefill_bf16(a, kv_shared, out_dtype == G4A_BF16, st));
 }
 

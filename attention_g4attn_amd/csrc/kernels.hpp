@@ -14,6 +14,7 @@ struct PrefillArgs {
   void* out;
   const int32_t* pos;
   int B, S, Hq, Hkv, D, window, n_rot;
+  int nrc_log2;       // ceil(log2(ceil(n_rot / 4))): rotated 16-byte chunks, rounded up
   double log2_theta;
   float scale_log2e;  // log2(e) / sqrt(D)
   float scale;        // 1 / sqrt(D)
@@ -36,9 +37,16 @@ struct DecodeArgs {
   float* part_ml;  // [B, Hq, nchunk, 2]
 };
 
-// bf16 inputs, matrix-core path; D in {256, 512}, G in {1, 2, 4, 8}
+// bf16 inputs, matrix-core path; D in {256, 512}, G in {1, 2, 4, 8}.
+// Separate K and V with D = 512 needs n_rot <= 64 (see prefill_supported).
+bool prefill_supported(int D, bool kv_shared, int n_rot);
 hipError_t launch_prefill_bf16(const PrefillArgs& a, bool kv_shared, bool out_bf16,
                                hipStream_t st);
+// per-family launchers (one translation unit each)
+hipError_t launch_prefill_kv512(const PrefillArgs& a, bool out_bf16, hipStream_t st);
+hipError_t launch_prefill_d256(const PrefillArgs& a, bool kv_shared, bool out_bf16,
+                               hipStream_t st);
+hipError_t launch_prefill_sep512(const PrefillArgs& a, bool out_bf16, hipStream_t st);
 // f32 inputs, fp32 vector path; D in {64, 128, 256, 512}, G in {1, 2, 4, 8}
 hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t st);
 

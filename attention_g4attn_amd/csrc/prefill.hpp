@@ -1,0 +1,572 @@
+// Causal (sliding-window or global) prefill attention for bf16 inputs on the
+// gfx950 matrix cores.
+//
+// What is computed: for every query row (b, i, h), the softmax over the
+// visible keys of the rotated scores, times the raw values.  Local layers:
+// separate K and V, window W, full rotation.  Global layers: K=V (one tensor
+// is rotated for the scores and read raw as the values) with only the first
+// n_rot pairs rotated (p-RoPE).  Sources: "Guia visual do Gemma 4"
+// (pt.news.hada.io), sections "Intercalacao de camadas de atencao", "GQA",
+// "Tecnica K=V" and "p-RoPE".
+//
+// Work decomposition: one workgroup = 4 waves = M = 128*MB query rows.
+//   - The M tile packs the G query heads of TQ = M/G consecutive tokens that
+//     share one KV head, so every staged KV tile feeds all G heads.  Row r is
+//     token t0 + r/G, head hkv*G + r%G; wave w owns rows RW*w .. RW*w+RW-1,
+//     as MB blocks of 32 that share every K/V fragment read from LDS.
+//   - KV tiles of 32 keys stream from HBM straight into an NST-deep LDS ring
+//     (16-byte direct-to-LDS loads, no staging registers), issued two tiles
+//     ahead when NST = 3.  Raw tiles are row-major with 16-byte chunks
+//     XOR-swizzled by row so both read patterns below are bank-conflict free.
+//   - The rotated part of each key (chunks holding pairs < n_rot) is written
+//     once per tile into a small "slab" by all threads, interleaved with the
+//     score products of the previous tile; the rest of the score operand is
+//     read from the raw tile.
+//   - Scores are computed transposed, S^T = K~ Q~^T, so each lane owns one
+//     query row per block: the softmax needs one exchange with lane l^32 and
+//     the output rescale is a per-lane scalar; P goes from the score registers
+//     straight into the B operand of O^T += V^T P^T.
+//   - The value operand V^T is read from the raw row-major tile with the LDS
+//     transpose read (ds_read_b64_tr_b16): 4 consecutive keys of one dim per
+//     lane per read.  For K=V this is the same raw tile the scores read.
+//   - Online softmax in fp32 (base 2, scale folded with log2 e); the output is
+//     rescaled only when the running max grows by more than 2^8.
+//   - Tiles outside a wave's causal band are skipped; only edge tiles are
+//     masked.  Grid order: KV heads fastest, then query tiles from the longest
+//     causal row down, so each XCD streams one KV head's tiles in step.
+#pragma once
+#include <type_traits>
+
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace g4a {
+namespace pf {
+
+constexpr int NW = 4;   // waves per workgroup
+constexpr int BN = 32;  // keys per KV tile
+constexpr int FG = 2;   // LDS fragments per software-pipelined group
+
+// 16-byte chunk swizzle of row r: rows r..r+7 map one chunk to 8 different
+// bank groups, and 4 consecutive rows (r % 4 == 0) map two adjacent chunks to
+// 8 different bank groups.
+__device__ __forceinline__ int swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+__device__ __forceinline__ u32x2 lds_read_tr16(const unsigned char* p) {
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
+  return __builtin_bit_cast(u32x2, v);
+}
+
+// Buffer resource over [base, base + bytes): loads past the end return zeros.
+// base and bytes must be the same in every lane; they are moved to scalar
+// registers explicitly so the loads need no per-lane loop.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)p);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(p >> 32));
+  const uint32_t n = __builtin_amdgcn_readfirstlane(bytes);
+  void* u = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(u, (short)0, (int)n, 0x00020000);
+}
+
+// Direct load into LDS: each lane's `size` bytes at rsrc + voff land at
+// ldst + lane * size (ldst wave-uniform).
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rs, uint32_t voff,
+                                          uint32_t soff, unsigned char* ldst) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(ldst),
+                                           16, voff, soff, 0, 0);
+}
+__device__ __forceinline__ void lds_dma4(__amdgpu_buffer_rsrc_t rs, uint32_t voff,
+                                         unsigned char* ldst) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(ldst),
+                                           4, voff, 0, 0, 0);
+}
+
+// wait until at most n vector-memory operations of this wave are in flight
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// LDS layout.  Every ring stage is its own __shared__ object (raw K tile, raw
+// V tile when separate, then the tile's key positions), so the compiler can
+// tell the stage being read from the stages the direct loads are filling and
+// does not wait for those loads before reading.
+template <int D, bool KVS, int SW, int NST>
+struct Lds {
+  static constexpr int RAW = BN * D * 2;             // one raw tile, bytes
+  static constexpr int NT = KVS ? 1 : 2;             // raw tensors per stage
+  static constexpr int POS = NT * RAW;               // key positions (256 B) in a stage
+  static constexpr int STAGE = POS + 256;
+  static constexpr int SLAB = BN * SW * 2;           // one rotated slab
+  static constexpr int TOTAL = NST * STAGE + 2 * SLAB + (D / 2) * 8;
+};
+
+template <int N>
+using IC = std::integral_constant<int, N>;
+
+template <class T>
+__device__ __forceinline__ T& lds_at(unsigned char* base, int off) {
+  return *reinterpret_cast<T*>(base + off);
+}
+
+// Exact attention row (token t, query head h) for a wave, with the row max m
+// (base-2 scaled) known in advance, so no rescaling is needed.  Lane e owns
+// dims e*(D/64) .. +D/64-1; every key's score is a wave-wide reduction.
+template <int D, bool KVS, bool OBF>
+__device__ __noinline__ void exact_row(const PrefillArgs& a, int b, int hkv, int t, int h,
+                                       float m, const double* gtab) {
+  constexpr int E = D / 64;  // dims per lane, even
+  const int lane = threadIdx.x & 63;
+  const int S = a.S, W = a.window;
+  const uint16_t* qr = static_cast<const uint16_t*>(a.q) + (((size_t)b * S + t) * a.Hq + h) * D;
+  const int qp = a.pos[(size_t)b * S + t];
+  float qv[E];
+#pragma unroll
+  for (int e = 0; e < E; e += 2) {
+    const int d0 = lane * E + e;
+    float x0 = bf_lo(qr[d0]), x1 = bf_lo(qr[d0 + 1]);
+    if (d0 / 2 < a.n_rot) {
+      float c, s;
+      rope_cs_accurate(qp, gtab[d0 / 2], c, s);
+      const float y0 = x0 * c - x1 * s, y1 = x0 * s + x1 * c;
+      x0 = y0;
+      x1 = y1;
+    }
+    qv[e] = x0;
+    qv[e + 1] = x1;
+  }
+  float o[E], l = 0.f;
+#pragma unroll
+  for (int e = 0; e < E; ++e) o[e] = 0.f;
+  const int lo = W > 0 ? max(0, t - W + 1) : 0;
+  for (int j = lo; j <= t; ++j) {
+    const size_t row = ((size_t)b * S + j) * a.Hkv + hkv;
+    const uint16_t* kr = static_cast<const uint16_t*>(a.k) + row * D;
+    const uint16_t* vr = static_cast<const uint16_t*>(a.v) + row * D;
+    const int kp = a.pos[(size_t)b * S + j];
+    float part = 0.f;
+#pragma unroll
+    for (int e = 0; e < E; e += 2) {
+      const int d0 = lane * E + e;
+      float x0 = bf_lo(kr[d0]), x1 = bf_lo(kr[d0 + 1]);
+      if (d0 / 2 < a.n_rot) {
+        float c, s;
+        rope_cs_accurate(kp, gtab[d0 / 2], c, s);
+        const float y0 = x0 * c - x1 * s, y1 = x0 * s + x1 * c;
+        x0 = y0;
+        x1 = y1;
+      }
+      part += qv[e] * x0 + qv[e + 1] * x1;
+    }
+    const float p = __builtin_amdgcn_exp2f(wave_sum(part) * a.scale_log2e - m);
+    l += p;
+#pragma unroll
+    for (int e = 0; e < E; ++e) o[e] += p * bf_lo(vr[lane * E + e]);
+  }
+  const size_t ob = (((size_t)b * S + t) * a.Hq + h) * D + lane * E;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    if constexpr (OBF)
+      static_cast<uint16_t*>(a.out)[ob + e] = (uint16_t)(pack_bf16(o[e] / l, 0.f) & 0xffffu);
+    else
+      static_cast<float*>(a.out)[ob + e] = o[e] / l;
+  }
+}
+
+// SW = dims of each key kept rotated in the slab: D/4 (pairs < D/8 may turn,
+// e.g. p = 0.25) or D (any p).  Score k-steps s < SW/16 read the slab, the
+// others the raw tile.
+template <int D, int G, bool KVS, bool OBF, int SW, int NST, int MB>
+__global__ void __launch_bounds__(NW * 64, 1) prefill_kernel(PrefillArgs a) {
+  constexpr int RW = 32 * MB;          // rows per wave
+  constexpr int M = NW * RW;           // rows per workgroup
+  constexpr int TQ = M / G;            // tokens per workgroup
+  constexpr int NDS = D / 16;          // k-steps of the score product
+  constexpr int NSS = SW / 16;         // k-steps read from the slab
+  constexpr int NDB = D / 32;          // 32-dim blocks of the output
+  constexpr int RPI = 1024 / (2 * D);  // rows per direct-load instruction (64 lanes x 16 B)
+  constexpr int LPT = BN / RPI / NW;   // direct loads per thread per tensor per tile
+  constexpr int SWC = SW / 8;          // slab chunks per key
+  constexpr int IPT = BN * SWC / (NW * 64);  // rotation items per thread per tile
+  constexpr int RDR = NW * 64 / SWC;   // rows between a thread's rotation items
+  using L = Lds<D, KVS, SW, NST>;
+  static_assert(L::TOTAL <= 160 * 1024, "LDS budget");
+  static_assert(SWC >= 8 && IPT >= 1 && NDS % 4 == 0 && NSS % 4 == 0, "tile shape");
+  __shared__ __attribute__((aligned(16))) unsigned char st0[L::STAGE];
+  __shared__ __attribute__((aligned(16))) unsigned char st1[L::STAGE];
+  __shared__ __attribute__((aligned(16))) unsigned char st2[NST == 3 ? L::STAGE : 16];
+  __shared__ __attribute__((aligned(16))) unsigned char slabs[2 * L::SLAB];
+  __shared__ double gtab[D / 2];
+  // ring stage s (a compile-time constant) -> its LDS object
+  auto stp = [&](auto s) -> unsigned char* {
+    if constexpr (decltype(s)::value == 0) return st0;
+    else if constexpr (decltype(s)::value == 1) return st1;
+    else return st2;
+  };
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, in a scalar register
+  const int l32 = lane & 31, hl = lane >> 5;
+  const int S = a.S;
+  const int W = a.window;
+  const int n_rot = a.n_rot;
+
+  const int hb = blockIdx.x % a.nheads;
+  const int qt = a.nq - 1 - blockIdx.x / a.nheads;
+  const int b = hb / a.Hkv, hkv = hb % a.Hkv;
+  const int t0 = qt * TQ;
+  const int t_end = min(t0 + TQ, S);
+
+  for (int t = tid; t < D / 2; t += NW * 64) gtab[t] = rope_rev_per_pos(t, D, a.log2_theta);
+  __syncthreads();
+
+  // ---- query rows of this lane (one per block), rotated, as B operands ----
+  int tq[MB], hq[MB];
+  bool row_ok[MB];
+  u32x4 qf[MB][NDS];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    const int row = RW * w + 32 * mb + l32;
+    tq[mb] = t0 + row / G;
+    hq[mb] = hkv * G + row % G;
+    row_ok[mb] = tq[mb] < S;
+    const int tqc = row_ok[mb] ? tq[mb] : S - 1;
+    const int qpos = a.pos[(size_t)b * S + tqc];
+    const uint16_t* qrow =
+        static_cast<const uint16_t*>(a.q) + (((size_t)b * S + tqc) * a.Hq + hq[mb]) * D;
+#pragma unroll
+    for (int s = 0; s < NDS; ++s) {
+      const u32x4 x = *reinterpret_cast<const u32x4*>(qrow + 8 * (2 * s + hl));
+      qf[mb][s] = row_ok[mb] ? x : u32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int s = 0; s < NSS; ++s)
+      if (8 * s < n_rot) qf[mb][s] = rotate_chunk_bf16(qf[mb][s], 2 * s + hl, qpos, n_rot, gtab);
+  }
+
+  // token span of this wave's rows
+  const int tw0 = t0 + (RW * w) / G;
+  const int tw1 = min(t0 + (RW * w + RW - 1) / G, S - 1);
+  const bool wave_ok = tw0 < S;
+  const int klo = W > 0 ? max(0, t0 - W + 1) : 0;
+  const int kt0 = klo / BN, kt1 = (t_end - 1) / BN;
+
+  // ---- direct HBM -> LDS loads of one tile ----
+  // Per tile a buffer resource covers the rows kv0 .. S-1 (rows past the end
+  // read as zeros); each lane's 32-bit offset inside a tile is fixed.
+  const uint32_t row_bytes = (uint32_t)(a.Hkv * D * 2);
+  const uint16_t* kbase = static_cast<const uint16_t*>(a.k) + ((size_t)b * S * a.Hkv + hkv) * D;
+  const uint16_t* vbase = static_cast<const uint16_t*>(a.v) + ((size_t)b * S * a.Hkv + hkv) * D;
+  const int32_t* pbase = a.pos + (size_t)b * S;
+  auto issue_loads = [&](int kt, auto stage) {
+    unsigned char* sp = stp(stage);
+    // padding tiles past the sequence reload its last tile: finite data whose
+    // keys are all masked for this workgroup's rows
+    const int kv0 = min(kt * BN, ((S - 1) / BN) * BN);
+    const uint32_t rows = (uint32_t)min(S - kv0, BN);  // >= 1
+    const size_t toff = (size_t)kv0 * a.Hkv * D;
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase + toff, rows * row_bytes - (row_bytes - D * 2));
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase + toff, rows * row_bytes - (row_bytes - D * 2));
+    // the lane id is laundered so the offsets below are recomputed here (two
+    // or three instructions) instead of being held across the loop
+    int ln = lane;
+    int wl = __builtin_amdgcn_readfirstlane(w);
+    uint32_t rb = __builtin_amdgcn_readfirstlane(row_bytes);
+    asm volatile("" : "+v"(ln), "+s"(wl), "+s"(rb));
+#pragma unroll
+    for (int n = 0; n < LPT; ++n) {
+      const int r0 = (wl * LPT + n) * RPI;  // first row of this load, wave-uniform
+      uint32_t voff;
+      if constexpr (RPI == 1) {
+        voff = (uint32_t)r0 * rb + ((uint32_t)(ln ^ swz(r0)) << 4);
+      } else {
+        const int r = r0 + (ln >> 5);
+        voff = (uint32_t)r * rb + ((uint32_t)((ln & 31) ^ swz(r)) << 4);
+      }
+      unsigned char* dst = sp + r0 * (2 * D);
+      lds_dma16(rk, voff, 0, dst);
+      if constexpr (!KVS) lds_dma16(rv, voff, 0, dst + L::RAW);
+    }
+    if (w == 0)  // positions of the tile's keys (lanes past the end read zeros)
+      lds_dma4(make_rsrc(pbase + kv0, rows * 4), 4 * lane, sp + L::POS);
+  };
+
+  // ---- rotation of one tile's first SW dims into a slab ----
+  // item m of this thread: chunk tid % SWC of row tid / SWC + m * RDR.  The
+  // thread id is laundered so these per-lane values are recomputed at each use
+  // rather than held in registers across the KV loop.
+  auto rotate_item = [&](auto stage, int slot, int m) {
+    unsigned char* sp = stp(stage);
+    int t = tid;
+    asm volatile("" : "+v"(t));
+    const int rc_c = t % SWC;
+    const int r = t / SWC + m * RDR;
+    const int sw = (rc_c ^ swz(r)) << 4;
+    u32x4 x = lds_at<u32x4>(sp, r * (2 * D) + sw);
+    if (4 * rc_c < n_rot) {  // chunk holds at least one turning pair
+      const int p = lds_at<int>(sp, L::POS + 4 * r);
+      x = rotate_chunk_bf16(x, rc_c, p, n_rot, gtab);
+    }
+    lds_at<u32x4>(slabs, slot * L::SLAB + r * (2 * SW) + sw) = x;
+  };
+
+  f32x16 oacc[MB][NDB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int i = 0; i < NDB; ++i) oacc[mb][i] = f32x16{};
+  // Softmax state per row (base 2, scores scaled by log2(e)/sqrt(d)).  The
+  // reference max m_ref is fixed at the first tile where the row sees a key,
+  // when O is still zero, so O never needs rescaling.  m_seen tracks the true
+  // running max.  If a later tile ever exceeds m_ref by more than 2^64 (P or O
+  // could overflow), the row is flagged in ovf and recomputed exactly after
+  // the epilogue, with m_seen as the reference.
+  constexpr float UNSET = -1e30f;
+  float m_ref[MB], m_seen[MB], l_run[MB];
+  int ovf = 0;  // bit mb: row of block mb overflowed its reference
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    m_ref[mb] = UNSET;
+    m_seen[mb] = UNSET;
+    l_run[mb] = 0.f;
+  }
+  const float cs = a.scale_log2e;
+
+  // ---- one tile: scores (with the next tile's rotation interleaved), softmax, PV ----
+  auto compute = [&](int kt, auto stage, int slot, bool rot_next, auto nstage, int nslot) {
+    unsigned char* sp = stp(stage);
+    const int kv0 = kt * BN;
+    // Lane parts of the fragment offsets, recomputed per tile from a laundered
+    // lane id (cheap) so they do not occupy registers across the loop.
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int l32 = ln & 31, hl = ln >> 5;
+    // score operand (key l32, chunk c = 2s + hl): chunk position
+    // c ^ swz(l32) = 8*(s/4) + ((2*(s%4) + hl) ^ swz(l32))
+    const int sw_n = swz(l32);
+    int soff[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) soff[i] = ((2 * i + hl) ^ sw_n) << 4;
+    // value operand by transpose reads: lane (g = ln/16, i = ln%16) reads row
+    // 4*(g/2) + i/4 (+8, +16*k2) at dims 32*db + 16*(g%2) + 4*(i%4)
+    const int tr_i = ln & 15, tr_g = ln >> 4;
+    const int tr_row = 4 * (tr_g >> 1) + (tr_i >> 2);
+    const int tr_sw = swz(tr_row);
+    const int tr_x = 2 * (tr_g & 1) + ((tr_i & 3) >> 1);
+    const int voff0 = tr_row * (2 * D) + (tr_i & 1) * 8 + ((tr_x ^ tr_sw) << 4);
+    const int voff1 = tr_row * (2 * D) + (tr_i & 1) * 8 + (((4 + tr_x) ^ tr_sw) << 4);
+    const int rbase = l32 * (2 * D);
+    const int sbase = slot * L::SLAB + l32 * (2 * SW);
+
+    f32x16 sacc[MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) sacc[mb] = f32x16{};
+    {
+      // k-step s lives in the slab for s < NSS, in the raw tile otherwise;
+      // fragments stream in groups of FG, one group ahead
+      auto frag = [&](int s) -> u32x4 {
+        if (s < NSS) return lds_at<u32x4>(slabs, sbase + 128 * (s >> 2) + soff[s & 3]);
+        return lds_at<u32x4>(sp, rbase + 128 * (s >> 2) + soff[s & 3]);
+      };
+      constexpr int NG = NDS / FG;
+      constexpr int RSTEP = NG / IPT > 0 ? NG / IPT : 1;  // groups between rotation items
+      u32x4 kf[2][FG];
+#pragma unroll
+      for (int i = 0; i < FG; ++i) kf[0][i] = frag(i);
+#pragma unroll
+      for (int g = 0; g < NG; ++g) {
+        if (g + 1 < NG) {
+#pragma unroll
+          for (int i = 0; i < FG; ++i) kf[(g + 1) & 1][i] = frag(FG * (g + 1) + i);
+        }
+#pragma unroll
+        for (int i = 0; i < FG; ++i)
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb)
+            sacc[mb] = mfma32x32x16(kf[g & 1][i], qf[mb][FG * g + i], sacc[mb]);
+        if (g % RSTEP == 0 && g / RSTEP < IPT && rot_next) rotate_item(nstage, nslot, g / RSTEP);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int m = (NG + RSTEP - 1) / RSTEP; m < IPT; ++m)
+        if (rot_next) rotate_item(nstage, nslot, m);
+    }
+
+    u32x4 pf[MB][2];
+    const bool need_mask = (kv0 + BN - 1 > tw0) || (W > 0 && kv0 <= tw1 - W);
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      if (need_mask) {  // wave-uniform
+        const int lo = W > 0 ? tq[mb] - W + 1 : 0;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int j = kv0 + 8 * (r >> 2) + 4 * hl + (r & 3);
+          sacc[mb][r] = (j <= tq[mb] && j >= lo) ? sacc[mb][r] : -INFINITY;
+        }
+      }
+      float mx = sacc[mb][0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sacc[mb][r]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float m_tile = mx * cs;  // -inf when the row sees no key here
+      m_seen[mb] = fmaxf(m_seen[mb], m_tile);
+      m_ref[mb] = m_ref[mb] == UNSET ? fmaxf(m_tile, UNSET) : m_ref[mb];
+      ovf |= (m_tile > m_ref[mb] + 64.f) << mb;
+      const float mr = m_ref[mb] == UNSET ? 0.f : m_ref[mb];
+      float lsum = 0.f;
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[mb][8 * k2 + 2 * i], cs, -mr));
+          const float p1 =
+              __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[mb][8 * k2 + 2 * i + 1], cs, -mr));
+          lsum += p0 + p1;
+          pf[mb][k2][i] = pack_bf16(p0, p1);
+        }
+      l_run[mb] += lsum;
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    // O^T += V^T P^T, V^T fragments by transpose reads of the raw value tile
+    const int vbase_off = KVS ? 0 : L::RAW;
+    auto vfrag = [&](int db, int k2) -> u32x4 {
+      const int off = vbase_off + ((db & 1) ? voff1 : voff0) + 128 * (db >> 1) + (16 * k2) * (2 * D);
+      const u32x2 lo = lds_read_tr16(sp + off);
+      const u32x2 hi = lds_read_tr16(sp + off + 8 * (2 * D));
+      return u32x4{lo[0], lo[1], hi[0], hi[1]};
+    };
+    {
+      constexpr int NG = 2 * NDB / FG;
+      u32x4 vf[2][FG];
+#pragma unroll
+      for (int i = 0; i < FG; ++i) vf[0][i] = vfrag(i >> 1, i & 1);
+#pragma unroll
+      for (int g = 0; g < NG; ++g) {
+        if (g + 1 < NG) {
+#pragma unroll
+          for (int i = 0; i < FG; ++i) {
+            const int f = FG * (g + 1) + i;
+            vf[(g + 1) & 1][i] = vfrag(f >> 1, f & 1);
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < FG; ++i) {
+          const int f = FG * g + i;
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb)
+            oacc[mb][f >> 1] = mfma32x32x16(vf[g & 1][i], pf[mb][f & 1], oacc[mb][f >> 1]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  };
+
+  // ---- KV loop, unrolled by the ring depth so every stage is a fixed object ----
+  // The tile count is padded up to a multiple of the ring depth; padding tiles
+  // lie past the last query token, so every key in them is masked.
+  const int ktp = kt0 + (kt1 - kt0 + NST) / NST * NST - 1;  // last (padded) tile
+  if constexpr (NST == 3) {
+    issue_loads(kt0, IC<0>{});
+    issue_loads(kt0 + 1, IC<1>{});
+    wait_vmcnt<0>();
+    __syncthreads();
+#pragma unroll
+    for (int m = 0; m < IPT; ++m) rotate_item(IC<0>{}, 0, m);
+    __syncthreads();
+    // one tile: prefetch tile kt+2, compute tile kt while rotating tile kt+1
+    auto step = [&](int kt, auto s) {
+      constexpr int S0 = decltype(s)::value;
+      if (kt + 2 <= ktp) issue_loads(kt + 2, IC<(S0 + 2) % 3>{});
+      compute(kt, s, (kt - kt0) & 1, true, IC<(S0 + 1) % 3>{}, (kt - kt0 + 1) & 1);
+      wait_vmcnt<0>();
+      __syncthreads();
+    };
+    for (int kt = kt0; kt <= ktp; kt += 3) {
+      step(kt, IC<0>{});
+      step(kt + 1, IC<1>{});
+      step(kt + 2, IC<2>{});
+    }
+  } else {
+    issue_loads(kt0, IC<0>{});
+    // one tile: rotate it, prefetch the next, compute it
+    auto step = [&](int kt, auto s) {
+      constexpr int S0 = decltype(s)::value;
+      wait_vmcnt<0>();
+      __syncthreads();  // tile kt visible; every wave is past tile kt-1
+#pragma unroll
+      for (int m = 0; m < IPT; ++m) rotate_item(s, 0, m);
+      if (kt + 1 <= ktp) issue_loads(kt + 1, IC<1 - S0>{});
+      __syncthreads();  // slab visible
+      compute(kt, s, 0, false, s, 0);
+    };
+    for (int kt = kt0; kt <= ktp; kt += 2) {
+      step(kt, IC<0>{});
+      step(kt + 1, IC<1>{});
+    }
+  }
+
+  // ---- epilogue: O / l ----
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    const float lt = l_run[mb] + __shfl_xor(l_run[mb], 32);
+    if (!row_ok[mb] || ((ovf >> mb) & 1)) continue;
+    const float inv = 1.f / lt;
+    const size_t obase = (((size_t)b * S + tq[mb]) * a.Hq + hq[mb]) * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int dim = 32 * db + 8 * g4 + 4 * hl;
+        const float o0 = oacc[mb][db][4 * g4 + 0] * inv, o1 = oacc[mb][db][4 * g4 + 1] * inv;
+        const float o2 = oacc[mb][db][4 * g4 + 2] * inv, o3 = oacc[mb][db][4 * g4 + 3] * inv;
+        if constexpr (OBF) {
+          u32x2 pk = {pack_bf16(o0, o1), pack_bf16(o2, o3)};
+          *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.out) + obase + dim) = pk;
+        } else {
+          *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + obase + dim) =
+              f32x4{o0, o1, o2, o3};
+        }
+      }
+  }
+
+  // ---- rows flagged above: exact recompute with the known row max ----
+  // One wave per row, lanes over head dims; taken only when some row's score
+  // grew 2^64 past its first visible tile (never for normalised data).
+  ovf |= __shfl_xor(ovf, 32);
+  if (__any(ovf)) {
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      unsigned long long rows = __ballot(((ovf >> mb) & 1) && row_ok[mb]) & 0xffffffffull;
+      while (rows) {
+        const int src_lane = __builtin_ctzll(rows);
+        rows &= rows - 1;
+        const int t = __shfl(tq[mb], src_lane), h = __shfl(hq[mb], src_lane);
+        const float mref = __shfl(m_seen[mb], src_lane);
+        exact_row<D, KVS, OBF>(a, b, hkv, t, h, mref, gtab);
+      }
+    }
+  }
+}
+
+template <int D, int G, bool KVS, bool OBF, int SW, int NST, int MB>
+hipError_t launch(const PrefillArgs& a, hipStream_t st) {
+  constexpr int TQ = NW * 32 * MB / G;
+  PrefillArgs x = a;
+  x.nq = (a.S + TQ - 1) / TQ;
+  x.nheads = a.B * a.Hkv;
+  const long long nblk = (long long)x.nq * x.nheads;
+  if (nblk == 0) return hipSuccess;
+  if (nblk > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((prefill_kernel<D, G, KVS, OBF, SW, NST, MB>), dim3((unsigned)nblk),
+                     dim3(NW * 64), 0, st, x);
+  return hipGetLastError();
+}
+
+}  // namespace pf
+}  // namespace g4a

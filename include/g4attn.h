@@ -43,7 +43,9 @@
  *     Inside the kernels bf16 inputs are multiplied on the matrix cores with
  *     fp32 accumulation; f32 inputs are computed in fp32 throughout.
  *   - Supported shapes: d in {256, 512} for bf16 inputs, d in {64, 128, 256,
- *     512} for f32 inputs; G = Hq / Hkv in {1, 2, 4, 8}.
+ *     512} for f32 inputs; G = Hq / Hkv in {1, 2, 4, 8}.  For bf16 inputs
+ *     with separate K and V and d = 512, at most 64 pairs may rotate
+ *     (p <= 0.25); other combinations return G4A_EUNSUPPORTED.
  */
 #ifndef G4ATTN_H
 #define G4ATTN_H

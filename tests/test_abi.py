@@ -75,7 +75,7 @@ def dec(**kw):
     (dict(Hkv=0), -1), (dict(Hq=5), -1), (dict(d=255), -1), (dict(window=-1), -1),
     (dict(theta=0.0), -1), (dict(theta=float("nan")), -1), (dict(p=1.5), -1),
     (dict(p=-0.1), -1), (dict(p=float("nan")), -1), (dict(i=2), -1), (dict(o=3), -1),
-    (dict(d=128), -2), (dict(Hq=6, Hkv=2), -2), (dict(Hq=32, Hkv=2), -2), (dict(i=0, o=1), -2),
+    (dict(d=128), -2), (dict(d=512, p=0.5), -2), (dict(Hq=6, Hkv=2), -2), (dict(Hq=32, Hkv=2), -2), (dict(i=0, o=1), -2),
     (dict(q=A + 8), -3), (dict(out=4 * A + 4), -3), (dict(pos=5 * A + 2), -3),
 ])
 def test_local_prefill_validation(kw, code):

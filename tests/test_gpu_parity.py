@@ -51,7 +51,7 @@ SMALL = [
     inputs.Layer("local", 1, 700, 16, 8, 256, 256, 1e4, 1.0),
     inputs.Layer("local", 1, 200, 2, 2, 256, 1, 1e4, 1.0),
     inputs.Layer("global", 1, 150, 4, 1, 256, 0, 1e6, 0.5),
-    inputs.Layer("local", 1, 190, 8, 2, 512, 40, 1e4, 1.0),
+    inputs.Layer("local", 1, 190, 8, 2, 512, 40, 1e4, 0.25),
     inputs.Layer("global", 1, 129, 2, 1, 512, 0, 1e4, 0.0),
     inputs.Layer("local", 1, 100, 4, 4, 256, 0, 1e4, 0.25),
 ]
@@ -169,3 +169,26 @@ def test_decode_equals_last_prefill_row():
                     torch.tensor([S - 1], dtype=torch.int32, device=DEV), 0, 1e6, 0.25)
     torch.cuda.synchronize()
     assert (dec - pre[:, S - 1]).abs().max().item() <= 1e-2
+
+
+@pytest.mark.parametrize("kind", ["global", "local"])
+def test_score_far_above_first_tile_takes_exact_path(kind):
+    """A key whose score lies ~130 (base 2) above the row's first visible tile
+    sends the row to the exact recompute path; the result must still match."""
+    if kind == "global":
+        layer = inputs.Layer("global", 1, 200, 8, 1, 512, 0, 1e6, 0.25)
+    else:
+        layer = inputs.Layer("local", 1, 300, 4, 2, 256, 128, 1e4, 1.0)
+    q, k, v, pos = inputs.prefill_inputs(layer, 93, 0, torch.bfloat16, DEV)
+    q = torch.ones_like(q)
+    k = k.clone()
+    k[:, :64] = 0          # rows' first tiles score exactly 0
+    k[:, 150] = 8.0        # scores of key 150 are ~100 natural units
+    if kind == "global":
+        v = k
+        out = g4.global_prefill(q, k, pos, 0, layer.theta, layer.p)
+    else:
+        out = g4.local_prefill(q, k, v, pos, layer.window, layer.theta, layer.p)
+    torch.cuda.synchronize()
+    ref = oracle_prefill(layer, q, k, v, pos, layer.window)
+    assert_parity(out, ref, torch.bfloat16, f"overflow {kind}")
