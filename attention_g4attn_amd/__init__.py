@@ -70,28 +70,46 @@ def _check(rc, where):
         raise G4AttnError(rc, where)
 
 
-def local_prefill(q, k, v, pos, window, theta=1e4, p=1.0, out=None, out_dtype=None):
+def prefill_workspace_bytes(B, S, Hkv, d, p, in_dtype=BF16):
+    return int(_g4lib().g4attn_prefill_workspace_bytes(B, S, Hkv, d, float(p), int(in_dtype)))
+
+
+def _workspace(need, workspace, device):
+    if workspace is None:
+        return _torch().empty(max(need, 16), dtype=_torch().uint8, device=device)
+    return workspace
+
+
+def _nbytes(t):
+    return t.numel() * t.element_size()
+
+
+def local_prefill(q, k, v, pos, window, theta=1e4, p=1.0, out=None, out_dtype=None,
+                  workspace=None):
     """Causal sliding-window attention, separate K and V (g4attn_local_prefill)."""
-    _dev(q, k, v, pos, out)
+    _dev(q, k, v, pos, out, workspace)
     B, S, Hq, d = q.shape
     Hkv = k.shape[2]
     out = _out((B, S, Hq, d), out, out_dtype, q.device)
+    ws = _workspace(prefill_workspace_bytes(B, S, Hkv, d, p, _code(q)), workspace, q.device)
     rc = _g4lib().g4attn_local_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(pos), B, S, Hq,
                                      Hkv, d, int(window), float(theta), float(p), _code(q),
-                                     _code(out), _stream())
+                                     _code(out), _ptr(ws), _nbytes(ws), _stream())
     _check(rc, "g4attn_local_prefill")
     return out
 
 
-def global_prefill(q, kv, pos, window=0, theta=1e6, p=0.25, out=None, out_dtype=None):
+def global_prefill(q, kv, pos, window=0, theta=1e6, p=0.25, out=None, out_dtype=None,
+                   workspace=None):
     """Causal attention with keys identical to values (g4attn_global_prefill)."""
-    _dev(q, kv, pos, out)
+    _dev(q, kv, pos, out, workspace)
     B, S, Hq, d = q.shape
     Hkv = kv.shape[2]
     out = _out((B, S, Hq, d), out, out_dtype, q.device)
+    ws = _workspace(prefill_workspace_bytes(B, S, Hkv, d, p, _code(q)), workspace, q.device)
     rc = _g4lib().g4attn_global_prefill(_ptr(q), _ptr(kv), _ptr(out), _ptr(pos), B, S, Hq, Hkv, d,
                                       int(window), float(theta), float(p), _code(q), _code(out),
-                                      _stream())
+                                      _ptr(ws), _nbytes(ws), _stream())
     _check(rc, "g4attn_global_prefill")
     return out
 
@@ -111,10 +129,9 @@ def decode(q, k_cache, v_cache, pos, window, theta, p, out=None, workspace=None,
     B, Hq, d = q.shape
     _, Hkv, C, _ = k_cache.shape
     out = _out((B, Hq, d), out, out_dtype, q.device)
-    need = decode_workspace_bytes(B, Hq, Hkv, d, C, window)
-    if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
-    nbytes = workspace.numel() * workspace.element_size()
+    workspace = _workspace(decode_workspace_bytes(B, Hq, Hkv, d, C, window), workspace,
+                           q.device)
+    nbytes = _nbytes(workspace)
     rc = _g4lib().g4attn_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out), _ptr(pos), B, Hq,
                               Hkv, d, C, int(window), float(theta), float(p), _code(q),
                               _code(out), _ptr(workspace), nbytes, _stream())

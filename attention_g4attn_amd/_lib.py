@@ -12,8 +12,9 @@ _LIB = None
 # names and argtypes, in the order include/g4attn.h declares them
 P, I, F, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
 SIGNATURES = {
-    "g4attn_local_prefill": ([P, P, P, P, P, I, I, I, I, I, I, F, F, I, I, P], I),
-    "g4attn_global_prefill": ([P, P, P, P, I, I, I, I, I, I, F, F, I, I, P], I),
+    "g4attn_prefill_workspace_bytes": ([I, I, I, I, F, I], Z),
+    "g4attn_local_prefill": ([P, P, P, P, P, I, I, I, I, I, I, F, F, I, I, P, Z, P], I),
+    "g4attn_global_prefill": ([P, P, P, P, I, I, I, I, I, I, F, F, I, I, P, Z, P], I),
     "g4attn_decode": ([P, P, P, P, P, I, I, I, I, I, I, F, F, I, I, P, Z, P], I),
     "g4attn_decode_workspace_bytes": ([I, I, I, I, I, I], Z),
     "g4attn_strerror": ([I], ctypes.c_char_p),

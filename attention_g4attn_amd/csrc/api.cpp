@@ -49,9 +49,16 @@ int finish(hipError_t e) {
   return G4A_EHIP;
 }
 
+// bytes of the rotated key slab a bf16 prefill needs (0 for f32 inputs)
+size_t prefill_ws_bytes(int B, int S, int Hkv, int d, int n_rot, int in_dtype) {
+  if (in_dtype != G4A_BF16) return 0;
+  return (size_t)B * S * Hkv * g4a::prefill_slab_dims(d, n_rot) * 2;
+}
+
 int prefill(const void* q, const void* k, const void* v, void* out, const int32_t* pos, int B,
             int S, int Hq, int Hkv, int d, int window, float theta, float p, int in_dtype,
-            int out_dtype, void* stream, bool kv_shared) {
+            int out_dtype, void* workspace, size_t workspace_bytes, void* stream,
+            bool kv_shared) {
   if (B < 0 || S < 0) return G4A_EINVAL;
   int rc = check_common(Hq, Hkv, d, window, theta, p, in_dtype, out_dtype);
   if (rc) return rc;
@@ -74,36 +81,41 @@ int prefill(const void* q, const void* k, const void* v, void* out, const int32_
   a.D = d;
   a.window = window;
   a.n_rot = rotated_pairs(d, p);
-  {
-    const int nrc = (a.n_rot + 3) / 4;  // 16-byte chunks holding rotated pairs
-    int l2 = 0;
-    while ((1 << l2) < nrc) ++l2;
-    a.nrc_log2 = l2;
-  }
   a.log2_theta = log2((double)theta);
   a.scale = (float)(1.0 / sqrt((double)d));
   a.scale_log2e = (float)(1.4426950408889634 / sqrt((double)d));
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (in_dtype == G4A_F32) return finish(g4a::launch_prefill_f32(a, st));
-  if (!g4a::prefill_supported(d, kv_shared, a.n_rot)) return G4A_EUNSUPPORTED;
+  if (!g4a::prefill_supported(d)) return G4A_EUNSUPPORTED;
+  const size_t need = prefill_ws_bytes(B, S, Hkv, d, a.n_rot, in_dtype);
+  if (!workspace || workspace_bytes < need) return G4A_EWORKSPACE;
+  if (misaligned(workspace)) return G4A_EALIGN;
+  a.ws = workspace;
   return finish(g4a::launch_prefill_bf16(a, kv_shared, out_dtype == G4A_BF16, st));
 }
 
 }  // namespace
 
+G4A_API size_t g4attn_prefill_workspace_bytes(int B, int S, int Hkv, int d, float p,
+                                              int in_dtype) {
+  if (B < 0 || S < 0 || Hkv <= 0 || d <= 0 || !(p >= 0.f && p <= 1.f)) return 0;
+  return prefill_ws_bytes(B, S, Hkv, d, rotated_pairs(d, p), in_dtype);
+}
+
 G4A_API int g4attn_local_prefill(const void* q, const void* k, const void* v, void* out,
                                  const int32_t* pos, int B, int S, int Hq, int Hkv, int d,
                                  int window, float theta, float p, int in_dtype, int out_dtype,
-                                 void* stream) {
+                                 void* workspace, size_t workspace_bytes, void* stream) {
   return prefill(q, k, v, out, pos, B, S, Hq, Hkv, d, window, theta, p, in_dtype, out_dtype,
-                 stream, k == v);
+                 workspace, workspace_bytes, stream, k == v);
 }
 
 G4A_API int g4attn_global_prefill(const void* q, const void* kv, void* out, const int32_t* pos,
                                   int B, int S, int Hq, int Hkv, int d, int window, float theta,
-                                  float p, int in_dtype, int out_dtype, void* stream) {
+                                  float p, int in_dtype, int out_dtype, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
   return prefill(q, kv, kv, out, pos, B, S, Hq, Hkv, d, window, theta, p, in_dtype, out_dtype,
-                 stream, true);
+                 workspace, workspace_bytes, stream, true);
 }
 
 G4A_API size_t g4attn_decode_workspace_bytes(int B, int Hq, int Hkv, int d, int capacity,
@@ -166,7 +178,7 @@ G4A_API const char* g4attn_strerror(int status) {
     case G4A_EINVAL: return "invalid argument";
     case G4A_EUNSUPPORTED: return "unsupported head dim, group size or dtype pair";
     case G4A_EALIGN: return "tensor pointer not 16-byte aligned";
-    case G4A_EWORKSPACE: return "decode workspace missing or too small";
+    case G4A_EWORKSPACE: return "workspace missing or too small";
     case G4A_EHIP: return "HIP launch failed (see g4attn_last_hip_error)";
   }
   return "unknown status";

@@ -13,8 +13,8 @@ struct PrefillArgs {
   const void* v;  // equals k for the K=V layer
   void* out;
   const int32_t* pos;
+  void* ws;       // rotated key slab [B, S, Hkv, prefill_slab_dims(D, n_rot)] bf16
   int B, S, Hq, Hkv, D, window, n_rot;
-  int nrc_log2;       // ceil(log2(ceil(n_rot / 4))): rotated 16-byte chunks, rounded up
   double log2_theta;
   float scale_log2e;  // log2(e) / sqrt(D)
   float scale;        // 1 / sqrt(D)
@@ -38,8 +38,9 @@ struct DecodeArgs {
 };
 
 // bf16 inputs, matrix-core path; D in {256, 512}, G in {1, 2, 4, 8}.
-// Separate K and V with D = 512 needs n_rot <= 64 (see prefill_supported).
-bool prefill_supported(int D, bool kv_shared, int n_rot);
+bool prefill_supported(int D);
+// key dims kept in the rotated slab (workspace) for this head dim and n_rot
+int prefill_slab_dims(int D, int n_rot);
 hipError_t launch_prefill_bf16(const PrefillArgs& a, bool kv_shared, bool out_bf16,
                                hipStream_t st);
 // per-family launchers (one translation unit each)

@@ -14,24 +14,26 @@
 //     share one KV head, so every staged KV tile feeds all G heads.  Row r is
 //     token t0 + r/G, head hkv*G + r%G; wave w owns rows RW*w .. RW*w+RW-1,
 //     as MB blocks of 32 that share every K/V fragment read from LDS.
-//   - KV tiles of 32 keys stream from HBM straight into an NST-deep LDS ring
-//     (16-byte direct-to-LDS loads, no staging registers), issued two tiles
-//     ahead when NST = 3.  Raw tiles are row-major with 16-byte chunks
-//     XOR-swizzled by row so both read patterns below are bank-conflict free.
-//   - The rotated part of each key (chunks holding pairs < n_rot) is written
-//     once per tile into a small "slab" by all threads, interleaved with the
-//     score products of the previous tile; the rest of the score operand is
-//     read from the raw tile.
+//   - Keys are rotated once, before the attention kernel, by a pass that
+//     writes the first SW dims of every key, rotated, into a workspace slab
+//     (SW = 128 when only pairs < 64 turn, as for p-RoPE at d = 512; else d).
+//     Queries are rotated in registers when the workgroup loads them.
+//   - KV tiles of 32 keys (slab rows, plus the raw rows the scores or values
+//     still need) stream from HBM straight into an NST-deep LDS ring (16-byte
+//     direct-to-LDS loads, no staging registers), requested two tiles ahead
+//     when NST = 3.  Rows are stored with 16-byte chunks XOR-swizzled by row
+//     so both read patterns below are free of bank conflicts.
 //   - Scores are computed transposed, S^T = K~ Q~^T, so each lane owns one
 //     query row per block: the softmax needs one exchange with lane l^32 and
-//     the output rescale is a per-lane scalar; P goes from the score registers
+//     the row statistics are per-lane scalars; P goes from the score registers
 //     straight into the B operand of O^T += V^T P^T.
 //   - The value operand V^T is read from the raw row-major tile with the LDS
 //     transpose read (ds_read_b64_tr_b16): 4 consecutive keys of one dim per
 //     lane per read.  For K=V this is the same raw tile the scores read.
-//   - Online softmax in fp32 (base 2, scale folded with log2 e); the output is
-//     rescaled only when the running max grows by more than 2^8.
-//   - Tiles outside a wave's causal band are skipped; only edge tiles are
+//   - Softmax in fp32 (base 2, scale folded with log2 e) against a reference
+//     max fixed at the first tile a row sees, so O is never rescaled; a row
+//     whose scores later exceed that reference by 2^64 is recomputed exactly.
+//   - A wave skips tiles none of its rows can see; only edge tiles are
 //     masked.  Grid order: KV heads fastest, then query tiles from the longest
 //     causal row down, so each XCD streams one KV head's tiles in step.
 #pragma once
@@ -47,10 +49,14 @@ constexpr int NW = 4;   // waves per workgroup
 constexpr int BN = 32;  // keys per KV tile
 constexpr int FG = 2;   // LDS fragments per software-pipelined group
 
-// 16-byte chunk swizzle of row r: rows r..r+7 map one chunk to 8 different
-// bank groups, and 4 consecutive rows (r % 4 == 0) map two adjacent chunks to
-// 8 different bank groups.
-__device__ __forceinline__ int swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
+// 16-byte chunk swizzle of row r: chunk c of the row is stored at chunk
+// c ^ swz(r).  The 64 LDS banks of gfx950 span 256 bytes (16 chunks), and a
+// 16-byte read is served 16 lanes at a time, an 8-byte read 32 lanes at a time.
+// swz is a bit swap of r % 16, so (a) one chunk of 16 consecutive rows lands on
+// 16 different bank groups (score operand: lane = key row), and (b) 4
+// consecutive rows (r % 4 == 0) put 4 aligned adjacent chunks into 16 different
+// bank groups (value operand: transpose reads, 4 rows x 4 chunks per 32 lanes).
+__device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
@@ -79,11 +85,6 @@ __device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rs, uint32_t vo
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(ldst),
                                            16, voff, soff, 0, 0);
 }
-__device__ __forceinline__ void lds_dma4(__amdgpu_buffer_rsrc_t rs, uint32_t voff,
-                                         unsigned char* ldst) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(ldst),
-                                           4, voff, 0, 0, 0);
-}
 
 // wait until at most n vector-memory operations of this wave are in flight
 template <int N>
@@ -92,18 +93,24 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// LDS layout.  Every ring stage is its own __shared__ object (raw K tile, raw
-// V tile when separate, then the tile's key positions), so the compiler can
-// tell the stage being read from the stages the direct loads are filling and
-// does not wait for those loads before reading.
+// LDS layout.  Every ring stage is its own __shared__ object, so the compiler
+// can tell the stage being read from the stages the direct loads are filling
+// and does not wait for those loads before reading.  A stage holds one KV tile:
+//   [slab]  the first SW dims of the 32 keys, already rotated (from the
+//           workspace written by rope_keys_kernel), BN x SW bf16;
+//   [raw K] the raw key rows (K=V: the one tensor, read raw as the values),
+//           needed when SW < D (score dims >= SW) or for K=V;
+//   [raw V] the raw value rows when K and V are separate.
 template <int D, bool KVS, int SW, int NST>
 struct Lds {
-  static constexpr int RAW = BN * D * 2;             // one raw tile, bytes
-  static constexpr int NT = KVS ? 1 : 2;             // raw tensors per stage
-  static constexpr int POS = NT * RAW;               // key positions (256 B) in a stage
-  static constexpr int STAGE = POS + 256;
-  static constexpr int SLAB = BN * SW * 2;           // one rotated slab
-  static constexpr int TOTAL = NST * STAGE + 2 * SLAB + (D / 2) * 8;
+  static constexpr int RAW = BN * D * 2;    // one raw tile, bytes
+  static constexpr int SLAB = BN * SW * 2;  // one rotated slab tile
+  static constexpr int NRAW = KVS ? 1 : (SW < D ? 2 : 1);
+  static constexpr int KOFF = SLAB;                                     // raw K rows
+  static constexpr int VOFF = KVS ? SLAB : (SW < D ? SLAB + RAW : SLAB);  // raw V rows
+  static constexpr int STAGE = SLAB + NRAW * RAW;
+  static constexpr int NLD = STAGE / (1024 * NW);  // direct loads per lane per tile
+  static constexpr int TOTAL = NST * STAGE + (D / 2) * 8;
 };
 
 template <int N>
@@ -114,25 +121,58 @@ __device__ __forceinline__ T& lds_at(unsigned char* base, int off) {
   return *reinterpret_cast<T*>(base + off);
 }
 
+// Rotated key slab, one pass over the keys: ws[row][0 .. SW) = the first SW
+// dims of k[row] with pair t < n_rot turned by pos * theta^(-2t/D), rounded to
+// bf16; row = (b*S + j)*Hkv + hkv.  One 16-byte chunk (4 pairs) per thread.
+template <int SW>
+__global__ void __launch_bounds__(256) rope_keys_kernel(const uint16_t* __restrict__ k,
+                                                       uint16_t* __restrict__ ws,
+                                                       const int32_t* __restrict__ pos,
+                                                       long long nchunks, int Hkv, int D, int n_rot,
+                                                       double log2_theta) {
+  constexpr int CPR = SW / 8;  // chunks per slab row
+  for (long long i = blockIdx.x * 256ll + threadIdx.x; i < nchunks;
+       i += (long long)gridDim.x * 256) {
+    const long long row = i / CPR;
+    const int c = (int)(i % CPR);
+    u32x4 x = *reinterpret_cast<const u32x4*>(k + row * D + 8 * c);
+    if (4 * c < n_rot) {
+      const int p = pos[row / Hkv];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int t = 4 * c + e;
+        float cs, sn;
+        rope_cs_accurate(p, rope_rev_per_pos(t, D, log2_theta), cs, sn);
+        const float x0 = bf_lo(x[e]), x1 = bf_hi(x[e]);
+        const uint32_t r = pack_bf16(x0 * cs - x1 * sn, x0 * sn + x1 * cs);
+        x[e] = t < n_rot ? r : x[e];
+      }
+    }
+    *reinterpret_cast<u32x4*>(ws + row * SW + 8 * c) = x;
+  }
+}
+
 // Exact attention row (token t, query head h) for a wave, with the row max m
 // (base-2 scaled) known in advance, so no rescaling is needed.  Lane e owns
 // dims e*(D/64) .. +D/64-1; every key's score is a wave-wide reduction.
-template <int D, bool KVS, bool OBF>
-__device__ __noinline__ void exact_row(const PrefillArgs& a, int b, int hkv, int t, int h,
-                                       float m, const double* gtab) {
+// Keys are read raw and rotated here.
+template <int D, bool OBF>
+__device__ __noinline__ void exact_row(const uint16_t* qp, const uint16_t* kp, const uint16_t* vp,
+                                       void* outp, const int32_t* posp, int S, int Hq, int Hkv,
+                                       int W, int n_rot, float scale_log2e, int b, int hkv, int t,
+                                       int h, float m, const double* gtab) {
   constexpr int E = D / 64;  // dims per lane, even
   const int lane = threadIdx.x & 63;
-  const int S = a.S, W = a.window;
-  const uint16_t* qr = static_cast<const uint16_t*>(a.q) + (((size_t)b * S + t) * a.Hq + h) * D;
-  const int qp = a.pos[(size_t)b * S + t];
+  const uint16_t* qr = qp + (((size_t)b * S + t) * Hq + h) * D;
+  const int qpos = posp[(size_t)b * S + t];
   float qv[E];
 #pragma unroll
   for (int e = 0; e < E; e += 2) {
     const int d0 = lane * E + e;
     float x0 = bf_lo(qr[d0]), x1 = bf_lo(qr[d0 + 1]);
-    if (d0 / 2 < a.n_rot) {
+    if (d0 / 2 < n_rot) {
       float c, s;
-      rope_cs_accurate(qp, gtab[d0 / 2], c, s);
+      rope_cs_accurate(qpos, gtab[d0 / 2], c, s);
       const float y0 = x0 * c - x1 * s, y1 = x0 * s + x1 * c;
       x0 = y0;
       x1 = y1;
@@ -145,42 +185,42 @@ __device__ __noinline__ void exact_row(const PrefillArgs& a, int b, int hkv, int
   for (int e = 0; e < E; ++e) o[e] = 0.f;
   const int lo = W > 0 ? max(0, t - W + 1) : 0;
   for (int j = lo; j <= t; ++j) {
-    const size_t row = ((size_t)b * S + j) * a.Hkv + hkv;
-    const uint16_t* kr = static_cast<const uint16_t*>(a.k) + row * D;
-    const uint16_t* vr = static_cast<const uint16_t*>(a.v) + row * D;
-    const int kp = a.pos[(size_t)b * S + j];
+    const size_t row = ((size_t)b * S + j) * Hkv + hkv;
+    const uint16_t* kr = kp + row * D;
+    const uint16_t* vr = vp + row * D;
+    const int kpos = posp[(size_t)b * S + j];
     float part = 0.f;
 #pragma unroll
     for (int e = 0; e < E; e += 2) {
       const int d0 = lane * E + e;
       float x0 = bf_lo(kr[d0]), x1 = bf_lo(kr[d0 + 1]);
-      if (d0 / 2 < a.n_rot) {
+      if (d0 / 2 < n_rot) {
         float c, s;
-        rope_cs_accurate(kp, gtab[d0 / 2], c, s);
+        rope_cs_accurate(kpos, gtab[d0 / 2], c, s);
         const float y0 = x0 * c - x1 * s, y1 = x0 * s + x1 * c;
         x0 = y0;
         x1 = y1;
       }
       part += qv[e] * x0 + qv[e + 1] * x1;
     }
-    const float p = __builtin_amdgcn_exp2f(wave_sum(part) * a.scale_log2e - m);
+    const float p = __builtin_amdgcn_exp2f(wave_sum(part) * scale_log2e - m);
     l += p;
 #pragma unroll
     for (int e = 0; e < E; ++e) o[e] += p * bf_lo(vr[lane * E + e]);
   }
-  const size_t ob = (((size_t)b * S + t) * a.Hq + h) * D + lane * E;
+  const size_t ob = (((size_t)b * S + t) * Hq + h) * D + lane * E;
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     if constexpr (OBF)
-      static_cast<uint16_t*>(a.out)[ob + e] = (uint16_t)(pack_bf16(o[e] / l, 0.f) & 0xffffu);
+      static_cast<uint16_t*>(outp)[ob + e] = (uint16_t)(pack_bf16(o[e] / l, 0.f) & 0xffffu);
     else
-      static_cast<float*>(a.out)[ob + e] = o[e] / l;
+      static_cast<float*>(outp)[ob + e] = o[e] / l;
   }
 }
 
-// SW = dims of each key kept rotated in the slab: D/4 (pairs < D/8 may turn,
-// e.g. p = 0.25) or D (any p).  Score k-steps s < SW/16 read the slab, the
-// others the raw tile.
+// SW = key dims the score product reads from the rotated slab: 128 (only
+// pairs < 64 may turn, e.g. p = 0.25 at D = 512) or D (any p).  Score k-steps
+// s < SW/16 read the slab, the others the raw key tile.
 template <int D, int G, bool KVS, bool OBF, int SW, int NST, int MB>
 __global__ void __launch_bounds__(NW * 64, 1) prefill_kernel(PrefillArgs a) {
   constexpr int RW = 32 * MB;          // rows per wave
@@ -189,18 +229,13 @@ __global__ void __launch_bounds__(NW * 64, 1) prefill_kernel(PrefillArgs a) {
   constexpr int NDS = D / 16;          // k-steps of the score product
   constexpr int NSS = SW / 16;         // k-steps read from the slab
   constexpr int NDB = D / 32;          // 32-dim blocks of the output
-  constexpr int RPI = 1024 / (2 * D);  // rows per direct-load instruction (64 lanes x 16 B)
-  constexpr int LPT = BN / RPI / NW;   // direct loads per thread per tensor per tile
-  constexpr int SWC = SW / 8;          // slab chunks per key
-  constexpr int IPT = BN * SWC / (NW * 64);  // rotation items per thread per tile
-  constexpr int RDR = NW * 64 / SWC;   // rows between a thread's rotation items
   using L = Lds<D, KVS, SW, NST>;
   static_assert(L::TOTAL <= 160 * 1024, "LDS budget");
-  static_assert(SWC >= 8 && IPT >= 1 && NDS % 4 == 0 && NSS % 4 == 0, "tile shape");
+  static_assert(SW >= 128 && SW <= D && NDS % 8 == 0 && NSS % 8 == 0, "tile shape");
+  static_assert(L::STAGE % (1024 * NW) == 0, "stage = whole direct loads per wave");
   __shared__ __attribute__((aligned(16))) unsigned char st0[L::STAGE];
   __shared__ __attribute__((aligned(16))) unsigned char st1[L::STAGE];
   __shared__ __attribute__((aligned(16))) unsigned char st2[NST == 3 ? L::STAGE : 16];
-  __shared__ __attribute__((aligned(16))) unsigned char slabs[2 * L::SLAB];
   __shared__ double gtab[D / 2];
   // ring stage s (a compile-time constant) -> its LDS object
   auto stp = [&](auto s) -> unsigned char* {
@@ -257,62 +292,46 @@ __global__ void __launch_bounds__(NW * 64, 1) prefill_kernel(PrefillArgs a) {
   const int kt0 = klo / BN, kt1 = (t_end - 1) / BN;
 
   // ---- direct HBM -> LDS loads of one tile ----
-  // Per tile a buffer resource covers the rows kv0 .. S-1 (rows past the end
-  // read as zeros); each lane's 32-bit offset inside a tile is fixed.
+  // Per tile a buffer resource covers the rows kv0 .. kv0+rows-1 of this KV
+  // head (and the matching slab rows); each lane's 32-bit offset is fixed.
   const uint32_t row_bytes = (uint32_t)(a.Hkv * D * 2);
+  const uint32_t srow_bytes = (uint32_t)(a.Hkv * SW * 2);
   const uint16_t* kbase = static_cast<const uint16_t*>(a.k) + ((size_t)b * S * a.Hkv + hkv) * D;
   const uint16_t* vbase = static_cast<const uint16_t*>(a.v) + ((size_t)b * S * a.Hkv + hkv) * D;
-  const int32_t* pbase = a.pos + (size_t)b * S;
+  const uint16_t* sbase_g = static_cast<const uint16_t*>(a.ws) + ((size_t)b * S * a.Hkv + hkv) * SW;
+  // one tensor's tile: rows of RB bytes in HBM (stride rbytes), placed at dst
+  // with 16-byte chunks swizzled by row
+  auto load_tensor = [&](auto rbc, const uint16_t* base, uint32_t rbytes, int rows,
+                         unsigned char* dst) {
+    constexpr int RB = decltype(rbc)::value;  // bytes per row in LDS
+    constexpr int CPR = RB / 16;              // chunks per row
+    constexpr int RPI = 1024 / RB;            // rows per direct load
+    constexpr int LPW = BN / RPI / NW;        // direct loads per wave
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(base, rows * rbytes - (rbytes - RB));
+    // the lane id is laundered so the offsets below are recomputed here (two
+    // or three instructions) instead of being held across the loop
+    int ln = lane;
+    int wl = __builtin_amdgcn_readfirstlane(w);
+    uint32_t rb = __builtin_amdgcn_readfirstlane(rbytes);
+    asm volatile("" : "+v"(ln), "+s"(wl), "+s"(rb));
+#pragma unroll
+    for (int n = 0; n < LPW; ++n) {
+      const int r0 = (wl * LPW + n) * RPI;  // first row of this load, wave-uniform
+      const int r = r0 + ln / CPR;
+      const uint32_t voff = (uint32_t)r * rb + ((uint32_t)((ln % CPR) ^ swz(r)) << 4);
+      lds_dma16(rs, voff, 0, dst + r0 * RB);
+    }
+  };
   auto issue_loads = [&](int kt, auto stage) {
     unsigned char* sp = stp(stage);
     // padding tiles past the sequence reload its last tile: finite data whose
     // keys are all masked for this workgroup's rows
     const int kv0 = min(kt * BN, ((S - 1) / BN) * BN);
-    const uint32_t rows = (uint32_t)min(S - kv0, BN);  // >= 1
-    const size_t toff = (size_t)kv0 * a.Hkv * D;
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase + toff, rows * row_bytes - (row_bytes - D * 2));
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase + toff, rows * row_bytes - (row_bytes - D * 2));
-    // the lane id is laundered so the offsets below are recomputed here (two
-    // or three instructions) instead of being held across the loop
-    int ln = lane;
-    int wl = __builtin_amdgcn_readfirstlane(w);
-    uint32_t rb = __builtin_amdgcn_readfirstlane(row_bytes);
-    asm volatile("" : "+v"(ln), "+s"(wl), "+s"(rb));
-#pragma unroll
-    for (int n = 0; n < LPT; ++n) {
-      const int r0 = (wl * LPT + n) * RPI;  // first row of this load, wave-uniform
-      uint32_t voff;
-      if constexpr (RPI == 1) {
-        voff = (uint32_t)r0 * rb + ((uint32_t)(ln ^ swz(r0)) << 4);
-      } else {
-        const int r = r0 + (ln >> 5);
-        voff = (uint32_t)r * rb + ((uint32_t)((ln & 31) ^ swz(r)) << 4);
-      }
-      unsigned char* dst = sp + r0 * (2 * D);
-      lds_dma16(rk, voff, 0, dst);
-      if constexpr (!KVS) lds_dma16(rv, voff, 0, dst + L::RAW);
-    }
-    if (w == 0)  // positions of the tile's keys (lanes past the end read zeros)
-      lds_dma4(make_rsrc(pbase + kv0, rows * 4), 4 * lane, sp + L::POS);
-  };
-
-  // ---- rotation of one tile's first SW dims into a slab ----
-  // item m of this thread: chunk tid % SWC of row tid / SWC + m * RDR.  The
-  // thread id is laundered so these per-lane values are recomputed at each use
-  // rather than held in registers across the KV loop.
-  auto rotate_item = [&](auto stage, int slot, int m) {
-    unsigned char* sp = stp(stage);
-    int t = tid;
-    asm volatile("" : "+v"(t));
-    const int rc_c = t % SWC;
-    const int r = t / SWC + m * RDR;
-    const int sw = (rc_c ^ swz(r)) << 4;
-    u32x4 x = lds_at<u32x4>(sp, r * (2 * D) + sw);
-    if (4 * rc_c < n_rot) {  // chunk holds at least one turning pair
-      const int p = lds_at<int>(sp, L::POS + 4 * r);
-      x = rotate_chunk_bf16(x, rc_c, p, n_rot, gtab);
-    }
-    lds_at<u32x4>(slabs, slot * L::SLAB + r * (2 * SW) + sw) = x;
+    const int rows = min(S - kv0, BN);  // >= 1
+    const size_t toff = (size_t)kv0 * a.Hkv;
+    load_tensor(IC<2 * SW>{}, sbase_g + toff * SW, srow_bytes, rows, sp);
+    if constexpr (KVS || SW < D) load_tensor(IC<2 * D>{}, kbase + toff * D, row_bytes, rows, sp + L::KOFF);
+    if constexpr (!KVS) load_tensor(IC<2 * D>{}, vbase + toff * D, row_bytes, rows, sp + L::VOFF);
   };
 
   f32x16 oacc[MB][NDB];
@@ -337,8 +356,8 @@ __global__ void __launch_bounds__(NW * 64, 1) prefill_kernel(PrefillArgs a) {
   }
   const float cs = a.scale_log2e;
 
-  // ---- one tile: scores (with the next tile's rotation interleaved), softmax, PV ----
-  auto compute = [&](int kt, auto stage, int slot, bool rot_next, auto nstage, int nslot) {
+  // ---- one tile: scores, softmax, PV ----
+  auto compute = [&](int kt, auto stage) {
     unsigned char* sp = stp(stage);
     const int kv0 = kt * BN;
     // Lane parts of the fragment offsets, recomputed per tile from a laundered
@@ -347,34 +366,39 @@ __global__ void __launch_bounds__(NW * 64, 1) prefill_kernel(PrefillArgs a) {
     asm volatile("" : "+v"(ln));
     const int l32 = ln & 31, hl = ln >> 5;
     // score operand (key l32, chunk c = 2s + hl): chunk position
-    // c ^ swz(l32) = 8*(s/4) + ((2*(s%4) + hl) ^ swz(l32))
+    // c ^ swz(l32) = 16*(s/8) + ((2*(s%8) + hl) ^ swz(l32))
     const int sw_n = swz(l32);
-    int soff[4];
+    int soff[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) soff[i] = ((2 * i + hl) ^ sw_n) << 4;
+    for (int i = 0; i < 8; ++i) soff[i] = ((2 * i + hl) ^ sw_n) << 4;
     // value operand by transpose reads: lane (g = ln/16, i = ln%16) reads row
-    // 4*(g/2) + i/4 (+8, +16*k2) at dims 32*db + 16*(g%2) + 4*(i%4)
+    // 4*(g/2) + i/4 (then +8 rows for the upper 4 keys, +16*k2) at dims
+    // 32*db + 16*(g%2) + 4*(i%4), i.e. chunk 4*db + tr_x, byte 8*(i%2)
     const int tr_i = ln & 15, tr_g = ln >> 4;
     const int tr_row = 4 * (tr_g >> 1) + (tr_i >> 2);
-    const int tr_sw = swz(tr_row);
     const int tr_x = 2 * (tr_g & 1) + ((tr_i & 3) >> 1);
-    const int voff0 = tr_row * (2 * D) + (tr_i & 1) * 8 + ((tr_x ^ tr_sw) << 4);
-    const int voff1 = tr_row * (2 * D) + (tr_i & 1) * 8 + (((4 + tr_x) ^ tr_sw) << 4);
-    const int rbase = l32 * (2 * D);
-    const int sbase = slot * L::SLAB + l32 * (2 * SW);
+    // voff[h][e]: rows tr_row + 8h, 32-dim block db with db % 4 == e
+    int voff[2][4];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        voff[h][e] = (tr_row + 8 * h) * (2 * D) + (tr_i & 1) * 8 +
+                     (((4 * e + tr_x) ^ swz(tr_row + 8 * h)) << 4);
+    const int kbase_off = L::KOFF + l32 * (2 * D);
+    const int sbase_off = l32 * (2 * SW);
 
     f32x16 sacc[MB];
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) sacc[mb] = f32x16{};
     {
-      // k-step s lives in the slab for s < NSS, in the raw tile otherwise;
+      // k-step s lives in the slab for s < NSS, in the raw key tile otherwise;
       // fragments stream in groups of FG, one group ahead
       auto frag = [&](int s) -> u32x4 {
-        if (s < NSS) return lds_at<u32x4>(slabs, sbase + 128 * (s >> 2) + soff[s & 3]);
-        return lds_at<u32x4>(sp, rbase + 128 * (s >> 2) + soff[s & 3]);
+        if (s < NSS) return lds_at<u32x4>(sp, sbase_off + 256 * (s >> 3) + soff[s & 7]);
+        return lds_at<u32x4>(sp, kbase_off + 256 * (s >> 3) + soff[s & 7]);
       };
       constexpr int NG = NDS / FG;
-      constexpr int RSTEP = NG / IPT > 0 ? NG / IPT : 1;  // groups between rotation items
       u32x4 kf[2][FG];
 #pragma unroll
       for (int i = 0; i < FG; ++i) kf[0][i] = frag(i);
@@ -389,12 +413,8 @@ __global__ void __launch_bounds__(NW * 64, 1) prefill_kernel(PrefillArgs a) {
 #pragma unroll
           for (int mb = 0; mb < MB; ++mb)
             sacc[mb] = mfma32x32x16(kf[g & 1][i], qf[mb][FG * g + i], sacc[mb]);
-        if (g % RSTEP == 0 && g / RSTEP < IPT && rot_next) rotate_item(nstage, nslot, g / RSTEP);
         __builtin_amdgcn_sched_barrier(0);
       }
-#pragma unroll
-      for (int m = (NG + RSTEP - 1) / RSTEP; m < IPT; ++m)
-        if (rot_next) rotate_item(nstage, nslot, m);
     }
 
     u32x4 pf[MB][2];
@@ -434,11 +454,10 @@ __global__ void __launch_bounds__(NW * 64, 1) prefill_kernel(PrefillArgs a) {
     __builtin_amdgcn_sched_barrier(0);
 
     // O^T += V^T P^T, V^T fragments by transpose reads of the raw value tile
-    const int vbase_off = KVS ? 0 : L::RAW;
     auto vfrag = [&](int db, int k2) -> u32x4 {
-      const int off = vbase_off + ((db & 1) ? voff1 : voff0) + 128 * (db >> 1) + (16 * k2) * (2 * D);
-      const u32x2 lo = lds_read_tr16(sp + off);
-      const u32x2 hi = lds_read_tr16(sp + off + 8 * (2 * D));
+      const int off = L::VOFF + 256 * (db >> 2) + (16 * k2) * (2 * D);
+      const u32x2 lo = lds_read_tr16(sp + off + voff[0][db & 3]);
+      const u32x2 hi = lds_read_tr16(sp + off + voff[1][db & 3]);
       return u32x4{lo[0], lo[1], hi[0], hi[1]};
     };
     {
@@ -466,25 +485,31 @@ __global__ void __launch_bounds__(NW * 64, 1) prefill_kernel(PrefillArgs a) {
       }
     }
   };
+  // a wave skips tiles where none of its rows sees a key (past its last
+  // token, before its window, or padding)
+  auto visible = [&](int kt) {
+    const int kv0 = kt * BN;
+    return wave_ok && kv0 <= tw1 && !(W > 0 && kv0 + BN - 1 <= tw0 - W);
+  };
 
   // ---- KV loop, unrolled by the ring depth so every stage is a fixed object ----
   // The tile count is padded up to a multiple of the ring depth; padding tiles
-  // lie past the last query token, so every key in them is masked.
+  // lie past the last query token, so every wave skips them.
   const int ktp = kt0 + (kt1 - kt0 + NST) / NST * NST - 1;  // last (padded) tile
   if constexpr (NST == 3) {
+    // tile kt+2 is requested while tile kt is computed; at the end of the
+    // step only tile kt+1 must have landed (vmcnt <= one tile's loads)
     issue_loads(kt0, IC<0>{});
     issue_loads(kt0 + 1, IC<1>{});
-    wait_vmcnt<0>();
+    wait_vmcnt<L::NLD>();
     __syncthreads();
-#pragma unroll
-    for (int m = 0; m < IPT; ++m) rotate_item(IC<0>{}, 0, m);
-    __syncthreads();
-    // one tile: prefetch tile kt+2, compute tile kt while rotating tile kt+1
     auto step = [&](int kt, auto s) {
       constexpr int S0 = decltype(s)::value;
-      if (kt + 2 <= ktp) issue_loads(kt + 2, IC<(S0 + 2) % 3>{});
-      compute(kt, s, (kt - kt0) & 1, true, IC<(S0 + 1) % 3>{}, (kt - kt0 + 1) & 1);
-      wait_vmcnt<0>();
+      const bool more = kt + 2 <= ktp;
+      if (more) issue_loads(kt + 2, IC<(S0 + 2) % 3>{});
+      if (visible(kt)) compute(kt, s);
+      if (more) wait_vmcnt<L::NLD>();
+      else wait_vmcnt<0>();
       __syncthreads();
     };
     for (int kt = kt0; kt <= ktp; kt += 3) {
@@ -494,16 +519,14 @@ __global__ void __launch_bounds__(NW * 64, 1) prefill_kernel(PrefillArgs a) {
     }
   } else {
     issue_loads(kt0, IC<0>{});
-    // one tile: rotate it, prefetch the next, compute it
+    wait_vmcnt<0>();
+    __syncthreads();
     auto step = [&](int kt, auto s) {
       constexpr int S0 = decltype(s)::value;
-      wait_vmcnt<0>();
-      __syncthreads();  // tile kt visible; every wave is past tile kt-1
-#pragma unroll
-      for (int m = 0; m < IPT; ++m) rotate_item(s, 0, m);
       if (kt + 1 <= ktp) issue_loads(kt + 1, IC<1 - S0>{});
-      __syncthreads();  // slab visible
-      compute(kt, s, 0, false, s, 0);
+      if (visible(kt)) compute(kt, s);
+      wait_vmcnt<0>();
+      __syncthreads();
     };
     for (int kt = kt0; kt <= ktp; kt += 2) {
       step(kt, IC<0>{});
@@ -548,12 +571,15 @@ __global__ void __launch_bounds__(NW * 64, 1) prefill_kernel(PrefillArgs a) {
         rows &= rows - 1;
         const int t = __shfl(tq[mb], src_lane), h = __shfl(hq[mb], src_lane);
         const float mref = __shfl(m_seen[mb], src_lane);
-        exact_row<D, KVS, OBF>(a, b, hkv, t, h, mref, gtab);
+        exact_row<D, OBF>(static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
+                          static_cast<const uint16_t*>(a.v), a.out, a.pos, S, a.Hq, a.Hkv, W,
+                          n_rot, cs, b, hkv, t, h, mref, gtab);
       }
     }
   }
 }
 
+// Rotated key slab for slab width SW, then the attention kernel, on stream st.
 template <int D, int G, bool KVS, bool OBF, int SW, int NST, int MB>
 hipError_t launch(const PrefillArgs& a, hipStream_t st) {
   constexpr int TQ = NW * 32 * MB / G;
@@ -563,6 +589,12 @@ hipError_t launch(const PrefillArgs& a, hipStream_t st) {
   const long long nblk = (long long)x.nq * x.nheads;
   if (nblk == 0) return hipSuccess;
   if (nblk > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  const long long nchunks = (long long)a.B * a.S * a.Hkv * (SW / 8);
+  const long long rblk = (nchunks + 255) / 256;
+  hipLaunchKernelGGL((rope_keys_kernel<SW>), dim3((unsigned)(rblk < 65536 ? rblk : 65536)),
+                     dim3(256), 0, st, static_cast<const uint16_t*>(a.k),
+                     static_cast<uint16_t*>(a.ws), a.pos, nchunks, a.Hkv, D, a.n_rot,
+                     a.log2_theta);
   hipLaunchKernelGGL((prefill_kernel<D, G, KVS, OBF, SW, NST, MB>), dim3((unsigned)nblk),
                      dim3(NW * 64), 0, st, x);
   return hipGetLastError();

@@ -7,7 +7,8 @@ namespace g4a {
 
 template <int G, bool OBF>
 static hipError_t sep512(const PrefillArgs& a, hipStream_t st) {
-  return pf::launch<512, G, false, OBF, 128, 2, 1>(a, st);
+  if (a.n_rot <= 64) return pf::launch<512, G, false, OBF, 128, 2, 1>(a, st);
+  return pf::launch<512, G, false, OBF, 512, 2, 1>(a, st);
 }
 
 template <bool OBF>
@@ -25,15 +26,13 @@ hipError_t launch_prefill_sep512(const PrefillArgs& a, bool out_bf16, hipStream_
   return out_bf16 ? sep512_g<true>(a, st) : sep512_g<false>(a, st);
 }
 
-bool prefill_supported(int D, bool kv_shared, int n_rot) {
-  if (D == 256) return true;
-  if (D == 512) return kv_shared || n_rot <= 64;
-  return false;
-}
+bool prefill_supported(int D) { return D == 256 || D == 512; }
+
+int prefill_slab_dims(int D, int n_rot) { return (D == 512 && n_rot <= 64) ? 128 : D; }
 
 hipError_t launch_prefill_bf16(const PrefillArgs& a, bool kv_shared, bool out_bf16,
                                hipStream_t st) {
-  if (!prefill_supported(a.D, kv_shared, a.n_rot)) return hipErrorInvalidValue;
+  if (!prefill_supported(a.D)) return hipErrorInvalidValue;
   if (a.D == 256) return launch_prefill_d256(a, kv_shared, out_bf16, st);
   if (kv_shared) return launch_prefill_kv512(a, out_bf16, st);
   return launch_prefill_sep512(a, out_bf16, st);

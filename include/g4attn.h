@@ -37,15 +37,14 @@
  *   - Argument errors are reported synchronously, before anything is
  *     launched, as a negative status.  Faults inside a kernel surface at the
  *     caller's next synchronisation of the stream.
- *   - Every tensor pointer must be 16-byte aligned.
+ *   - Every tensor and workspace pointer must be 16-byte aligned.
  *   - dtype codes: G4A_F32 = 0 (float32), G4A_BF16 = 1 (bfloat16).
  *     Supported (in_dtype, out_dtype): (F32, F32), (BF16, F32), (BF16, BF16).
  *     Inside the kernels bf16 inputs are multiplied on the matrix cores with
  *     fp32 accumulation; f32 inputs are computed in fp32 throughout.
  *   - Supported shapes: d in {256, 512} for bf16 inputs, d in {64, 128, 256,
- *     512} for f32 inputs; G = Hq / Hkv in {1, 2, 4, 8}.  For bf16 inputs
- *     with separate K and V and d = 512, at most 64 pairs may rotate
- *     (p <= 0.25); other combinations return G4A_EUNSUPPORTED.
+ *     512} for f32 inputs; G = Hq / Hkv in {1, 2, 4, 8}; other combinations
+ *     return G4A_EUNSUPPORTED.
  */
 #ifndef G4ATTN_H
 #define G4ATTN_H
@@ -62,8 +61,8 @@ extern "C" {
 #define G4A_EINVAL (-1)      /* null pointer, bad size, Hq % Hkv != 0, p outside [0,1],
                                 theta <= 0, window < 0, ring capacity != window */
 #define G4A_EUNSUPPORTED (-2) /* head dim, group size or dtype pair not built */
-#define G4A_EALIGN (-3)      /* a tensor pointer is not 16-byte aligned */
-#define G4A_EWORKSPACE (-4)  /* decode workspace missing or too small */
+#define G4A_EALIGN (-3)      /* a tensor or workspace pointer is not 16-byte aligned */
+#define G4A_EWORKSPACE (-4)  /* workspace missing or smaller than the size query says */
 #define G4A_EHIP (-5)        /* the HIP runtime refused a launch; see g4attn_last_hip_error */
 
 /* dtype codes */
@@ -71,11 +70,24 @@ extern "C" {
 #define G4A_BF16 1
 
 /*
+ * Prefill workspace: bf16 prefill first writes the rotated leading dims of
+ * every key (all d dims, or the first 128 when d = 512 and at most 64 pairs
+ * turn) into the workspace, once per key, and the attention kernel reads them
+ * from there.  Returns the bytes a prefill call with these sizes needs:
+ * B * S * Hkv * slab_dims * 2 for bf16 inputs, 0 for f32 inputs (0 also for
+ * invalid sizes).  The contents need no initialisation and are garbage
+ * afterwards; calls that share one workspace must be ordered on one stream.
+ */
+size_t g4attn_prefill_workspace_bytes(int B, int S, int Hkv, int d, float p, int in_dtype);
+
+/*
  * Sliding-window (local) causal prefill with separate keys and values.
  *   q    [B, S, Hq,  d]  in_dtype        k, v [B, S, Hkv, d]  in_dtype
  *   out  [B, S, Hq,  d]  out_dtype       pos  [B, S] int32 token positions
  *   window: keys per query including itself (0 = unbounded, i.e. global).
  *   theta: rotary base; p: rotated fraction of the pairs (1 = full RoPE).
+ *   workspace: device memory of at least g4attn_prefill_workspace_bytes(...)
+ *   bytes (may be NULL when that is 0).
  * Local layers: window 512/1024, G = 2, d = 256, theta 1e4, p = 1
  * ("Guia visual do Gemma 4", section "Intercalacao de camadas de atencao";
  * techtoday page, attention section, for G = 2 and d = 256).
@@ -83,7 +95,8 @@ extern "C" {
  */
 int g4attn_local_prefill(const void* q, const void* k, const void* v, void* out,
                          const int32_t* pos, int B, int S, int Hq, int Hkv, int d, int window,
-                         float theta, float p, int in_dtype, int out_dtype, void* stream);
+                         float theta, float p, int in_dtype, int out_dtype, void* workspace,
+                         size_t workspace_bytes, void* stream);
 
 /*
  * Global causal prefill with keys identical to values (K=V): one tensor kv
@@ -92,11 +105,13 @@ int g4attn_local_prefill(const void* q, const void* k, const void* v, void* out,
  * "p-RoPE": G = 8, d = 512, p = 0.25).
  *   q   [B, S, Hq, d]   kv [B, S, Hkv, d]   out [B, S, Hq, d]   pos [B, S]
  *   window: 0 for global layers (a positive window also works).
+ *   workspace: as for g4attn_local_prefill.
  * Returns G4A_OK or a negative status; out is written in full.
  */
 int g4attn_global_prefill(const void* q, const void* kv, void* out, const int32_t* pos, int B,
                           int S, int Hq, int Hkv, int d, int window, float theta, float p,
-                          int in_dtype, int out_dtype, void* stream);
+                          int in_dtype, int out_dtype, void* workspace, size_t workspace_bytes,
+                          void* stream);
 
 /*
  * Decode: one query token per sequence against a cache of raw (unrotated)

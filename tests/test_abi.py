@@ -49,14 +49,14 @@ A = 1 << 20
 
 def local(**kw):
     args = dict(q=A, k=2 * A, v=3 * A, out=4 * A, pos=5 * A, B=1, S=8, Hq=4, Hkv=2, d=256,
-                window=4, theta=1e4, p=1.0, i=1, o=0, stream=None)
+                window=4, theta=1e4, p=1.0, i=1, o=0, ws=6 * A, ws_bytes=1 << 40, stream=None)
     args.update(kw)
     return L.lib().g4attn_local_prefill(*args.values())
 
 
 def glob(**kw):
     args = dict(q=A, kv=2 * A, out=4 * A, pos=5 * A, B=1, S=8, Hq=8, Hkv=1, d=512, window=0,
-                theta=1e6, p=0.25, i=1, o=0, stream=None)
+                theta=1e6, p=0.25, i=1, o=0, ws=6 * A, ws_bytes=1 << 40, stream=None)
     args.update(kw)
     return L.lib().g4attn_global_prefill(*args.values())
 
@@ -75,8 +75,9 @@ def dec(**kw):
     (dict(Hkv=0), -1), (dict(Hq=5), -1), (dict(d=255), -1), (dict(window=-1), -1),
     (dict(theta=0.0), -1), (dict(theta=float("nan")), -1), (dict(p=1.5), -1),
     (dict(p=-0.1), -1), (dict(p=float("nan")), -1), (dict(i=2), -1), (dict(o=3), -1),
-    (dict(d=128), -2), (dict(d=512, p=0.5), -2), (dict(Hq=6, Hkv=2), -2), (dict(Hq=32, Hkv=2), -2), (dict(i=0, o=1), -2),
+    (dict(d=128), -2), (dict(Hq=6, Hkv=2), -2), (dict(Hq=32, Hkv=2), -2), (dict(i=0, o=1), -2),
     (dict(q=A + 8), -3), (dict(out=4 * A + 4), -3), (dict(pos=5 * A + 2), -3),
+    (dict(ws=None), -4), (dict(ws_bytes=8 * 2 * 256 * 2 - 1), -4), (dict(ws=6 * A + 8), -3),
 ])
 def test_local_prefill_validation(kw, code):
     assert local(**kw) == code
@@ -91,6 +92,7 @@ def test_empty_inputs_are_noops():
 
 @pytest.mark.parametrize("kw,code", [
     (dict(kv=None), -1), (dict(d=384), -2), (dict(Hq=24, Hkv=1), -2), (dict(kv=2 * A + 1), -3),
+    (dict(ws=None), -4), (dict(ws_bytes=8 * 128 * 2 - 1), -4),
 ])
 def test_global_prefill_validation(kw, code):
     assert glob(**kw) == code
@@ -106,6 +108,16 @@ def test_decode_validation(kw, code):
     if kw.get("d") == 100:
         code = -2  # even but not a supported head dim
     assert dec(**kw) == code
+
+
+def test_prefill_workspace_size():
+    f = L.lib().g4attn_prefill_workspace_bytes
+    # rotated slab [B, S, Hkv, slab dims] bf16: 128 dims when d = 512 and <= 64 pairs turn
+    assert f(1, 262144, 2, 512, 0.25, 1) == 262144 * 2 * 128 * 2
+    assert f(2, 1000, 8, 256, 1.0, 1) == 2 * 1000 * 8 * 256 * 2
+    assert f(1, 100, 4, 512, 0.5, 1) == 100 * 4 * 512 * 2
+    assert f(1, 100, 4, 512, 0.25, 0) == 0  # f32 inputs need none
+    assert f(1, 100, 4, 512, 1.5, 1) == 0
 
 
 def test_workspace_size():

@@ -54,6 +54,8 @@ SMALL = [
     inputs.Layer("local", 1, 190, 8, 2, 512, 40, 1e4, 0.25),
     inputs.Layer("global", 1, 129, 2, 1, 512, 0, 1e4, 0.0),
     inputs.Layer("local", 1, 100, 4, 4, 256, 0, 1e4, 0.25),
+    inputs.Layer("local", 1, 170, 4, 2, 512, 70, 1e4, 0.5),   # separate K/V, d=512, 128 pairs turn
+    inputs.Layer("global", 1, 140, 8, 1, 512, 0, 1e6, 1.0),   # K=V, every pair turns
 ]
 
 
@@ -69,6 +71,26 @@ def test_bf16_prefill_fp32_path_for_f32_inputs_small(layer):
     out, (q, k, v, pos, W) = run_prefill(layer, torch.float32)
     ref = oracle_prefill(layer, q, k, v, pos, W)
     assert_parity(out, ref, torch.float32, str(layer))
+
+
+def test_caller_workspace_of_queried_size_with_stale_contents():
+    """The key-slab workspace needs no initialisation: NaN bytes left in it by
+    an earlier user do not reach the output."""
+    for layer in (SMALL[0], SMALL[3]):
+        q, k, v, pos = inputs.prefill_inputs(layer, 91, 0, torch.bfloat16, DEV)
+        need = g4.prefill_workspace_bytes(layer.B, layer.S, layer.Hkv, layer.d, layer.p)
+        ws = torch.full((need // 2,), float("nan"), dtype=torch.bfloat16, device=DEV)
+        W = layer.window
+        if layer.kind == "global":
+            out = g4.global_prefill(q, k, pos, W, layer.theta, layer.p, workspace=ws)
+        else:
+            out = g4.local_prefill(q, k, v, pos, W, layer.theta, layer.p, workspace=ws)
+        torch.cuda.synchronize()
+        assert_parity(out, oracle_prefill(layer, q, k, v, pos, W), torch.bfloat16, str(layer))
+        with pytest.raises(g4.G4AttnError, match="EWORKSPACE"):
+            g4.global_prefill(q, k, pos, W, layer.theta, layer.p, workspace=ws[:need // 2 - 8]) \
+                if layer.kind == "global" else \
+                g4.local_prefill(q, k, v, pos, W, layer.theta, layer.p, workspace=ws[:need // 2 - 8])
 
 
 def test_large_positions_offset():

@@ -1,0 +1,118 @@
+"""Host-side replay of the prefill kernel's LDS layout (no GPU).
+
+Replays the index arithmetic of prefill.hpp for one KV tile of 32 keys:
+  - direct HBM->LDS loads: lane ln of a load instruction reads global chunk
+    ln ^ swz(row) (16 bytes) and the hardware stores it at LDS byte 16*ln of
+    the instruction's destination;
+  - score operand (ds_read_b128): lane l reads key row l % 32, 8 dims starting
+    at 16*s + 8*(l // 32), for k-step s;
+  - value operand (ds_read_b64_tr_b16, 2 reads per fragment): within a
+    16-lane group, destination lane i receives 16-bit element i % 4 of the
+    8 bytes addressed by source lanes i // 4 + 4*k, k = 0..3 (the lane map
+    measured on gfx950);
+and checks that every MFMA operand lane receives the (key, dim) element the
+matrix layout asks for, and that each group of lanes the LDS serves together
+(16 lanes for 16-byte reads, 32 lanes for 8-byte reads, 64 banks of 4 bytes)
+touches 64 distinct banks.
+"""
+import pytest
+
+BN = 32
+
+
+def swz(r):
+    return ((r & 3) << 2) | ((r >> 2) & 3)
+
+
+def lds_tile(D):
+    """LDS bytes of one tile, as a dict chunk-position -> (key, first dim)."""
+    RPI = 1024 // (2 * D)
+    lds = {}
+    for r0 in range(0, BN, RPI):
+        for ln in range(64):
+            if RPI == 1:
+                row, chunk = r0, ln ^ swz(r0)
+            else:
+                row, chunk = r0 + (ln >> 5), (ln & 31) ^ swz(r0 + (ln >> 5))
+            pos = r0 * (2 * D) + 16 * ln  # destination byte of this lane
+            assert pos not in lds
+            lds[pos] = (row, 8 * chunk)
+    assert len(lds) == BN * D // 8
+    return lds
+
+
+def element(lds, byte):
+    """(key, dim) of the bf16 element stored at LDS byte offset `byte`."""
+    key, dim0 = lds[byte - byte % 16]
+    return key, dim0 + (byte % 16) // 2
+
+
+def score_offsets(D, lane, s):
+    l32, hl = lane & 31, lane >> 5
+    soff = ((2 * (s % 8) + hl) ^ swz(l32)) << 4
+    return l32 * (2 * D) + 256 * (s // 8) + soff
+
+
+def value_offsets(D, lane, db, k2, h):
+    tr_i, tr_g = lane & 15, lane >> 4
+    tr_row = 4 * (tr_g >> 1) + (tr_i >> 2)
+    tr_x = 2 * (tr_g & 1) + ((tr_i & 3) >> 1)
+    voff = (tr_row + 8 * h) * (2 * D) + (tr_i & 1) * 8 + (((4 * (db % 4) + tr_x) ^ swz(tr_row + 8 * h)) << 4)
+    return voff + 256 * (db // 4) + 16 * k2 * (2 * D)
+
+
+def banks16(addrs):
+    return {(a >> 2) & 63 for a in addrs for a in (a, a + 4, a + 8, a + 12)}
+
+
+@pytest.mark.parametrize("D", [256, 512])
+def test_score_operand_reads(D):
+    lds = lds_tile(D)
+    for s in range(D // 16):
+        offs = [score_offsets(D, lane, s) for lane in range(64)]
+        for lane, off in enumerate(offs):
+            for e in range(8):
+                # A operand of the 32x32x16 product: row = key lane%32, k = 8*(lane//32) + e
+                assert element(lds, off + 2 * e) == (lane & 31, 16 * s + 8 * (lane >> 5) + e)
+        for g in range(4):  # 16 lanes served together: 16 chunks x 4 banks
+            assert len(banks16(offs[16 * g:16 * g + 16])) == 64, (D, s, g)
+
+
+@pytest.mark.parametrize("D", [256, 512])
+def test_value_operand_transpose_reads(D):
+    lds = lds_tile(D)
+    for db in range(D // 32):
+        for k2 in range(2):
+            for h in range(2):
+                src = [value_offsets(D, lane, db, k2, h) for lane in range(64)]
+                for half in range(2):  # 32 lanes served together, 8 bytes = 2 banks each
+                    banks = {(a >> 2) & 63 for a in src[32 * half:32 * half + 32] for a in (a, a + 4)}
+                    assert len(banks) == 64, (D, db, k2, h, half)
+                for lane in range(64):
+                    grp, i = lane // 16, lane % 16
+                    got = [element(lds, src[16 * grp + i // 4 + 4 * k] + 2 * (i % 4)) for k in range(4)]
+                    # A operand of O^T += V^T P^T: row = dim 32*db + lane%32; k slots 4h..4h+3
+                    # hold keys 16*k2 + 8*h + 4*(lane//32) + 0..3 (the score-register order)
+                    want = [(16 * k2 + 8 * h + 4 * (lane >> 5) + k, 32 * db + (lane & 31)) for k in range(4)]
+                    assert got == want, (D, db, k2, h, lane)
+
+
+@pytest.mark.parametrize("D,SW", [(512, 128), (256, 256), (512, 512)])
+def test_rotation_items_cover_slab_once(D, SW):
+    """Rotation items (chunk tid % SWC of row tid // SWC + m*RDR) cover every
+    slab chunk once, and each 16 lanes write 16 distinct bank groups."""
+    SWC = SW // 8
+    IPT = BN * SWC // 256
+    RDR = 256 // SWC
+    seen = set()
+    for m in range(IPT):
+        for tid in range(256):
+            c, r = tid % SWC, tid // SWC + m * RDR
+            pos = r * (2 * SW) + ((c ^ swz(r)) << 4)
+            assert pos not in seen
+            seen.add(pos)
+        for g in range(16):
+            addrs = [(tid // SWC + m * RDR) * (2 * SW) + (((tid % SWC) ^ swz(tid // SWC + m * RDR)) << 4)
+                     for tid in range(16 * g, 16 * g + 16)]
+            assert len(banks16(addrs)) == 64
+    assert len(seen) == BN * SWC
