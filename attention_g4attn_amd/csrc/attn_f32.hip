@@ -1,7 +1,7 @@
 // float32-input attention (prefill and decode) on the fp32 vector units.
 //
-// Computes the same function as the bf16 matrix-core kernels (see
-// prefill_bf16.hip) for f32 inputs, keeping every product in fp32 so that the
+// Computes the same function as the bf16 matrix-core kernels (prefill.hpp,
+// decode_bf16.hip) for f32 inputs, keeping every product in fp32 so that the
 // result tracks the exact one to ~1e-6.  One wave per (query token, KV head)
 // handles the G query heads of that KV head: keys stream in blocks of 64 (one
 // per lane) for the scores, the block softmax is merged online, and the value

@@ -1,0 +1,108 @@
+"""Turn rocprofv3 CSV output into the short text summaries kept under profiles/.
+
+  python -m attention_g4attn_amd.profsum stats <kernel_stats.csv> --cmd "<command>" --out <file>
+  python -m attention_g4attn_amd.profsum traffic --fetch <counter_collection.csv>
+      --write <counter_collection.csv> --kernel <name prefix> --copy-bytes N
+      --cmd-fetch "<command>" --cmd-write "<command>" --out <file>
+
+`traffic` scales FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of the kernel by
+what the same counters read for the plain device copy of --copy-bytes bytes in
+the same run (rocclr's copyBuffer kernel), and records the sha256 of the kernel
+sources so a reader can tell whether the figure still describes the code.
+"""
+import argparse
+import csv
+import hashlib
+import os
+import statistics
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+KERNEL_SOURCES = ["attention_g4attn_amd/csrc/prefill.hpp", "attention_g4attn_amd/csrc/common.hpp",
+                  "attention_g4attn_amd/csrc/prefill_kv512.hip"]
+
+
+def source_hash(files=KERNEL_SOURCES):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def stats(args):
+    rows = list(csv.DictReader(open(args.csv)))
+    lines = [f"# rocprofv3 kernel statistics", f"command: {args.cmd}", "",
+             f"{'calls':>6} {'avg_ms':>12} {'total_ms':>12} {'pct':>6}  kernel"]
+    for r in rows:
+        lines.append(f"{int(r['Calls']):>6} {float(r['AverageNs']) / 1e6:>12.4f} "
+                     f"{float(r['TotalDurationNs']) / 1e6:>12.3f} {float(r['Percentage']):>6.2f}  "
+                     f"{r['Name'][:150]}")
+    open(args.out, "w").write("\n".join(lines) + "\n")
+
+
+def counter(path, name_prefix, counter_name):
+    """Per-dispatch values of one counter for kernels whose name starts with name_prefix."""
+    per = {}
+    for r in csv.DictReader(open(path)):
+        if r["Counter_Name"] != counter_name or not r["Kernel_Name"].startswith(name_prefix):
+            continue
+        key = r["Dispatch_Id"]
+        per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+    return list(per.values())
+
+
+def traffic(args):
+    f_k = counter(args.fetch, args.kernel, "FETCH_SIZE")
+    w_k = counter(args.write, args.kernel, "WRITE_SIZE")
+    f_c = counter(args.fetch, "__amd_rocclr_copyBuffer", "FETCH_SIZE")
+    w_c = counter(args.write, "__amd_rocclr_copyBuffer", "WRITE_SIZE")
+    if not (f_k and w_k and f_c and w_c):
+        raise SystemExit("kernel or copy dispatches missing from the counter files")
+    # the calibration copy is the largest copyBuffer dispatch of the run
+    f_scale = args.copy_bytes / (max(f_c) * 1024.0)
+    w_scale = args.copy_bytes / (max(w_c) * 1024.0)
+    fb = statistics.mean(f_k) * 1024.0 * f_scale
+    wb = statistics.mean(w_k) * 1024.0 * w_scale
+    lines = [
+        "# HBM traffic of one launch, from rocprofv3 counters",
+        f"kernel: {args.kernel}",
+        f"command_fetch: {args.cmd_fetch}",
+        f"command_write: {args.cmd_write}",
+        f"dispatches: {len(f_k)} (fetch run), {len(w_k)} (write run)",
+        f"fetch_size_kib_per_dispatch: {statistics.mean(f_k):.1f}",
+        f"write_size_kib_per_dispatch: {statistics.mean(w_k):.1f}",
+        f"copy_calibration_bytes: {args.copy_bytes}",
+        f"copy_fetch_size_kib: {max(f_c):.1f}",
+        f"copy_write_size_kib: {max(w_c):.1f}",
+        f"fetch_scale: {f_scale:.5f}",
+        f"write_scale: {w_scale:.5f}",
+        f"hbm_read_bytes_per_launch: {fb:.6e}",
+        f"hbm_write_bytes_per_launch: {wb:.6e}",
+        f"hbm_bytes_per_launch: {fb + wb:.6e}",
+        f"source_sha256: {source_hash()}",
+        "sources: " + ", ".join(KERNEL_SOURCES),
+    ]
+    open(args.out, "w").write("\n".join(lines) + "\n")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="what", required=True)
+    s = sub.add_parser("stats")
+    s.add_argument("csv")
+    s.add_argument("--cmd", required=True)
+    s.add_argument("--out", required=True)
+    t = sub.add_parser("traffic")
+    t.add_argument("--fetch", required=True)
+    t.add_argument("--write", required=True)
+    t.add_argument("--kernel", required=True)
+    t.add_argument("--copy-bytes", type=int, required=True)
+    t.add_argument("--cmd-fetch", required=True)
+    t.add_argument("--cmd-write", required=True)
+    t.add_argument("--out", required=True)
+    a = ap.parse_args()
+    stats(a) if a.what == "stats" else traffic(a)
+
+
+if __name__ == "__main__":
+    main()

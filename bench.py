@@ -36,7 +36,31 @@ def parse():
     ap.add_argument("--only", choices=["all", "local", "global", "decode"], default="all",
                     help="restrict the step to one kernel kind (profiling runs)")
     ap.add_argument("--seq", type=int, default=None, help="override the prefill length")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the stand-alone local (B=4, S=8192) and global (S=32768) timings")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="finish with one plain device copy of MIB MiB (scale for HBM counters)")
     return ap.parse_args()
+
+
+TRAFFIC_SUMMARY = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
+                               "prefill_global_kv512_s262144_hbm_traffic.txt")
+def measured_traffic():
+    """HBM bytes per launch of the global prefill kernel, from the committed
+    rocprofv3 counter summary, or None when the kernel sources changed since."""
+    try:
+        text = open(TRAFFIC_SUMMARY).read()
+    except OSError:
+        return None
+    vals = dict(line.split(":", 1) for line in text.splitlines()
+                if ":" in line and line.split(":", 1)[0] in ("source_sha256", "hbm_bytes_per_launch"))
+    from attention_g4attn_amd.profsum import source_hash
+    if vals.get("source_sha256", "").strip() != source_hash():
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def prefill_flops(layer):
@@ -157,6 +181,7 @@ def main():
         if D_glo is not None:
             per_kind["global_decode"].append(next(it))
     print(f"# timed {args.steps} steps in {wall:.2f}s", file=sys.stderr, flush=True)
+    extra = {} if args.no_configs else time_configs(g4, inputs, torch)
 
     fl_loc, fl_glo = prefill_flops(loc), prefill_flops(glo)
     (fdl, bdl), (fdg, bdg) = decode_cost(dloc, lengths), decode_cost(dglo, lengths)
@@ -190,8 +215,10 @@ def main():
         t = mean(per_kind["global_prefill"])
         ach = fl_glo / t / 1e9
         roof = {"bound": "mfma", "achieved": ach, "peak": MFMA_BF16_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": ach / MFMA_BF16_PEAK_TFLOPS, "traffic": None,
-                "kernel": "prefill_bf16_kernel<512,8,KV=V>", "flops_per_launch": fl_glo}
+                "unit": "TFLOP/s", "frac": ach / MFMA_BF16_PEAK_TFLOPS,
+                "traffic": measured_traffic() if S == inputs.GROUP_S else None,
+                "kernel": "g4a::pf::prefill_kernel<512, 8, true, false, 128, 3, 1>",
+                "flops_per_launch": fl_glo, "ms_per_launch": t}
     roof_dec = None
     if run_decode:
         tg = mean(per_kind["global_decode"])
@@ -223,11 +250,55 @@ def main():
                    "global_batch": 1, "seq_len": S, "parallelism": "none (1 GPU)",
                    "only": args.only},
         "kinds": kind_rep,
+        "configs": extra,
         "roofline": roof,
         "roofline_decode": roof_dec,
         "cpu_baseline": cpu,
     }
+    if args.copy_calibration > 0:
+        n = args.copy_calibration << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty(n, dtype=torch.uint8, device=dev)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        rec["copy_calibration_bytes"] = n
     print(json.dumps(rec), flush=True)
+
+
+def time_configs(g4, inputs, torch, reps=5):
+    """Stand-alone timings of the local prefill (B=4, S=8192) and the global
+    prefill (S=32768) shapes, outside the timed step."""
+    res = {}
+    for name, layer, wl in (("local_prefill_b4_s8192", inputs.LOCAL_PREFILL, 2),
+                            ("global_prefill_s32768", inputs.GLOBAL_PREFILL, 3)):
+        q, k, v, pos = inputs.prefill_inputs(layer, wl, 0, torch.bfloat16, "cuda")
+        out = torch.empty(q.shape, dtype=torch.float32, device="cuda")
+        ws = torch.empty(max(16, g4.prefill_workspace_bytes(layer.B, layer.S, layer.Hkv, layer.d,
+                                                            layer.p)),
+                         dtype=torch.uint8, device="cuda")
+
+        def call():
+            if layer.kind == "global":
+                g4.global_prefill(q, k, pos, 0, layer.theta, layer.p, out=out, workspace=ws)
+            else:
+                g4.local_prefill(q, k, v, pos, layer.window, layer.theta, layer.p, out=out,
+                                 workspace=ws)
+        call()
+        torch.cuda.synchronize()
+        stream = torch.cuda.current_stream()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            call()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        fl = prefill_flops(layer)
+        res[name] = {"ms": ms, "tflops": fl / ms / 1e9,
+                     "frac_mfma": fl / ms / 1e9 / MFMA_BF16_PEAK_TFLOPS}
+        del q, k, v, pos, out, ws
+    return res
 
 
 def cpu_baseline(args, loc, glo, L0, G0, Lout, Gout):
@@ -262,14 +333,17 @@ def cpu_baseline(args, loc, glo, L0, G0, Lout, Gout):
         return f
 
     rng = np.random.default_rng(7)
-    # calibration: 2 global rows near the end, 64 local rows
-    rg = np.array([S - 1, S - 2])
-    rl = rng.choice(S, 64, replace=False)
-    tc, _, _ = run(rg, rl)
-    n_g = max(2, min(64, int(2 * args.cpu_seconds / max(tc, 1e-3))))
-    rows_g = np.unique(np.concatenate([[0, 1, S - 1], rng.choice(S, n_g, replace=False)]))
-    rows_l = np.unique(np.concatenate([[0, 1, 1023, 1024, S - 1], rng.choice(S, 8 * n_g, replace=False)]))
-    t, og, ol = run(rows_g, rows_l)
+    # calibration run, then a sample sized for about args.cpu_seconds of oracle time;
+    # global rows (2^18 keys each) dominate, local rows ride along 8 per global row
+    n_g = 4
+    for _ in range(2):
+        rows_g = np.unique(np.concatenate([[0, 1, S - 1], rng.choice(S, n_g, replace=False)]))
+        rows_l = np.unique(np.concatenate([[0, 1, 1023, 1024, S - 1],
+                                           rng.choice(S, 8 * n_g, replace=False)]))
+        t, og, ol = run(rows_g, rows_l)
+        if t >= 0.5 * args.cpu_seconds:
+            break
+        n_g = max(4, min(4096, int(n_g * args.cpu_seconds / max(t, 1e-3))))
     f = flops(rows_g, rows_l)
     got_g = Gout.view(S, glo.Hq, glo.d)[torch.as_tensor(rows_g, device=Gout.device)]
     got_l = Lout.view(S, loc.Hq, loc.d)[torch.as_tensor(rows_l, device=Lout.device)]
