@@ -11,16 +11,24 @@
 // (ai.google.dev), section "Principais Consideracoes para o planejamento de
 // memoria" (the KV cache grows with every token).
 //
-// Split kernel: one workgroup per (b, kv head, chunk of `chunk` cache rows);
-// its 4 waves take equal slices of the chunk in 32-row tiles.  Per tile a wave
-//   - loads the rows straight into registers in the A-operand layout of the
-//     16x16x32 product (16 rows x 8 dims per lane), rotates them, and forms
+// Split kernel: one single-wave workgroup per (b, kv head, chunk of `chunk`
+// cache rows), so several stream side by side on every CU with no barriers.
+// The rows of one (b, kv head) are contiguous, and the wave walks its chunk
+// in 16-row tiles through its own 3-stage LDS ring (16-byte direct loads,
+// two tiles in flight).  Per tile it
+//   - reads the key rows as A operands of the 16x16x32 product (16 rows x 8
+//     dims per lane), rotates them at their positions in registers, and forms
 //     S^T = K~ Q~^T for the G query heads (padded to 16 columns);
-//   - writes the raw rows transposed into its own LDS slice and forms
-//     O^T += V^T P^T, P taken straight from the score registers;
-// then the 4 waves merge through LDS and write (m, l, O) of the chunk to the
-// workspace.  The merge kernel combines the chunks of every query head with
-// log-sum-exp weights.  Rows the query may not see are never loaded.
+//   - updates the softmax per column (the output is rescaled only when a
+//     column's max grows by more than 2^8) and packs P^T straight from the
+//     score registers as the B operand of the 16x16x16 product;
+//   - forms O^T += V^T P^T with the value operand read by LDS transpose reads
+//     (4 consecutive rows of one dim per lane).
+// It writes (m, l, O) of its chunk to the workspace; the merge kernel combines
+// the chunks of every query head with log-sum-exp weights.  Rows the query may
+// not see are never loaded (the load extent stops at the last visible row).
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -28,50 +36,85 @@ namespace g4a {
 
 namespace {
 
-constexpr int DW = 4;        // waves per workgroup
-constexpr int TR = 32;       // cache rows per tile
+constexpr int TR = 16;  // cache rows per tile
 
-template <int D>
-struct DLds {
-  static constexpr int VP = TR * 2;           // transposed value row pitch (bytes)
-  static constexpr int WAVE = D * VP;         // one wave's transposed tile
-  static constexpr int GTAB = (D / 2) * 8;
-  static constexpr int TOTAL = DW * WAVE + GTAB;
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// D(16x16, fp32) += A(16x16) * B(16x16), bf16 operands.  Lane l holds
+// A[l % 16][4*(l/16) .. +3], B[4*(l/16) .. +3][l % 16] and D[4*(l/16) + r][l % 16].
+__device__ __forceinline__ f32x4 mfma16x16x16(u32x2 a, u32x2 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a),
+                                                   __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ u32x2 lds_read_tr16(const unsigned char* p) {
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
+  return __builtin_bit_cast(u32x2, v);
+}
+
+// 16-byte chunk swizzle of tile row r (chunk c stored at c ^ dswz(r)): a
+// bijection on r % 16, so a score read (16 lanes = 16 rows, one chunk) hits 16
+// bank groups; rows 0..7 map to even and rows 8..15 to odd values, so a
+// transpose read (32 lanes = 8 rows x 2 adjacent chunks) hits 16 as well.
+__device__ __forceinline__ int dswz(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)p);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(p >> 32));
+  const uint32_t n = __builtin_amdgcn_readfirstlane(bytes);
+  void* u = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(u, (short)0, (int)n, 0x00020000);
+}
+
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rs, uint32_t voff,
+                                          unsigned char* ldst) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(ldst),
+                                           16, voff, 0, 0, 0);
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+template <int N>
+using IC = std::integral_constant<int, N>;
+
+template <class T>
+__device__ __forceinline__ T& lds_at(unsigned char* base, int off) {
+  return *reinterpret_cast<T*>(base + off);
+}
+
+template <int D, bool KVS>
+struct DL {
+  static constexpr int KB = TR * D * 2;              // one tensor's tile, bytes
+  static constexpr int STAGE = KB * (KVS ? 1 : 2);   // K (or K=V) then V
+  static constexpr int NLD = STAGE / 1024;           // direct loads per lane per tile
 };
 
-// Position held by cache row r, or -1 if the query may not see it.
-__device__ __forceinline__ int row_position(int r, int P, int window) {
-  if (window > 0) {
-    const int t = P - (((P - r) % window) + window) % window;
-    return t;  // negative when the ring is not yet full
-  }
-  return r <= P ? r : -1;
-}
-
-// Byte offset of key k (0..31) within a 64-byte row of the transposed tile:
-// the 8 keys lane group q = (k & 15) >> 2 feeds are [4q .. 4q+3, 16+4q .. 16+4q+3],
-// stored as one 16-byte chunk, chunk index XOR-swizzled by dim.
-__device__ __forceinline__ int vt_key_off(int dim, int k) {
-  const int q = (k & 15) >> 2;
-  const int slot = (k & 3) + ((k >> 4) << 2);
-  return dim * (TR * 2) + ((q ^ ((dim >> 1) & 3)) << 4) + (slot << 1);
-}
-
-__device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
-template <int D, int G, bool KVS>
-__global__ void __launch_bounds__(DW * 64, 1) decode_split_kernel(DecodeArgs a) {
+// RK = score k-steps (32 dims each) that may hold turning pairs: 4 when
+// n_rot <= 64 (dims < 128, e.g. p-RoPE at p = 0.25), else all of them.
+template <int D, int G, bool KVS, int NST, int RK>
+__global__ void __launch_bounds__(64, 1) decode_split_kernel(DecodeArgs a) {
   constexpr int NS = D / 32;  // 32-dim k-steps of the score product
   constexpr int NB = D / 16;  // 16-dim blocks of the output
-  using L = DLds<D>;
-  __shared__ __attribute__((aligned(16))) unsigned char smem[L::TOTAL];
+  using L = DL<D, KVS>;
+  static_assert(G <= 16 && (NST == 2 || NST == 3) && RK <= NS, "shape");
+  __shared__ __attribute__((aligned(16))) unsigned char st0[L::STAGE];
+  __shared__ __attribute__((aligned(16))) unsigned char st1[L::STAGE];
+  __shared__ __attribute__((aligned(16))) unsigned char st2[NST == 3 ? L::STAGE : 16];
+  __shared__ double gtab[D / 2];
+  auto stp = [&](auto s) -> unsigned char* {
+    if constexpr (decltype(s)::value == 0) return st0;
+    else if constexpr (decltype(s)::value == 1) return st1;
+    else return st2;
+  };
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int l16 = lane & 15, q4 = lane >> 4;
+  const int lane = threadIdx.x;
+  const int l16 = lane & 15, g4 = lane >> 4;
   const int ch = blockIdx.x % a.nchunk;
   const int bh = blockIdx.x / a.nchunk;
   const int b = bh / a.Hkv, hkv = bh % a.Hkv;
@@ -81,172 +124,161 @@ __global__ void __launch_bounds__(DW * 64, 1) decode_split_kernel(DecodeArgs a) 
   const int last = W > 0 ? min(P, W - 1) : P;  // highest row index that may be visible
   const int r0 = ch * a.chunk;
   if (r0 > last) return;
+  const int r1 = min(r0 + a.chunk, last + 1);  // exclusive
+  const int ntiles = (r1 - r0 + TR - 1) / TR;
 
-  double* gtab = reinterpret_cast<double*>(smem + DW * L::WAVE);
-  for (int t = tid; t < D / 2; t += DW * 64) gtab[t] = rope_rev_per_pos(t, D, a.log2_theta);
+  for (int t = lane; t < D / 2; t += 64) gtab[t] = rope_rev_per_pos(t, D, a.log2_theta);
   __syncthreads();
   const int n_rot = a.n_rot;
 
-  // query heads hkv*G .. +G-1 as B operands (columns >= G are zero)
+  // query heads hkv*G .. +G-1 as B operands of the score product (columns >= G are zero)
   u32x4 qf[NS];
   {
     const int h = hkv * G + (l16 < G ? l16 : 0);
     const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + ((size_t)b * a.Hq + h) * D;
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-      const u32x4 x = *reinterpret_cast<const u32x4*>(qrow + 8 * (4 * s + q4));
+      const u32x4 x = *reinterpret_cast<const u32x4*>(qrow + 8 * (4 * s + g4));
       qf[s] = l16 < G ? x : u32x4{0, 0, 0, 0};
     }
 #pragma unroll
     for (int s = 0; s < NS; ++s)
-      if (16 * s < n_rot) qf[s] = rotate_chunk_bf16(qf[s], 4 * s + q4, P, n_rot, gtab);
+      if (16 * s < n_rot) qf[s] = rotate_chunk_bf16(qf[s], 4 * s + g4, P, n_rot, gtab);
   }
 
-  const uint16_t* kb = static_cast<const uint16_t*>(a.k) + ((size_t)b * a.Hkv + hkv) * C * D;
-  const uint16_t* vb = static_cast<const uint16_t*>(a.v) + ((size_t)b * a.Hkv + hkv) * C * D;
-  unsigned char* vt = smem + w * L::WAVE;
+  const size_t hoff = ((size_t)b * a.Hkv + hkv) * C * D;
+  const uint16_t* kbase = static_cast<const uint16_t*>(a.k) + hoff;
+  const uint16_t* vbase = static_cast<const uint16_t*>(a.v) + hoff;
+
+  // 16 rows of tile i into a ring slot; rows past r1 read as zeros
+  auto issue = [&](int i, auto slot) {
+    unsigned char* sp = stp(slot);
+    const int rr0 = r0 + i * TR;
+    const uint32_t bytes = (uint32_t)min(TR, r1 - rr0) * (2 * D);
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase + (size_t)rr0 * D, bytes);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase + (size_t)rr0 * D, bytes);
+    constexpr int CPR = D / 8;       // chunks per row
+    constexpr int RPI = 64 / CPR;    // rows per direct load
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+#pragma unroll
+    for (int n = 0; n < TR / RPI; ++n) {
+      const int row = n * RPI + ln / CPR;
+      const uint32_t voff = (uint32_t)row * (2 * D) + ((uint32_t)((ln % CPR) ^ dswz(row)) << 4);
+      lds_dma16(rk, voff, sp + n * 1024);
+      if constexpr (!KVS) lds_dma16(rv, voff, sp + L::KB + n * 1024);
+    }
+  };
 
   f32x4 oacc[NB];
 #pragma unroll
   for (int i = 0; i < NB; ++i) oacc[i] = f32x4{};
-  float m_run = -1e30f, l_run = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;  // per column (query head l16), base 2
   const float cs = a.scale_log2e;
 
-  const int rows_per_wave = a.chunk / DW;
-  const int wr0 = r0 + w * rows_per_wave;
-  const int wr1 = min(wr0 + rows_per_wave, last + 1);  // exclusive
-  for (int tb = wr0; tb < wr1; tb += TR) {
-    // ---- load 32 rows (2 blocks of 16) in A-operand layout ----
-    u32x4 kr[2][NS];
-    u32x4 vr[KVS ? 1 : 2][KVS ? 1 : NS];
-    int tpos[2];
-    bool ok[2];
+  auto compute = [&](int i, auto slot) {
+    unsigned char* sp = stp(slot);
+    const int rr0 = r0 + i * TR;
+    const int nrows = min(TR, r1 - rr0);
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int row = ln & 15, gq = ln >> 4;
+    // position of this lane's key row (rows past the tile end are masked)
+    const int r = min(rr0 + row, r1 - 1);
+    const int tpos = W > 0 ? P - (P - r) % W : r;
+    f32x4 sacc = {};
 #pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2) {
-      const int r = tb + 16 * kb2 + l16;
-      const int t = r < wr1 ? row_position(r, P, W) : -1;
-      ok[kb2] = t >= 0;
-      tpos[kb2] = t;
-      const size_t ro = (size_t)(ok[kb2] ? r : wr0) * D;  // unseen rows are never read
-#pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        kr[kb2][s] = *reinterpret_cast<const u32x4*>(kb + ro + 8 * (4 * s + q4));
-        if constexpr (!KVS) vr[kb2][s] = *reinterpret_cast<const u32x4*>(vb + ro + 8 * (4 * s + q4));
-      }
+    for (int s = 0; s < NS; ++s) {
+      const int c = 4 * s + gq;  // chunk of the row holding this lane's 8 dims
+      u32x4 kf = lds_at<u32x4>(sp, row * (2 * D) + 256 * (c >> 4) + (((c & 15) ^ dswz(row)) << 4));
+      if (s < RK) kf = rotate_chunk_bf16(kf, c, tpos, n_rot, gtab);  // per-pair select inside
+      sacc = mfma16x16x32(kf, qf[s], sacc);
     }
-#pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        kr[kb2][s] = ok[kb2] ? kr[kb2][s] : u32x4{0, 0, 0, 0};
-        if constexpr (!KVS) vr[kb2][s] = ok[kb2] ? vr[kb2][s] : u32x4{0, 0, 0, 0};
-      }
-
-    // ---- raw values, transposed, into this wave's LDS slice ----
-#pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2) {
-      const int k = 16 * kb2 + l16;
-#pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        u32x4 x;
-        if constexpr (KVS) x = kr[kb2][s]; else x = vr[kb2][s];
-        const int d0 = 8 * (4 * s + q4);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          *reinterpret_cast<uint16_t*>(vt + vt_key_off(d0 + 2 * i, k)) = (uint16_t)(x[i] & 0xffffu);
-          *reinterpret_cast<uint16_t*>(vt + vt_key_off(d0 + 2 * i + 1, k)) = (uint16_t)(x[i] >> 16);
-        }
-      }
-    }
-
-    // ---- scores S^T (16 rows x 16 heads) per block ----
-    f32x4 sacc[2];
-#pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2) {
-      sacc[kb2] = f32x4{};
-#pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        u32x4 kf = kr[kb2][s];
-        if (16 * s < n_rot) kf = rotate_chunk_bf16(kf, 4 * s + q4, tpos[kb2], n_rot, gtab);
-        sacc[kb2] = mfma16x16x32(kf, qf[s], sacc[kb2]);
-      }
-    }
-    // rows (keys) of the score registers: block kb2, rows 4*q4 + i
+    // S^T register j holds key 4*gq + j of column l16
     float mx = -INFINITY;
 #pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = tb + 16 * kb2 + 4 * q4 + i;
-        const bool vis = r < wr1 && row_position(r, P, W) >= 0;
-        sacc[kb2][i] = vis ? sacc[kb2][i] : -INFINITY;
-        mx = fmaxf(mx, sacc[kb2][i]);
-      }
+    for (int j = 0; j < 4; ++j) {
+      sacc[j] = 4 * gq + j < nrows ? sacc[j] : -INFINITY;
+      mx = fmaxf(mx, sacc[j]);
+    }
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx * cs);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    m_run = m_new;
-    l_run *= alpha;
+    const float mt = mx * cs;
+    if (__any(mt > m_run + 8.f)) {  // wave-uniform; rare after the first tile
+      const float mn = fmaxf(m_run, mt);
+      const float al = __builtin_amdgcn_exp2f(m_run - mn);
 #pragma unroll
-    for (int i = 0; i < NB; ++i) oacc[i] *= alpha;
-    float p[2][4];
+      for (int db = 0; db < NB; ++db) oacc[db] *= al;
+      l_run *= al;
+      m_run = mn;
+    }
+    float p[4];
 #pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        p[kb2][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb2][i], cs, -m_run));
-        l_run += p[kb2][i];
-      }
-    const u32x4 pf = {pack_bf16(p[0][0], p[0][1]), pack_bf16(p[0][2], p[0][3]),
-                      pack_bf16(p[1][0], p[1][1]), pack_bf16(p[1][2], p[1][3])};
-
-    wave_lds_sync();
-    // ---- O^T += V^T P^T ----
+    for (int j = 0; j < 4; ++j) {
+      p[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[j], cs, -m_run));
+      l_run += p[j];
+    }
+    const u32x2 pf = {pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3])};
+    // V^T fragments: source lane (gq, row) addresses tile row 4*gq + row/4,
+    // dims 16*db + 4*(row%4) .. +3 (chunk 2*db + (row%4)/2, half row%2)
+    const int trow = 4 * gq + (row >> 2);
+    const int tch = (row & 3) >> 1;
+    const int tb = (KVS ? 0 : L::KB) + trow * (2 * D) + (row & 1) * 8;
 #pragma unroll
     for (int db = 0; db < NB; ++db) {
-      const int dim = 16 * db + l16;
-      const u32x4 vf = *reinterpret_cast<const u32x4*>(
-          vt + dim * (TR * 2) + ((q4 ^ ((dim >> 1) & 3)) << 4));
-      oacc[db] = mfma16x16x32(vf, pf, oacc[db]);
+      const int c = 2 * db + tch;
+      const u32x2 vf = lds_read_tr16(sp + tb + 256 * (c >> 4) + (((c & 15) ^ dswz(trow)) << 4));
+      oacc[db] = mfma16x16x16(vf, pf, oacc[db]);
     }
-    wave_lds_sync();
+  };
+
+  // ---- ring of NST slots: tile i+NST-1 is requested while tile i is computed ----
+  if constexpr (NST == 3) {
+    issue(0, IC<0>{});
+    if (ntiles > 1) issue(1, IC<1>{});
+    auto step = [&](int i, auto s) {
+      constexpr int S0 = decltype(s)::value;
+      if (i + 2 < ntiles) issue(i + 2, IC<(S0 + 2) % 3>{});
+      const int after = min(ntiles - 1 - i, 2);  // tiles requested after tile i
+      if (after == 2) wait_vmcnt<2 * L::NLD>();
+      else if (after == 1) wait_vmcnt<L::NLD>();
+      else wait_vmcnt<0>();
+      compute(i, s);
+    };
+    for (int i = 0; i < ntiles; i += 3) {
+      step(i, IC<0>{});
+      if (i + 1 < ntiles) step(i + 1, IC<1>{});
+      if (i + 2 < ntiles) step(i + 2, IC<2>{});
+    }
+  } else {
+    issue(0, IC<0>{});
+    auto step = [&](int i, auto s) {
+      constexpr int S0 = decltype(s)::value;
+      if (i + 1 < ntiles) {
+        issue(i + 1, IC<1 - S0>{});
+        wait_vmcnt<L::NLD>();
+      } else {
+        wait_vmcnt<0>();
+      }
+      compute(i, s);
+    };
+    for (int i = 0; i < ntiles; i += 2) {
+      step(i, IC<0>{});
+      if (i + 1 < ntiles) step(i + 1, IC<1>{});
+    }
   }
 
-  // ---- merge the 4 waves of this workgroup through LDS ----
+  // ---- partial (m, l, O) of this chunk for the G query heads ----
   l_run += __shfl_xor(l_run, 16);
   l_run += __shfl_xor(l_run, 32);
-  __syncthreads();
-  float* ow = reinterpret_cast<float*>(smem);  // [DW][G][D] then [DW][G][2]
-  float* mlw = ow + DW * G * D;
   if (l16 < G) {
+    const size_t prow = ((size_t)b * a.Hq + hkv * G + l16) * a.nchunk + ch;
+    float* po = a.part_o + prow * D + 4 * g4;
 #pragma unroll
-    for (int db = 0; db < NB; ++db)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) ow[(w * G + l16) * D + 16 * db + 4 * q4 + i] = oacc[db][i];
-    if (q4 == 0) {
-      mlw[(w * G + l16) * 2 + 0] = m_run;
-      mlw[(w * G + l16) * 2 + 1] = l_run;
-    }
-  }
-  __syncthreads();
-  for (int idx = tid; idx < G * D; idx += DW * 64) {
-    const int h = idx / D, e = idx % D;
-    float M = -INFINITY;
-#pragma unroll
-    for (int ww = 0; ww < DW; ++ww) M = fmaxf(M, mlw[(ww * G + h) * 2]);
-    float o = 0.f, l = 0.f;
-#pragma unroll
-    for (int ww = 0; ww < DW; ++ww) {
-      const float f = __builtin_amdgcn_exp2f(mlw[(ww * G + h) * 2] - M);
-      o += f * ow[(ww * G + h) * D + e];
-      l += f * mlw[(ww * G + h) * 2 + 1];
-    }
-    const size_t prow = ((size_t)b * a.Hq + hkv * G + h) * a.nchunk + ch;
-    a.part_o[prow * D + e] = o;
-    if (e == 0) {
-      a.part_ml[prow * 2 + 0] = M;
-      a.part_ml[prow * 2 + 1] = l;
+    for (int db = 0; db < NB; ++db) *reinterpret_cast<f32x4*>(po + 16 * db) = oacc[db];
+    if (g4 == 0) {
+      a.part_ml[prow * 2 + 0] = m_run;
+      a.part_ml[prow * 2 + 1] = l_run;
     }
   }
 }
@@ -285,9 +317,16 @@ __global__ void __launch_bounds__(256) decode_merge_kernel(DecodeArgs a) {
 
 template <int D, int G, bool KVS>
 hipError_t launch_split(const DecodeArgs& a, hipStream_t st) {
+  // ring slots: 3 (two tiles in flight) unless two tiles of loads exceed the
+  // wait counter's range (separate K and V at D = 512)
+  constexpr int NST = 2 * DL<D, KVS>::NLD < 64 ? 3 : 2;
   const long long n = (long long)a.B * a.Hkv * a.nchunk;
   if (n > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((decode_split_kernel<D, G, KVS>), dim3((unsigned)n), dim3(DW * 64), 0, st, a);
+  if (a.n_rot <= 64)
+    hipLaunchKernelGGL((decode_split_kernel<D, G, KVS, NST, 4>), dim3((unsigned)n), dim3(64), 0, st, a);
+  else
+    hipLaunchKernelGGL((decode_split_kernel<D, G, KVS, NST, D / 32>), dim3((unsigned)n), dim3(64), 0,
+                       st, a);
   return hipGetLastError();
 }
 
@@ -308,7 +347,7 @@ int decode_chunk_rows(int D, int capacity, int window, bool f32) {
   (void)D;
   if (f32) return capacity;
   if (window > 0) return 128;  // ring: 4 chunks of a 512-slot window
-  return 2048;
+  return 1024;
 }
 
 int decode_num_chunks(int D, int capacity, int window, bool f32) {

@@ -116,3 +116,64 @@ def test_rotation_items_cover_slab_once(D, SW):
                      for tid in range(16 * g, 16 * g + 16)]
             assert len(banks16(addrs)) == 64
     assert len(seen) == BN * SWC
+
+
+# ---- decode tiles: 16 contiguous cache rows, chunk c of row r at c ^ dswz(r) ----
+
+TRD = 16
+
+
+def dswz(r):
+    return ((r & 7) << 1) | ((r >> 3) & 1)
+
+
+def decode_tile(D):
+    CPR = D // 8
+    RPI = 64 // CPR
+    lds = {}
+    for n in range(TRD // RPI):
+        for ln in range(64):
+            row = n * RPI + ln // CPR
+            chunk = (ln % CPR) ^ dswz(row)
+            pos = n * 1024 + 16 * ln
+            assert pos not in lds and 0 <= chunk < CPR
+            lds[pos] = (row, 8 * chunk)
+    assert len(lds) == TRD * D // 8
+    return lds
+
+
+@pytest.mark.parametrize("D", [256, 512])
+def test_decode_score_operand_reads(D):
+    """16x16x32 A operand: lane l holds key row l % 16, dims 32*s + 8*(l // 16) .. +7."""
+    lds = decode_tile(D)
+    for s in range(D // 32):
+        offs = []
+        for lane in range(64):
+            row, gq = lane & 15, lane >> 4
+            c = 4 * s + gq
+            off = row * (2 * D) + 256 * (c >> 4) + (((c & 15) ^ dswz(row)) << 4)
+            offs.append(off)
+            for e in range(8):
+                assert element(lds, off + 2 * e) == (row, 32 * s + 8 * gq + e)
+        for g in range(4):
+            assert len(banks16(offs[16 * g:16 * g + 16])) == 64, (D, s, g)
+
+
+@pytest.mark.parametrize("D", [256, 512])
+def test_decode_value_operand_transpose_reads(D):
+    """16x16x16 A operand V^T: lane l holds dim 16*db + l % 16, keys 4*(l // 16) .. +3."""
+    lds = decode_tile(D)
+    for db in range(D // 16):
+        src = []
+        for lane in range(64):
+            row, gq = lane & 15, lane >> 4
+            trow, tch = 4 * gq + (row >> 2), (row & 3) >> 1
+            c = 2 * db + tch
+            src.append(trow * (2 * D) + (row & 1) * 8 + 256 * (c >> 4) + (((c & 15) ^ dswz(trow)) << 4))
+        for half in range(2):
+            banks = {(a >> 2) & 63 for a in src[32 * half:32 * half + 32] for a in (a, a + 4)}
+            assert len(banks) == 64, (D, db, half)
+        for lane in range(64):
+            grp, i = lane // 16, lane % 16
+            got = [element(lds, src[16 * grp + i // 4 + 4 * k] + 2 * (i % 4)) for k in range(4)]
+            assert got == [(4 * grp + k, 16 * db + i) for k in range(4)], (D, db, lane)
