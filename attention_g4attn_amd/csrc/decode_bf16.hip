@@ -12,10 +12,13 @@
 // memoria" (the KV cache grows with every token).
 //
 // Split kernel: one single-wave workgroup per (b, kv head, chunk of `chunk`
-// cache rows), so several stream side by side on every CU with no barriers.
-// The rows of one (b, kv head) are contiguous, and the wave walks its chunk
-// in 16-row tiles through its own 3-stage LDS ring (16-byte direct loads,
-// two tiles in flight).  Per tile it
+// cache rows).  The rows of one (b, kv head) are contiguous; the wave walks
+// its chunk in 16-row tiles, each loaded straight into LDS with 16-byte
+// direct loads.  A wave keeps one tile slot and the CU runs 8 such waves (2
+// per SIMD, 18 KB of LDS each), so while one wave computes, the others' tile
+// loads are in flight and the SIMD has a second wave to issue from (measured
+// faster than 1 wave per SIMD with a 2- or 3-slot private ring).  Per tile
+// the wave
 //   - reads the key rows as A operands of the 16x16x32 product (16 rows x 8
 //     dims per lane), rotates them at their positions in registers, and forms
 //     S^T = K~ Q~^T for the G query heads (padded to 16 columns);
@@ -27,8 +30,6 @@
 // It writes (m, l, O) of its chunk to the workspace; the merge kernel combines
 // the chunks of every query head with log-sum-exp weights.  Rows the query may
 // not see are never loaded (the load extent stops at the last visible row).
-#include <type_traits>
-
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -80,9 +81,6 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-template <int N>
-using IC = std::integral_constant<int, N>;
-
 template <class T>
 __device__ __forceinline__ T& lds_at(unsigned char* base, int off) {
   return *reinterpret_cast<T*>(base + off);
@@ -92,26 +90,19 @@ template <int D, bool KVS>
 struct DL {
   static constexpr int KB = TR * D * 2;              // one tensor's tile, bytes
   static constexpr int STAGE = KB * (KVS ? 1 : 2);   // K (or K=V) then V
-  static constexpr int NLD = STAGE / 1024;           // direct loads per lane per tile
 };
 
 // RK = score k-steps (32 dims each) that may hold turning pairs: 4 when
 // n_rot <= 64 (dims < 128, e.g. p-RoPE at p = 0.25), else all of them.
-template <int D, int G, bool KVS, int NST, int RK>
-__global__ void __launch_bounds__(64, 1) decode_split_kernel(DecodeArgs a) {
+template <int D, int G, bool KVS, int RK>
+__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+decode_split_kernel(DecodeArgs a) {
   constexpr int NS = D / 32;  // 32-dim k-steps of the score product
   constexpr int NB = D / 16;  // 16-dim blocks of the output
   using L = DL<D, KVS>;
-  static_assert(G <= 16 && (NST == 2 || NST == 3) && RK <= NS, "shape");
-  __shared__ __attribute__((aligned(16))) unsigned char st0[L::STAGE];
-  __shared__ __attribute__((aligned(16))) unsigned char st1[L::STAGE];
-  __shared__ __attribute__((aligned(16))) unsigned char st2[NST == 3 ? L::STAGE : 16];
+  static_assert(G <= 16 && RK <= NS && NS % 4 == 0, "shape");
+  __shared__ __attribute__((aligned(16))) unsigned char tile[L::STAGE];
   __shared__ double gtab[D / 2];
-  auto stp = [&](auto s) -> unsigned char* {
-    if constexpr (decltype(s)::value == 0) return st0;
-    else if constexpr (decltype(s)::value == 1) return st1;
-    else return st2;
-  };
 
   const int lane = threadIdx.x;
   const int l16 = lane & 15, g4 = lane >> 4;
@@ -126,33 +117,25 @@ __global__ void __launch_bounds__(64, 1) decode_split_kernel(DecodeArgs a) {
   if (r0 > last) return;
   const int r1 = min(r0 + a.chunk, last + 1);  // exclusive
   const int ntiles = (r1 - r0 + TR - 1) / TR;
-
-  for (int t = lane; t < D / 2; t += 64) gtab[t] = rope_rev_per_pos(t, D, a.log2_theta);
-  __syncthreads();
   const int n_rot = a.n_rot;
 
-  // query heads hkv*G .. +G-1 as B operands of the score product (columns >= G are zero)
+  // query heads hkv*G .. +G-1 as B operands of the score product (columns >= G
+  // are zero); loaded first, so waiting for them leaves the tile loads below in flight
   u32x4 qf[NS];
   {
     const int h = hkv * G + (l16 < G ? l16 : 0);
     const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + ((size_t)b * a.Hq + h) * D;
 #pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      const u32x4 x = *reinterpret_cast<const u32x4*>(qrow + 8 * (4 * s + g4));
-      qf[s] = l16 < G ? x : u32x4{0, 0, 0, 0};
-    }
-#pragma unroll
-    for (int s = 0; s < NS; ++s)
-      if (16 * s < n_rot) qf[s] = rotate_chunk_bf16(qf[s], 4 * s + g4, P, n_rot, gtab);
+    for (int s = 0; s < NS; ++s) qf[s] = *reinterpret_cast<const u32x4*>(qrow + 8 * (4 * s + g4));
   }
 
   const size_t hoff = ((size_t)b * a.Hkv + hkv) * C * D;
   const uint16_t* kbase = static_cast<const uint16_t*>(a.k) + hoff;
   const uint16_t* vbase = static_cast<const uint16_t*>(a.v) + hoff;
 
-  // 16 rows of tile i into a ring slot; rows past r1 read as zeros
-  auto issue = [&](int i, auto slot) {
-    unsigned char* sp = stp(slot);
+  // 16 rows of tile i into the tile slot; rows past r1 read as zeros
+  auto issue = [&](int i) {
+    unsigned char* sp = tile;
     const int rr0 = r0 + i * TR;
     const uint32_t bytes = (uint32_t)min(TR, r1 - rr0) * (2 * D);
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase + (size_t)rr0 * D, bytes);
@@ -169,6 +152,15 @@ __global__ void __launch_bounds__(64, 1) decode_split_kernel(DecodeArgs a) {
       if constexpr (!KVS) lds_dma16(rv, voff, sp + L::KB + n * 1024);
     }
   };
+  issue(0);
+
+  for (int t = lane; t < D / 2; t += 64) gtab[t] = rope_rev_per_pos(t, D, a.log2_theta);
+  __syncthreads();
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    qf[s] = l16 < G ? qf[s] : u32x4{0, 0, 0, 0};
+    if (s < RK) qf[s] = rotate_chunk_bf16(qf[s], 4 * s + g4, P, n_rot, gtab);
+  }
 
   f32x4 oacc[NB];
 #pragma unroll
@@ -176,8 +168,8 @@ __global__ void __launch_bounds__(64, 1) decode_split_kernel(DecodeArgs a) {
   float m_run = -INFINITY, l_run = 0.f;  // per column (query head l16), base 2
   const float cs = a.scale_log2e;
 
-  auto compute = [&](int i, auto slot) {
-    unsigned char* sp = stp(slot);
+  auto compute = [&](int i) {
+    unsigned char* sp = tile;
     const int rr0 = r0 + i * TR;
     const int nrows = min(TR, r1 - rr0);
     int ln = lane;
@@ -186,14 +178,21 @@ __global__ void __launch_bounds__(64, 1) decode_split_kernel(DecodeArgs a) {
     // position of this lane's key row (rows past the tile end are masked)
     const int r = min(rr0 + row, r1 - 1);
     const int tpos = W > 0 ? P - (P - r) % W : r;
-    f32x4 sacc = {};
+    // score operand: chunk c = 4*s + gq of row `row`, stored at
+    // 16*(s/4) + ((4*(s%4) + gq) ^ dswz(row))
+    const int dsw = dswz(row);
+    int koff[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) koff[j] = row * (2 * D) + (((4 * j + gq) ^ dsw) << 4);
+    f32x4 sacc0 = {}, sacc1 = {};  // even / odd k-steps: two independent chains
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-      const int c = 4 * s + gq;  // chunk of the row holding this lane's 8 dims
-      u32x4 kf = lds_at<u32x4>(sp, row * (2 * D) + 256 * (c >> 4) + (((c & 15) ^ dswz(row)) << 4));
-      if (s < RK) kf = rotate_chunk_bf16(kf, c, tpos, n_rot, gtab);  // per-pair select inside
-      sacc = mfma16x16x32(kf, qf[s], sacc);
+      u32x4 kf = lds_at<u32x4>(sp, koff[s & 3] + 256 * (s >> 2));
+      if (s < RK) kf = rotate_chunk_bf16(kf, 4 * s + gq, tpos, n_rot, gtab);  // per-pair select inside
+      if (s & 1) sacc1 = mfma16x16x32(kf, qf[s], sacc1);
+      else sacc0 = mfma16x16x32(kf, qf[s], sacc0);
     }
+    f32x4 sacc = sacc0 + sacc1;
     // S^T register j holds key 4*gq + j of column l16
     float mx = -INFINITY;
 #pragma unroll
@@ -220,52 +219,28 @@ __global__ void __launch_bounds__(64, 1) decode_split_kernel(DecodeArgs a) {
     }
     const u32x2 pf = {pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3])};
     // V^T fragments: source lane (gq, row) addresses tile row 4*gq + row/4,
-    // dims 16*db + 4*(row%4) .. +3 (chunk 2*db + (row%4)/2, half row%2)
+    // dims 16*db + 4*(row%4) .. +3, i.e. chunk c = 2*db + (row%4)/2 (half
+    // row%2), stored at 16*(db/8) + ((2*(db%8) + (row%4)/2) ^ dswz(trow))
     const int trow = 4 * gq + (row >> 2);
     const int tch = (row & 3) >> 1;
-    const int tb = (KVS ? 0 : L::KB) + trow * (2 * D) + (row & 1) * 8;
+    const int tdsw = dswz(trow);
+    int voff[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      voff[j] = (KVS ? 0 : L::KB) + trow * (2 * D) + (row & 1) * 8 + (((2 * j + tch) ^ tdsw) << 4);
 #pragma unroll
     for (int db = 0; db < NB; ++db) {
-      const int c = 2 * db + tch;
-      const u32x2 vf = lds_read_tr16(sp + tb + 256 * (c >> 4) + (((c & 15) ^ dswz(trow)) << 4));
+      const u32x2 vf = lds_read_tr16(sp + voff[db & 7] + 256 * (db >> 3));
       oacc[db] = mfma16x16x16(vf, pf, oacc[db]);
     }
   };
 
-  // ---- ring of NST slots: tile i+NST-1 is requested while tile i is computed ----
-  if constexpr (NST == 3) {
-    issue(0, IC<0>{});
-    if (ntiles > 1) issue(1, IC<1>{});
-    auto step = [&](int i, auto s) {
-      constexpr int S0 = decltype(s)::value;
-      if (i + 2 < ntiles) issue(i + 2, IC<(S0 + 2) % 3>{});
-      const int after = min(ntiles - 1 - i, 2);  // tiles requested after tile i
-      if (after == 2) wait_vmcnt<2 * L::NLD>();
-      else if (after == 1) wait_vmcnt<L::NLD>();
-      else wait_vmcnt<0>();
-      compute(i, s);
-    };
-    for (int i = 0; i < ntiles; i += 3) {
-      step(i, IC<0>{});
-      if (i + 1 < ntiles) step(i + 1, IC<1>{});
-      if (i + 2 < ntiles) step(i + 2, IC<2>{});
-    }
-  } else {
-    issue(0, IC<0>{});
-    auto step = [&](int i, auto s) {
-      constexpr int S0 = decltype(s)::value;
-      if (i + 1 < ntiles) {
-        issue(i + 1, IC<1 - S0>{});
-        wait_vmcnt<L::NLD>();
-      } else {
-        wait_vmcnt<0>();
-      }
-      compute(i, s);
-    };
-    for (int i = 0; i < ntiles; i += 2) {
-      step(i, IC<0>{});
-      if (i + 1 < ntiles) step(i + 1, IC<1>{});
-    }
+  // the previous tile's LDS reads have completed (its products consumed them)
+  // before the next tile's loads are requested
+  for (int i = 0; i < ntiles; ++i) {
+    if (i > 0) issue(i);
+    wait_vmcnt<0>();
+    compute(i);
   }
 
   // ---- partial (m, l, O) of this chunk for the G query heads ----
@@ -317,16 +292,13 @@ __global__ void __launch_bounds__(256) decode_merge_kernel(DecodeArgs a) {
 
 template <int D, int G, bool KVS>
 hipError_t launch_split(const DecodeArgs& a, hipStream_t st) {
-  // ring slots: 3 (two tiles in flight) unless two tiles of loads exceed the
-  // wait counter's range (separate K and V at D = 512)
-  constexpr int NST = 2 * DL<D, KVS>::NLD < 64 ? 3 : 2;
   const long long n = (long long)a.B * a.Hkv * a.nchunk;
   if (n > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   if (a.n_rot <= 64)
-    hipLaunchKernelGGL((decode_split_kernel<D, G, KVS, NST, 4>), dim3((unsigned)n), dim3(64), 0, st, a);
+    hipLaunchKernelGGL((decode_split_kernel<D, G, KVS, 4>), dim3((unsigned)n), dim3(64), 0, st, a);
   else
-    hipLaunchKernelGGL((decode_split_kernel<D, G, KVS, NST, D / 32>), dim3((unsigned)n), dim3(64), 0,
-                       st, a);
+    hipLaunchKernelGGL((decode_split_kernel<D, G, KVS, D / 32>), dim3((unsigned)n), dim3(64), 0, st,
+                       a);
   return hipGetLastError();
 }
 
