@@ -86,25 +86,28 @@ __device__ __forceinline__ T& lds_at(unsigned char* base, int off) {
   return *reinterpret_cast<T*>(base + off);
 }
 
-template <int D, bool KVS>
-struct DL {
-  static constexpr int KB = TR * D * 2;              // one tensor's tile, bytes
-  static constexpr int STAGE = KB * (KVS ? 1 : 2);   // K (or K=V) then V
-};
-
 // RK = score k-steps (32 dims each) that may hold turning pairs: 4 when
 // n_rot <= 64 (dims < 128, e.g. p-RoPE at p = 0.25), else all of them.
-template <int D, int G, bool KVS, int RK>
-__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+// NW = waves per workgroup.  K=V: NW waves split the chunk and merge their
+// partials in LDS at the end (shorter waves, one partial per chunk).
+// Separate K and V: one wave whose K and V tiles are separate LDS objects,
+// so the next tile's keys are requested as soon as the scores are done and
+// its values as soon as the value product is done.
+template <int D, int G, bool KVS, int RK, int NW>
+__global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 decode_split_kernel(DecodeArgs a) {
   constexpr int NS = D / 32;  // 32-dim k-steps of the score product
   constexpr int NB = D / 16;  // 16-dim blocks of the output
-  using L = DL<D, KVS>;
-  static_assert(G <= 16 && RK <= NS && NS % 4 == 0, "shape");
-  __shared__ __attribute__((aligned(16))) unsigned char tile[L::STAGE];
+  constexpr int KB = TR * D * 2;     // one tensor's tile, bytes
+  constexpr int NLD = KB / 1024;     // direct loads per lane per tensor tile
+  static_assert(G <= 8 && RK <= NS && NS % 4 == 0 && (KVS || NW == 1), "shape");
+  __shared__ __attribute__((aligned(16))) unsigned char tk[NW * KB];      // K (or K=V) tile per wave
+  __shared__ __attribute__((aligned(16))) unsigned char tv[KVS ? 16 : KB];  // V tile
   __shared__ double gtab[D / 2];
+  __shared__ float mls[NW][16][2];
 
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l16 = lane & 15, g4 = lane >> 4;
   const int ch = blockIdx.x % a.nchunk;
   const int bh = blockIdx.x / a.nchunk;
@@ -116,8 +119,12 @@ decode_split_kernel(DecodeArgs a) {
   const int r0 = ch * a.chunk;
   if (r0 > last) return;
   const int r1 = min(r0 + a.chunk, last + 1);  // exclusive
-  const int ntiles = (r1 - r0 + TR - 1) / TR;
+  // this wave's rows: a TR-aligned share of the chunk (possibly empty)
+  const int per = (a.chunk / NW + TR - 1) / TR * TR;
+  const int wr0 = min(r0 + w * per, r1), wr1 = min(wr0 + per, r1);
+  const int ntiles = (wr1 - wr0 + TR - 1) / TR;
   const int n_rot = a.n_rot;
+  unsigned char* kt = tk + w * KB;
 
   // query heads hkv*G .. +G-1 as B operands of the score product (columns >= G
   // are zero); loaded first, so waiting for them leaves the tile loads below in flight
@@ -133,13 +140,11 @@ decode_split_kernel(DecodeArgs a) {
   const uint16_t* kbase = static_cast<const uint16_t*>(a.k) + hoff;
   const uint16_t* vbase = static_cast<const uint16_t*>(a.v) + hoff;
 
-  // 16 rows of tile i into the tile slot; rows past r1 read as zeros
-  auto issue = [&](int i) {
-    unsigned char* sp = tile;
-    const int rr0 = r0 + i * TR;
-    const uint32_t bytes = (uint32_t)min(TR, r1 - rr0) * (2 * D);
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase + (size_t)rr0 * D, bytes);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase + (size_t)rr0 * D, bytes);
+  // 16 rows of tile i of one tensor into an LDS tile; rows past wr1 read as zeros
+  auto issue = [&](const uint16_t* base, int i, unsigned char* dst) {
+    const int rr0 = wr0 + i * TR;
+    const uint32_t bytes = (uint32_t)min(TR, wr1 - rr0) * (2 * D);
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(base + (size_t)rr0 * D, bytes);
     constexpr int CPR = D / 8;       // chunks per row
     constexpr int RPI = 64 / CPR;    // rows per direct load
     int ln = lane;
@@ -148,14 +153,17 @@ decode_split_kernel(DecodeArgs a) {
     for (int n = 0; n < TR / RPI; ++n) {
       const int row = n * RPI + ln / CPR;
       const uint32_t voff = (uint32_t)row * (2 * D) + ((uint32_t)((ln % CPR) ^ dswz(row)) << 4);
-      lds_dma16(rk, voff, sp + n * 1024);
-      if constexpr (!KVS) lds_dma16(rv, voff, sp + L::KB + n * 1024);
+      lds_dma16(rs, voff, dst + n * 1024);
     }
   };
-  issue(0);
-
-  for (int t = lane; t < D / 2; t += 64) gtab[t] = rope_rev_per_pos(t, D, a.log2_theta);
+  // the barrier's fence waits for every outstanding load, so the angle table
+  // is built before the first tile is requested
+  for (int t = threadIdx.x; t < D / 2; t += 64 * NW) gtab[t] = rope_rev_per_pos(t, D, a.log2_theta);
   __syncthreads();
+  if (ntiles > 0) {
+    issue(kbase, 0, kt);
+    if constexpr (!KVS) issue(vbase, 0, tv);
+  }
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
     qf[s] = l16 < G ? qf[s] : u32x4{0, 0, 0, 0};
@@ -168,18 +176,15 @@ decode_split_kernel(DecodeArgs a) {
   float m_run = -INFINITY, l_run = 0.f;  // per column (query head l16), base 2
   const float cs = a.scale_log2e;
 
-  auto compute = [&](int i) {
-    unsigned char* sp = tile;
-    const int rr0 = r0 + i * TR;
-    const int nrows = min(TR, r1 - rr0);
+  // scores of tile i from the key tile: S^T register j = key 4*gq + j of column l16
+  auto scores = [&](int i) -> f32x4 {
+    const int rr0 = wr0 + i * TR;
     int ln = lane;
     asm volatile("" : "+v"(ln));
     const int row = ln & 15, gq = ln >> 4;
-    // position of this lane's key row (rows past the tile end are masked)
-    const int r = min(rr0 + row, r1 - 1);
+    const int r = min(rr0 + row, wr1 - 1);  // rows past the tile end are masked
     const int tpos = W > 0 ? P - (P - r) % W : r;
-    // score operand: chunk c = 4*s + gq of row `row`, stored at
-    // 16*(s/4) + ((4*(s%4) + gq) ^ dswz(row))
+    // chunk c = 4*s + gq of row `row` is stored at 16*(s/4) + ((4*(s%4) + gq) ^ dswz(row))
     const int dsw = dswz(row);
     int koff[4];
 #pragma unroll
@@ -187,17 +192,20 @@ decode_split_kernel(DecodeArgs a) {
     f32x4 sacc0 = {}, sacc1 = {};  // even / odd k-steps: two independent chains
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-      u32x4 kf = lds_at<u32x4>(sp, koff[s & 3] + 256 * (s >> 2));
+      u32x4 kf = lds_at<u32x4>(kt, koff[s & 3] + 256 * (s >> 2));
       if (s < RK) kf = rotate_chunk_bf16(kf, 4 * s + gq, tpos, n_rot, gtab);  // per-pair select inside
       if (s & 1) sacc1 = mfma16x16x32(kf, qf[s], sacc1);
       else sacc0 = mfma16x16x32(kf, qf[s], sacc0);
     }
-    f32x4 sacc = sacc0 + sacc1;
-    // S^T register j holds key 4*gq + j of column l16
+    return sacc0 + sacc1;
+  };
+  // softmax update of the columns; returns P^T as the B operand of the value product
+  auto softmax = [&](int i, f32x4 sacc) -> u32x2 {
+    const int nrows = min(TR, wr1 - (wr0 + i * TR));
     float mx = -INFINITY;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      sacc[j] = 4 * gq + j < nrows ? sacc[j] : -INFINITY;
+      sacc[j] = 4 * g4 + j < nrows ? sacc[j] : -INFINITY;
       mx = fmaxf(mx, sacc[j]);
     }
     mx = fmaxf(mx, __shfl_xor(mx, 16));
@@ -217,56 +225,117 @@ decode_split_kernel(DecodeArgs a) {
       p[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[j], cs, -m_run));
       l_run += p[j];
     }
-    const u32x2 pf = {pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3])};
-    // V^T fragments: source lane (gq, row) addresses tile row 4*gq + row/4,
-    // dims 16*db + 4*(row%4) .. +3, i.e. chunk c = 2*db + (row%4)/2 (half
-    // row%2), stored at 16*(db/8) + ((2*(db%8) + (row%4)/2) ^ dswz(trow))
+    return u32x2{pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3])};
+  };
+  // O^T += V^T P^T with V^T by transpose reads: source lane (gq, row) addresses
+  // tile row 4*gq + row/4, dims 16*db + 4*(row%4) .. +3, i.e. chunk
+  // c = 2*db + (row%4)/2 (half row%2), stored at 16*(db/8) + ((2*(db%8) + (row%4)/2) ^ dswz)
+  auto values = [&](const unsigned char* vt, u32x2 pf) {
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int row = ln & 15, gq = ln >> 4;
     const int trow = 4 * gq + (row >> 2);
     const int tch = (row & 3) >> 1;
     const int tdsw = dswz(trow);
     int voff[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j)
-      voff[j] = (KVS ? 0 : L::KB) + trow * (2 * D) + (row & 1) * 8 + (((2 * j + tch) ^ tdsw) << 4);
+      voff[j] = trow * (2 * D) + (row & 1) * 8 + (((2 * j + tch) ^ tdsw) << 4);
 #pragma unroll
     for (int db = 0; db < NB; ++db) {
-      const u32x2 vf = lds_read_tr16(sp + voff[db & 7] + 256 * (db >> 3));
+      const u32x2 vf = lds_read_tr16(vt + voff[db & 7] + 256 * (db >> 3));
       oacc[db] = mfma16x16x16(vf, pf, oacc[db]);
     }
   };
 
-  // the previous tile's LDS reads have completed (its products consumed them)
-  // before the next tile's loads are requested
-  for (int i = 0; i < ntiles; ++i) {
-    if (i > 0) issue(i);
-    wait_vmcnt<0>();
-    compute(i);
+  if constexpr (KVS) {
+    // one tile slot: the previous tile's LDS reads have completed (its
+    // products consumed them) before the next tile's loads are requested
+    for (int i = 0; i < ntiles; ++i) {
+      if (i > 0) issue(kbase, i, kt);
+      wait_vmcnt<0>();
+      const u32x2 pf = softmax(i, scores(i));
+      values(kt, pf);
+    }
+  } else {
+    // keys of tile i+1 load during the softmax and value product of tile i,
+    // values of tile i+1 during the scores of tile i+1
+    for (int i = 0; i < ntiles; ++i) {
+      wait_vmcnt<NLD>();  // keys of tile i (its values may still be in flight)
+      const f32x4 sacc = scores(i);
+      const bool more = i + 1 < ntiles;
+      if (more) issue(kbase, i + 1, kt);
+      const u32x2 pf = softmax(i, sacc);
+      if (more) wait_vmcnt<NLD>();  // values of tile i (next keys may be in flight)
+      else wait_vmcnt<0>();
+      values(tv, pf);
+      if (more) issue(vbase, i + 1, tv);
+    }
   }
 
   // ---- partial (m, l, O) of this chunk for the G query heads ----
   l_run += __shfl_xor(l_run, 16);
   l_run += __shfl_xor(l_run, 32);
-  if (l16 < G) {
-    const size_t prow = ((size_t)b * a.Hq + hkv * G + l16) * a.nchunk + ch;
-    float* po = a.part_o + prow * D + 4 * g4;
+  if constexpr (NW == 1) {
+    if (l16 < G) {
+      const size_t prow = ((size_t)b * a.Hq + hkv * G + l16) * a.nchunk + ch;
+      float* po = a.part_o + prow * D + 4 * g4;
 #pragma unroll
-    for (int db = 0; db < NB; ++db) *reinterpret_cast<f32x4*>(po + 16 * db) = oacc[db];
-    if (g4 == 0) {
-      a.part_ml[prow * 2 + 0] = m_run;
-      a.part_ml[prow * 2 + 1] = l_run;
+      for (int db = 0; db < NB; ++db) *reinterpret_cast<f32x4*>(po + 16 * db) = oacc[db];
+      if (g4 == 0) {
+        a.part_ml[prow * 2 + 0] = m_run;
+        a.part_ml[prow * 2 + 1] = l_run;
+      }
+    }
+  } else {
+    // merge the NW waves through LDS (the tile slots are free now): wave w
+    // leaves O[w][n][dim] (G x D floats fit in its tile) and (m, l) per column
+    __syncthreads();
+    float* ow = reinterpret_cast<float*>(tk);
+    if (l16 < G) {
+#pragma unroll
+      for (int db = 0; db < NB; ++db)
+        *reinterpret_cast<f32x4*>(ow + ((size_t)w * G + l16) * D + 16 * db + 4 * g4) = oacc[db];
+      if (g4 == 0) {
+        mls[w][l16][0] = m_run;
+        mls[w][l16][1] = l_run;
+      }
+    }
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < G * D / 4; idx += 64 * NW) {
+      const int n = idx / (D / 4), e = 4 * (idx % (D / 4));
+      float M = -INFINITY;
+#pragma unroll
+      for (int v = 0; v < NW; ++v) M = fmaxf(M, mls[v][n][0]);
+      f32x4 o = {};
+      float l = 0.f;
+#pragma unroll
+      for (int v = 0; v < NW; ++v) {
+        const float f = __builtin_amdgcn_exp2f(mls[v][n][0] - M);  // 0 for a wave with no rows
+        o += f * *reinterpret_cast<const f32x4*>(ow + ((size_t)v * G + n) * D + e);
+        l += f * mls[v][n][1];
+      }
+      const size_t prow = ((size_t)b * a.Hq + hkv * G + n) * a.nchunk + ch;
+      *reinterpret_cast<f32x4*>(a.part_o + prow * D + e) = o;
+      if (e == 0) {
+        a.part_ml[prow * 2 + 0] = M;
+        a.part_ml[prow * 2 + 1] = l;
+      }
     }
   }
 }
 
-// Combine the chunk partials of query head (b, h): weights 2^(m_c - M).
+// Combine the chunk partials of query head (b, h): weights 2^(m_c - M).  Each
+// of the 128 threads owns 4 dims; the chunk loop keeps 4 loads in flight.
 template <bool OBF>
-__global__ void __launch_bounds__(256) decode_merge_kernel(DecodeArgs a) {
+__global__ void __launch_bounds__(128) decode_merge_kernel(DecodeArgs a) {
+  __shared__ float red[2][2];
   const int b = blockIdx.x / a.Hq, h = blockIdx.x % a.Hq;
-  const int D = a.D;
+  const int D = a.D, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int P = a.pos[b];
   const size_t orow = ((size_t)b * a.Hq + h) * D;
   if (P < 0 || (a.window == 0 && P >= a.capacity)) {
-    for (int e = threadIdx.x; e < D; e += 256) {
+    for (int e = tid; e < D; e += 128) {
       if constexpr (OBF) static_cast<uint16_t*>(a.out)[orow + e] = 0x7fc0;
       else static_cast<float*>(a.out)[orow + e] = __builtin_nanf("");
     }
@@ -275,30 +344,57 @@ __global__ void __launch_bounds__(256) decode_merge_kernel(DecodeArgs a) {
   const int last = a.window > 0 ? min(P, a.window - 1) : P;
   const int nch = last / a.chunk + 1;
   const size_t prow = ((size_t)b * a.Hq + h) * a.nchunk;
+  const float* ml = a.part_ml + prow * 2;
   float M = -INFINITY;
-  for (int c = 0; c < nch; ++c) M = fmaxf(M, a.part_ml[(prow + c) * 2]);
-  for (int e = threadIdx.x; e < D; e += 256) {
-    float o = 0.f, l = 0.f;
-    for (int c = 0; c < nch; ++c) {
-      const float f = __builtin_amdgcn_exp2f(a.part_ml[(prow + c) * 2] - M);
-      o += f * a.part_o[(prow + c) * D + e];
-      l += f * a.part_ml[(prow + c) * 2 + 1];
+  for (int c = tid; c < nch; c += 128) M = fmaxf(M, ml[2 * c]);
+  M = wave_max(M);
+  if (lane == 0) red[0][w] = M;
+  __syncthreads();
+  M = fmaxf(red[0][0], red[0][1]);
+  float l = 0.f;
+  for (int c = tid; c < nch; c += 128) l += __builtin_amdgcn_exp2f(ml[2 * c] - M) * ml[2 * c + 1];
+  l = wave_sum(l);
+  if (lane == 0) red[1][w] = l;
+  __syncthreads();
+  const float inv = 1.f / (red[1][0] + red[1][1]);
+  for (int e = 4 * tid; e < D; e += 512) {
+    const float* po = a.part_o + prow * D + e;
+    f32x4 o = {};
+    int c = 0;
+    for (; c + 4 <= nch; c += 4) {
+      f32x4 v[4];
+      float f[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        v[j] = *reinterpret_cast<const f32x4*>(po + (size_t)(c + j) * D);
+        f[j] = __builtin_amdgcn_exp2f(ml[2 * (c + j)] - M);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) o += f[j] * v[j];
     }
-    const float r = o / l;
-    if constexpr (OBF) static_cast<uint16_t*>(a.out)[orow + e] = (uint16_t)(pack_bf16(r, 0.f) & 0xffffu);
-    else static_cast<float*>(a.out)[orow + e] = r;
+    for (; c < nch; ++c)
+      o += __builtin_amdgcn_exp2f(ml[2 * c] - M) * *reinterpret_cast<const f32x4*>(po + (size_t)c * D);
+    o *= inv;
+    if constexpr (OBF) {
+      const u32x2 pk = {pack_bf16(o[0], o[1]), pack_bf16(o[2], o[3])};
+      *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.out) + orow + e) = pk;
+    } else {
+      *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + orow + e) = o;
+    }
   }
 }
 
 template <int D, int G, bool KVS>
 hipError_t launch_split(const DecodeArgs& a, hipStream_t st) {
+  constexpr int NW = KVS ? 4 : 1;
   const long long n = (long long)a.B * a.Hkv * a.nchunk;
   if (n > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   if (a.n_rot <= 64)
-    hipLaunchKernelGGL((decode_split_kernel<D, G, KVS, 4>), dim3((unsigned)n), dim3(64), 0, st, a);
+    hipLaunchKernelGGL((decode_split_kernel<D, G, KVS, 4, NW>), dim3((unsigned)n), dim3(64 * NW), 0,
+                       st, a);
   else
-    hipLaunchKernelGGL((decode_split_kernel<D, G, KVS, D / 32>), dim3((unsigned)n), dim3(64), 0, st,
-                       a);
+    hipLaunchKernelGGL((decode_split_kernel<D, G, KVS, D / 32, NW>), dim3((unsigned)n),
+                       dim3(64 * NW), 0, st, a);
   return hipGetLastError();
 }
 
@@ -336,8 +432,8 @@ hipError_t launch_decode_bf16(const DecodeArgs& a, bool kv_shared, bool out_bf16
   else return hipErrorInvalidValue;
   if (e != hipSuccess) return e;
   const long long n = (long long)a.B * a.Hq;
-  if (out_bf16) hipLaunchKernelGGL(decode_merge_kernel<true>, dim3((unsigned)n), dim3(256), 0, st, a);
-  else hipLaunchKernelGGL(decode_merge_kernel<false>, dim3((unsigned)n), dim3(256), 0, st, a);
+  if (out_bf16) hipLaunchKernelGGL(decode_merge_kernel<true>, dim3((unsigned)n), dim3(128), 0, st, a);
+  else hipLaunchKernelGGL(decode_merge_kernel<false>, dim3((unsigned)n), dim3(128), 0, st, a);
   return hipGetLastError();
 }
 
