@@ -221,6 +221,8 @@ __device__ __noinline__ void exact_row(const uint16_t* qp, const uint16_t* kp, c
 // SW = key dims the score product reads from the rotated slab: 128 (only
 // pairs < 64 may turn, e.g. p = 0.25 at D = 512) or D (any p).  Score k-steps
 // s < SW/16 read the slab, the others the raw key tile.
+// NST = LDS ring depth (2 or 3): each tile is computed whole (scores,
+// softmax, value product) while the next one or two tiles load.
 template <int D, int G, bool KVS, bool OBF, int SW, int NST, int MB>
 __global__ void __launch_bounds__(NW * 64, 1) prefill_kernel(PrefillArgs a) {
   constexpr int RW = 32 * MB;          // rows per wave
@@ -233,6 +235,7 @@ __global__ void __launch_bounds__(NW * 64, 1) prefill_kernel(PrefillArgs a) {
   static_assert(L::TOTAL <= 160 * 1024, "LDS budget");
   static_assert(SW >= 128 && SW <= D && NDS % 8 == 0 && NSS % 8 == 0, "tile shape");
   static_assert(L::STAGE % (1024 * NW) == 0, "stage = whole direct loads per wave");
+  static_assert(NST == 2 || NST == 3, "ring");
   __shared__ __attribute__((aligned(16))) unsigned char st0[L::STAGE];
   __shared__ __attribute__((aligned(16))) unsigned char st1[L::STAGE];
   __shared__ __attribute__((aligned(16))) unsigned char st2[NST == 3 ? L::STAGE : 16];
@@ -356,10 +359,9 @@ __global__ void __launch_bounds__(NW * 64, 1) prefill_kernel(PrefillArgs a) {
   }
   const float cs = a.scale_log2e;
 
-  // ---- one tile: scores, softmax, PV ----
-  auto compute = [&](int kt, auto stage) {
+  // ---- scores S^T = K~ Q~^T of one tile (fragments stream in groups of FG, one group ahead) ----
+  auto scores = [&](auto stage, f32x16 (&sacc)[MB]) {
     unsigned char* sp = stp(stage);
-    const int kv0 = kt * BN;
     // Lane parts of the fragment offsets, recomputed per tile from a laundered
     // lane id (cheap) so they do not occupy registers across the loop.
     int ln = lane;
@@ -371,57 +373,41 @@ __global__ void __launch_bounds__(NW * 64, 1) prefill_kernel(PrefillArgs a) {
     int soff[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) soff[i] = ((2 * i + hl) ^ sw_n) << 4;
-    // value operand by transpose reads: lane (g = ln/16, i = ln%16) reads row
-    // 4*(g/2) + i/4 (then +8 rows for the upper 4 keys, +16*k2) at dims
-    // 32*db + 16*(g%2) + 4*(i%4), i.e. chunk 4*db + tr_x, byte 8*(i%2)
-    const int tr_i = ln & 15, tr_g = ln >> 4;
-    const int tr_row = 4 * (tr_g >> 1) + (tr_i >> 2);
-    const int tr_x = 2 * (tr_g & 1) + ((tr_i & 3) >> 1);
-    // voff[h][e]: rows tr_row + 8h, 32-dim block db with db % 4 == e
-    int voff[2][4];
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        voff[h][e] = (tr_row + 8 * h) * (2 * D) + (tr_i & 1) * 8 +
-                     (((4 * e + tr_x) ^ swz(tr_row + 8 * h)) << 4);
     const int kbase_off = L::KOFF + l32 * (2 * D);
     const int sbase_off = l32 * (2 * SW);
-
-    f32x16 sacc[MB];
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) sacc[mb] = f32x16{};
-    {
-      // k-step s lives in the slab for s < NSS, in the raw key tile otherwise;
-      // fragments stream in groups of FG, one group ahead
-      auto frag = [&](int s) -> u32x4 {
-        if (s < NSS) return lds_at<u32x4>(sp, sbase_off + 256 * (s >> 3) + soff[s & 7]);
-        return lds_at<u32x4>(sp, kbase_off + 256 * (s >> 3) + soff[s & 7]);
-      };
-      constexpr int NG = NDS / FG;
-      u32x4 kf[2][FG];
+    // k-step s lives in the slab for s < NSS, in the raw key tile otherwise
+    auto frag = [&](int s) -> u32x4 {
+      if (s < NSS) return lds_at<u32x4>(sp, sbase_off + 256 * (s >> 3) + soff[s & 7]);
+      return lds_at<u32x4>(sp, kbase_off + 256 * (s >> 3) + soff[s & 7]);
+    };
+    constexpr int NG = NDS / FG;
+    u32x4 kf[2][FG];
 #pragma unroll
-      for (int i = 0; i < FG; ++i) kf[0][i] = frag(i);
+    for (int i = 0; i < FG; ++i) kf[0][i] = frag(i);
 #pragma unroll
-      for (int g = 0; g < NG; ++g) {
-        if (g + 1 < NG) {
+    for (int g = 0; g < NG; ++g) {
+      if (g + 1 < NG) {
 #pragma unroll
-          for (int i = 0; i < FG; ++i) kf[(g + 1) & 1][i] = frag(FG * (g + 1) + i);
-        }
-#pragma unroll
-        for (int i = 0; i < FG; ++i)
-#pragma unroll
-          for (int mb = 0; mb < MB; ++mb)
-            sacc[mb] = mfma32x32x16(kf[g & 1][i], qf[mb][FG * g + i], sacc[mb]);
-        __builtin_amdgcn_sched_barrier(0);
+        for (int i = 0; i < FG; ++i) kf[(g + 1) & 1][i] = frag(FG * (g + 1) + i);
       }
-    }
-
-    u32x4 pf[MB][2];
-    const bool need_mask = (kv0 + BN - 1 > tw0) || (W > 0 && kv0 <= tw1 - W);
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      if (need_mask) {  // wave-uniform
+      for (int i = 0; i < FG; ++i)
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+          sacc[mb] = mfma32x32x16(kf[g & 1][i], qf[mb][FG * g + i], sacc[mb]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // ---- causal / band mask of tile kt (edge tiles only) ----
+  auto mask = [&](int kt, f32x16 (&sacc)[MB]) {
+    const int kv0 = kt * BN;
+    const bool need_mask = (kv0 + BN - 1 > tw0) || (W > 0 && kv0 <= tw1 - W);
+    if (need_mask) {  // wave-uniform
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
         const int lo = W > 0 ? tq[mb] - W + 1 : 0;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -429,6 +415,13 @@ __global__ void __launch_bounds__(NW * 64, 1) prefill_kernel(PrefillArgs a) {
           sacc[mb][r] = (j <= tq[mb] && j >= lo) ? sacc[mb][r] : -INFINITY;
         }
       }
+    }
+  };
+
+  // ---- softmax of masked scores -> P^T as B operands of the value product ----
+  auto softmax = [&](const f32x16 (&sacc)[MB], u32x4 (&pf)[MB][2]) {
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
       float mx = sacc[mb][0];
 #pragma unroll
       for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sacc[mb][r]);
@@ -451,39 +444,66 @@ __global__ void __launch_bounds__(NW * 64, 1) prefill_kernel(PrefillArgs a) {
         }
       l_run[mb] += lsum;
     }
-    __builtin_amdgcn_sched_barrier(0);
+  };
 
-    // O^T += V^T P^T, V^T fragments by transpose reads of the raw value tile
+  // ---- O^T += V^T P^T, V^T fragments by transpose reads of the raw value tile ----
+  auto values = [&](auto stage, const u32x4 (&pf)[MB][2]) {
+    unsigned char* sp = stp(stage);
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    // value operand by transpose reads: lane (g = ln/16, i = ln%16) reads row
+    // 4*(g/2) + i/4 (then +8 rows for the upper 4 keys, +16*k2) at dims
+    // 32*db + 16*(g%2) + 4*(i%4), i.e. chunk 4*db + tr_x, byte 8*(i%2)
+    const int tr_i = ln & 15, tr_g = ln >> 4;
+    const int tr_row = 4 * (tr_g >> 1) + (tr_i >> 2);
+    const int tr_x = 2 * (tr_g & 1) + ((tr_i & 3) >> 1);
+    // voff[h][e]: rows tr_row + 8h, 32-dim block db with db % 4 == e
+    int voff[2][4];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        voff[h][e] = (tr_row + 8 * h) * (2 * D) + (tr_i & 1) * 8 +
+                     (((4 * e + tr_x) ^ swz(tr_row + 8 * h)) << 4);
     auto vfrag = [&](int db, int k2) -> u32x4 {
       const int off = L::VOFF + 256 * (db >> 2) + (16 * k2) * (2 * D);
       const u32x2 lo = lds_read_tr16(sp + off + voff[0][db & 3]);
       const u32x2 hi = lds_read_tr16(sp + off + voff[1][db & 3]);
       return u32x4{lo[0], lo[1], hi[0], hi[1]};
     };
-    {
-      constexpr int NG = 2 * NDB / FG;
-      u32x4 vf[2][FG];
+    constexpr int NG = 2 * NDB / FG;
+    u32x4 vf[2][FG];
 #pragma unroll
-      for (int i = 0; i < FG; ++i) vf[0][i] = vfrag(i >> 1, i & 1);
+    for (int i = 0; i < FG; ++i) vf[0][i] = vfrag(i >> 1, i & 1);
 #pragma unroll
-      for (int g = 0; g < NG; ++g) {
-        if (g + 1 < NG) {
-#pragma unroll
-          for (int i = 0; i < FG; ++i) {
-            const int f = FG * (g + 1) + i;
-            vf[(g + 1) & 1][i] = vfrag(f >> 1, f & 1);
-          }
-        }
+    for (int g = 0; g < NG; ++g) {
+      if (g + 1 < NG) {
 #pragma unroll
         for (int i = 0; i < FG; ++i) {
-          const int f = FG * g + i;
-#pragma unroll
-          for (int mb = 0; mb < MB; ++mb)
-            oacc[mb][f >> 1] = mfma32x32x16(vf[g & 1][i], pf[mb][f & 1], oacc[mb][f >> 1]);
+          const int f = FG * (g + 1) + i;
+          vf[(g + 1) & 1][i] = vfrag(f >> 1, f & 1);
         }
-        __builtin_amdgcn_sched_barrier(0);
       }
+#pragma unroll
+      for (int i = 0; i < FG; ++i) {
+        const int f = FG * g + i;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+          oacc[mb][f >> 1] = mfma32x32x16(vf[g & 1][i], pf[mb][f & 1], oacc[mb][f >> 1]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
+  };
+
+  // one whole tile
+  auto compute = [&](int kt, auto stage) {
+    f32x16 sacc[MB];
+    u32x4 pf[MB][2];
+    scores(stage, sacc);
+    mask(kt, sacc);
+    softmax(sacc, pf);
+    __builtin_amdgcn_sched_barrier(0);
+    values(stage, pf);
   };
   // a wave skips tiles where none of its rows sees a key (past its last
   // token, before its window, or padding)
@@ -494,7 +514,7 @@ __global__ void __launch_bounds__(NW * 64, 1) prefill_kernel(PrefillArgs a) {
 
   // ---- KV loop, unrolled by the ring depth so every stage is a fixed object ----
   // The tile count is padded up to a multiple of the ring depth; padding tiles
-  // lie past the last query token, so every wave skips them.
+  // lie past the last query token, so every key in them is masked.
   const int ktp = kt0 + (kt1 - kt0 + NST) / NST * NST - 1;  // last (padded) tile
   if constexpr (NST == 3) {
     // tile kt+2 is requested while tile kt is computed; at the end of the

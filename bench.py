@@ -336,14 +336,14 @@ def cpu_baseline(args, loc, glo, L0, G0, Lout, Gout):
     # calibration run, then a sample sized for about args.cpu_seconds of oracle time;
     # global rows (2^18 keys each) dominate, local rows ride along 8 per global row
     n_g = 4
-    for _ in range(2):
+    for _ in range(5):
         rows_g = np.unique(np.concatenate([[0, 1, S - 1], rng.choice(S, n_g, replace=False)]))
         rows_l = np.unique(np.concatenate([[0, 1, 1023, 1024, S - 1],
                                            rng.choice(S, 8 * n_g, replace=False)]))
         t, og, ol = run(rows_g, rows_l)
-        if t >= 0.5 * args.cpu_seconds:
+        if t >= 0.6 * args.cpu_seconds or n_g >= 4096:
             break
-        n_g = max(4, min(4096, int(n_g * args.cpu_seconds / max(t, 1e-3))))
+        n_g = max(n_g + 1, min(4096, int(n_g * args.cpu_seconds / max(t, 1e-3))))
     f = flops(rows_g, rows_l)
     got_g = Gout.view(S, glo.Hq, glo.d)[torch.as_tensor(rows_g, device=Gout.device)]
     got_l = Lout.view(S, loc.Hq, loc.d)[torch.as_tensor(rows_l, device=Lout.device)]
