@@ -88,21 +88,28 @@ __device__ __forceinline__ T& lds_at(unsigned char* base, int off) {
 
 // RK = score k-steps (32 dims each) that may hold turning pairs: 4 when
 // n_rot <= 64 (dims < 128, e.g. p-RoPE at p = 0.25), else all of them.
-// NW = waves per workgroup.  K=V: NW waves split the chunk and merge their
-// partials in LDS at the end (shorter waves, one partial per chunk).
-// Separate K and V: one wave whose K and V tiles are separate LDS objects,
-// so the next tile's keys are requested as soon as the scores are done and
-// its values as soon as the value product is done.
-template <int D, int G, bool KVS, int RK, int NW>
+// NW = waves per workgroup.  With NW > 1 the waves split the chunk and merge
+// their partials in LDS at the end (shorter waves, one partial per chunk);
+// when one chunk covers every row the workgroup writes the final output and
+// no merge kernel runs.
+// Separate K and V at D = 256: one wave; keys load straight into registers
+// (already in the score operand layout) two tiles ahead, values into the
+// second of two LDS slots one tile ahead, so about a tile and a half is always
+// in flight.  Separate K and V at D = 512: one wave whose
+// K and V tiles are separate LDS objects; the next keys are requested as soon
+// as the scores are done, the next values as soon as the value product is.
+template <int D, int G, bool KVS, int RK, int NW, bool OBF>
 __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 decode_split_kernel(DecodeArgs a) {
   constexpr int NS = D / 32;  // 32-dim k-steps of the score product
   constexpr int NB = D / 16;  // 16-dim blocks of the output
   constexpr int KB = TR * D * 2;     // one tensor's tile, bytes
   constexpr int NLD = KB / 1024;     // direct loads per lane per tensor tile
-  static_assert(G <= 8 && RK <= NS && NS % 4 == 0 && (KVS || NW == 1), "shape");
-  __shared__ __attribute__((aligned(16))) unsigned char tk[NW * KB];      // K (or K=V) tile per wave
-  __shared__ __attribute__((aligned(16))) unsigned char tv[KVS ? 16 : KB];  // V tile
+  constexpr bool KREG = !KVS && D == 256;  // keys through registers
+  static_assert(G <= 8 && RK <= NS && NS % 4 == 0 && (KVS || KREG || NW == 1), "shape");
+  __shared__ __attribute__((aligned(16))) unsigned char tk[KREG ? 16 : NW * KB];   // K (or K=V) tile per wave
+  __shared__ __attribute__((aligned(16))) unsigned char tv[KVS ? 16 : NW * KB];    // V tile per wave
+  __shared__ __attribute__((aligned(16))) unsigned char tv2[KREG ? NW * KB : 16];  // second V slot per wave
   __shared__ double gtab[D / 2];
   __shared__ float mls[NW][16][2];
 
@@ -114,7 +121,16 @@ decode_split_kernel(DecodeArgs a) {
   const int b = bh / a.Hkv, hkv = bh % a.Hkv;
   const int P = a.pos[b];
   const int W = a.window, C = a.capacity;
-  if (P < 0 || (W == 0 && P >= C)) return;  // the merge writes NaN rows
+  const bool direct = NW > 1 && a.nchunk == 1;  // this workgroup writes the output
+  if (P < 0 || (W == 0 && P >= C)) {  // bad position: NaN rows (else the merge writes them)
+    if (direct)
+      for (int idx = threadIdx.x; idx < G * D; idx += 64 * NW) {
+        const size_t o = ((size_t)b * a.Hq + hkv * G) * D + idx;
+        if constexpr (OBF) static_cast<uint16_t*>(a.out)[o] = 0x7fc0;
+        else static_cast<float*>(a.out)[o] = __builtin_nanf("");
+      }
+    return;
+  }
   const int last = W > 0 ? min(P, W - 1) : P;  // highest row index that may be visible
   const int r0 = ch * a.chunk;
   if (r0 > last) return;
@@ -124,7 +140,9 @@ decode_split_kernel(DecodeArgs a) {
   const int wr0 = min(r0 + w * per, r1), wr1 = min(wr0 + per, r1);
   const int ntiles = (wr1 - wr0 + TR - 1) / TR;
   const int n_rot = a.n_rot;
-  unsigned char* kt = tk + w * KB;
+  unsigned char* kt = tk + (KREG ? 0 : w * KB);
+  unsigned char* vt0 = tv + (KVS ? 0 : w * KB);
+  unsigned char* vt1 = tv2 + (KREG ? w * KB : 0);
 
   // query heads hkv*G .. +G-1 as B operands of the score product (columns >= G
   // are zero); loaded first, so waiting for them leaves the tile loads below in flight
@@ -156,13 +174,32 @@ decode_split_kernel(DecodeArgs a) {
       lds_dma16(rs, voff, dst + n * 1024);
     }
   };
-  // the barrier's fence waits for every outstanding load, so the angle table
-  // is built before the first tile is requested
+  // The angle table is shared by the waves of a workgroup.  With several
+  // waves the barrier (whose fence waits for every outstanding load) comes
+  // before the first tile is requested; a single wave reads its own LDS
+  // writes in order and needs no barrier, so its query and tile loads overlap.
   for (int t = threadIdx.x; t < D / 2; t += 64 * NW) gtab[t] = rope_rev_per_pos(t, D, a.log2_theta);
-  __syncthreads();
+  if constexpr (NW > 1) __syncthreads();
+  // keys of tile i into registers, lane (row = l % 16, gq = l / 16) holding
+  // dims 32*s + 8*gq .. +7 of its row for every k-step s; rows past wr1 read as zeros
+  auto load_keys = [&](int i, u32x4 (&kr)[NS]) {
+    const int rr0 = wr0 + i * TR;
+    const uint32_t bytes = (uint32_t)min(TR, wr1 - rr0) * (2 * D);
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(kbase + (size_t)rr0 * D, bytes);
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const uint32_t base = (uint32_t)(ln & 15) * (2 * D) + (uint32_t)(ln >> 4) * 16;
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+      kr[s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, base + 64 * s, 0, 0));
+  };
+  u32x4 kr0[KREG ? NS : 1], kr1[KREG ? NS : 1], kr2[KREG ? NS : 1];
   if (ntiles > 0) {
-    issue(kbase, 0, kt);
-    if constexpr (!KVS) issue(vbase, 0, tv);
+    if constexpr (KREG) load_keys(0, kr0);
+    else issue(kbase, 0, kt);
+    if constexpr (!KVS) issue(vbase, 0, vt0);
+    if constexpr (KREG)
+      if (ntiles > 1) load_keys(1, kr1);
   }
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
@@ -176,8 +213,9 @@ decode_split_kernel(DecodeArgs a) {
   float m_run = -INFINITY, l_run = 0.f;  // per column (query head l16), base 2
   const float cs = a.scale_log2e;
 
-  // scores of tile i from the key tile: S^T register j = key 4*gq + j of column l16
-  auto scores = [&](int i) -> f32x4 {
+  // scores of tile i from the key tile (or, kr non-null, from key registers):
+  // S^T register j = key 4*gq + j of column l16
+  auto scores = [&](int i, const u32x4* kr) -> f32x4 {
     const int rr0 = wr0 + i * TR;
     int ln = lane;
     asm volatile("" : "+v"(ln));
@@ -192,7 +230,7 @@ decode_split_kernel(DecodeArgs a) {
     f32x4 sacc0 = {}, sacc1 = {};  // even / odd k-steps: two independent chains
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-      u32x4 kf = lds_at<u32x4>(kt, koff[s & 3] + 256 * (s >> 2));
+      u32x4 kf = KREG ? kr[s] : lds_at<u32x4>(kt, koff[s & 3] + 256 * (s >> 2));
       if (s < RK) kf = rotate_chunk_bf16(kf, 4 * s + gq, tpos, n_rot, gtab);  // per-pair select inside
       if (s & 1) sacc1 = mfma16x16x32(kf, qf[s], sacc1);
       else sacc0 = mfma16x16x32(kf, qf[s], sacc0);
@@ -254,22 +292,46 @@ decode_split_kernel(DecodeArgs a) {
     for (int i = 0; i < ntiles; ++i) {
       if (i > 0) issue(kbase, i, kt);
       wait_vmcnt<0>();
-      const u32x2 pf = softmax(i, scores(i));
+      const u32x2 pf = softmax(i, scores(i, nullptr));
       values(kt, pf);
+    }
+  } else if constexpr (KREG) {
+    // step i requests the values of tile i+1, then the keys of tile i+2, and
+    // computes tile i.  Issue order is V_i, K_(i+1), V_(i+1), K_(i+2), so
+    // waiting until only the last three groups are in flight means keys and
+    // values of tile i have landed.  Key sets rotate over 3 registers blocks
+    // and value slots over 2, so the loop is unrolled by 6.
+    auto step = [&](int i, u32x4 (&kc)[NS], u32x4 (&kn2)[NS], unsigned char* vc,
+                    unsigned char* vn) {
+      if (i + 1 < ntiles) issue(vbase, i + 1, vn);
+      if (i + 2 < ntiles) load_keys(i + 2, kn2);
+      if (i + 2 < ntiles) wait_vmcnt<2 * NS + NLD>();
+      else if (i + 1 < ntiles) wait_vmcnt<NS + NLD>();
+      else wait_vmcnt<0>();
+      const u32x2 pf = softmax(i, scores(i, kc));
+      values(vc, pf);
+    };
+    for (int i = 0; i < ntiles; i += 6) {
+      step(i, kr0, kr2, vt0, vt1);
+      if (i + 1 < ntiles) step(i + 1, kr1, kr0, vt1, vt0);
+      if (i + 2 < ntiles) step(i + 2, kr2, kr1, vt0, vt1);
+      if (i + 3 < ntiles) step(i + 3, kr0, kr2, vt1, vt0);
+      if (i + 4 < ntiles) step(i + 4, kr1, kr0, vt0, vt1);
+      if (i + 5 < ntiles) step(i + 5, kr2, kr1, vt1, vt0);
     }
   } else {
     // keys of tile i+1 load during the softmax and value product of tile i,
     // values of tile i+1 during the scores of tile i+1
     for (int i = 0; i < ntiles; ++i) {
       wait_vmcnt<NLD>();  // keys of tile i (its values may still be in flight)
-      const f32x4 sacc = scores(i);
+      const f32x4 sacc = scores(i, nullptr);
       const bool more = i + 1 < ntiles;
       if (more) issue(kbase, i + 1, kt);
       const u32x2 pf = softmax(i, sacc);
       if (more) wait_vmcnt<NLD>();  // values of tile i (next keys may be in flight)
       else wait_vmcnt<0>();
-      values(tv, pf);
-      if (more) issue(vbase, i + 1, tv);
+      values(vt0, pf);
+      if (more) issue(vbase, i + 1, vt0);
     }
   }
 
@@ -291,7 +353,7 @@ decode_split_kernel(DecodeArgs a) {
     // merge the NW waves through LDS (the tile slots are free now): wave w
     // leaves O[w][n][dim] (G x D floats fit in its tile) and (m, l) per column
     __syncthreads();
-    float* ow = reinterpret_cast<float*>(tk);
+    float* ow = reinterpret_cast<float*>(KREG ? tv : tk);
     if (l16 < G) {
 #pragma unroll
       for (int db = 0; db < NB; ++db)
@@ -315,11 +377,22 @@ decode_split_kernel(DecodeArgs a) {
         o += f * *reinterpret_cast<const f32x4*>(ow + ((size_t)v * G + n) * D + e);
         l += f * mls[v][n][1];
       }
-      const size_t prow = ((size_t)b * a.Hq + hkv * G + n) * a.nchunk + ch;
-      *reinterpret_cast<f32x4*>(a.part_o + prow * D + e) = o;
-      if (e == 0) {
-        a.part_ml[prow * 2 + 0] = M;
-        a.part_ml[prow * 2 + 1] = l;
+      if (direct) {
+        o *= 1.f / l;
+        const size_t orow = ((size_t)b * a.Hq + hkv * G + n) * D + e;
+        if constexpr (OBF) {
+          const u32x2 pk = {pack_bf16(o[0], o[1]), pack_bf16(o[2], o[3])};
+          *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.out) + orow) = pk;
+        } else {
+          *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + orow) = o;
+        }
+      } else {
+        const size_t prow = ((size_t)b * a.Hq + hkv * G + n) * a.nchunk + ch;
+        *reinterpret_cast<f32x4*>(a.part_o + prow * D + e) = o;
+        if (e == 0) {
+          a.part_ml[prow * 2 + 0] = M;
+          a.part_ml[prow * 2 + 1] = l;
+        }
       }
     }
   }
@@ -384,28 +457,38 @@ __global__ void __launch_bounds__(128) decode_merge_kernel(DecodeArgs a) {
   }
 }
 
-template <int D, int G, bool KVS>
+// waves per split workgroup (the D = 512 separate-K/V path keeps one)
+constexpr int split_waves(int D, bool kv_shared) { return (kv_shared || D == 256) ? 4 : 1; }
+
+template <int D, int G, bool KVS, bool OBF>
 hipError_t launch_split(const DecodeArgs& a, hipStream_t st) {
-  constexpr int NW = KVS ? 4 : 1;
+  constexpr int NW = split_waves(D, KVS);
   const long long n = (long long)a.B * a.Hkv * a.nchunk;
   if (n > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   if (a.n_rot <= 64)
-    hipLaunchKernelGGL((decode_split_kernel<D, G, KVS, 4, NW>), dim3((unsigned)n), dim3(64 * NW), 0,
-                       st, a);
+    hipLaunchKernelGGL((decode_split_kernel<D, G, KVS, 4, NW, OBF>), dim3((unsigned)n),
+                       dim3(64 * NW), 0, st, a);
   else
-    hipLaunchKernelGGL((decode_split_kernel<D, G, KVS, D / 32, NW>), dim3((unsigned)n),
+    hipLaunchKernelGGL((decode_split_kernel<D, G, KVS, D / 32, NW, OBF>), dim3((unsigned)n),
                        dim3(64 * NW), 0, st, a);
   return hipGetLastError();
 }
 
-template <int D, bool KVS>
+template <int D, bool KVS, bool OBF>
 hipError_t launch_split_g(const DecodeArgs& a, hipStream_t st) {
   switch (a.Hq / a.Hkv) {
-    case 1: return launch_split<D, 1, KVS>(a, st);
-    case 2: return launch_split<D, 2, KVS>(a, st);
-    case 4: return launch_split<D, 4, KVS>(a, st);
-    case 8: return launch_split<D, 8, KVS>(a, st);
+    case 1: return launch_split<D, 1, KVS, OBF>(a, st);
+    case 2: return launch_split<D, 2, KVS, OBF>(a, st);
+    case 4: return launch_split<D, 4, KVS, OBF>(a, st);
+    case 8: return launch_split<D, 8, KVS, OBF>(a, st);
   }
+  return hipErrorInvalidValue;
+}
+
+template <bool OBF>
+hipError_t launch_split_d(const DecodeArgs& a, bool kv_shared, hipStream_t st) {
+  if (a.D == 256) return kv_shared ? launch_split_g<256, true, OBF>(a, st) : launch_split_g<256, false, OBF>(a, st);
+  if (a.D == 512) return kv_shared ? launch_split_g<512, true, OBF>(a, st) : launch_split_g<512, false, OBF>(a, st);
   return hipErrorInvalidValue;
 }
 
@@ -414,7 +497,7 @@ hipError_t launch_split_g(const DecodeArgs& a, hipStream_t st) {
 int decode_chunk_rows(int D, int capacity, int window, bool f32) {
   (void)D;
   if (f32) return capacity;
-  if (window > 0) return 128;  // ring: 4 chunks of a 512-slot window
+  if (window > 0) return 512;  // ring: one 4-wave workgroup per 512 slots
   return 1024;
 }
 
@@ -426,11 +509,11 @@ int decode_num_chunks(int D, int capacity, int window, bool f32) {
 hipError_t launch_decode_bf16(const DecodeArgs& a, bool kv_shared, bool out_bf16,
                               hipStream_t st) {
   if ((long long)a.B * a.Hkv == 0) return hipSuccess;
-  hipError_t e;
-  if (a.D == 256) e = kv_shared ? launch_split_g<256, true>(a, st) : launch_split_g<256, false>(a, st);
-  else if (a.D == 512) e = kv_shared ? launch_split_g<512, true>(a, st) : launch_split_g<512, false>(a, st);
-  else return hipErrorInvalidValue;
+  const hipError_t e = out_bf16 ? launch_split_d<true>(a, kv_shared, st)
+                                : launch_split_d<false>(a, kv_shared, st);
   if (e != hipSuccess) return e;
+  // a single chunk per (b, kv head) split over several waves is finished in place
+  if (a.nchunk == 1 && split_waves(a.D, kv_shared) > 1) return hipSuccess;
   const long long n = (long long)a.B * a.Hq;
   if (out_bf16) hipLaunchKernelGGL(decode_merge_kernel<true>, dim3((unsigned)n), dim3(128), 0, st, a);
   else hipLaunchKernelGGL(decode_merge_kernel<false>, dim3((unsigned)n), dim3(128), 0, st, a);

@@ -123,6 +123,6 @@ def test_prefill_workspace_size():
 def test_workspace_size():
     f = L.lib().g4attn_decode_workspace_bytes
     assert f(64, 16, 2, 512, 65536, 0) == 64 * 16 * 64 * (512 + 2) * 4  # 1024-row chunks
-    assert f(64, 16, 8, 256, 512, 512) == 64 * 16 * 4 * (256 + 2) * 4
+    assert f(64, 16, 8, 256, 512, 512) == 64 * 16 * 1 * (256 + 2) * 4  # one 512-slot chunk
     assert f(1, 16, 8, 256, 1024, 512) == 0  # ring capacity must equal the window
     assert f(1, 0, 8, 256, 512, 512) == 0
