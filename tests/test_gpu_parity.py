@@ -156,6 +156,12 @@ DEC = [
     inputs.DecodeLayer("local", 4, 16, 8, 256, 512, 512, 1e4, 1.0),
     inputs.DecodeLayer("local", 3, 8, 4, 256, 96, 96, 1e4, 1.0),
     inputs.DecodeLayer("global", 3, 8, 1, 512, 700, 0, 1e6, 0.25),
+    # two 512-row chunks of a 1024-slot ring (merge kernel), G = 1
+    inputs.DecodeLayer("local", 4, 4, 4, 256, 1024, 1024, 1e4, 1.0),
+    # separate K and V at d = 512 (one-wave path), every pair turning, G = 4
+    inputs.DecodeLayer("local", 3, 8, 2, 512, 256, 256, 1e4, 1.0),
+    # separate K and V in a linear cache (no window)
+    inputs.DecodeLayer("local", 3, 4, 2, 256, 700, 0, 1e4, 1.0),
 ]
 
 
@@ -169,6 +175,38 @@ def test_decode_small(layer, dtype):
         lengths = torch.tensor([1, min(2049, C // 2 + 1), C, min(1500, C - 3)][:layer.B])
     out, ref = run_decode(layer, dtype, lengths)
     assert_parity(out, ref, dtype, str(layer))
+
+
+@pytest.mark.parametrize("layer", [DEC[1], DEC[0]], ids=["local-direct", "global-merge"])
+def test_decode_bf16_output(layer):
+    lengths = torch.tensor([1, 300, layer.capacity, 77])
+    q, kc, vc, pos, _ = inputs.decode_inputs(layer, 98, 0, torch.bfloat16, DEV, lengths)
+    out = g4.decode(q, kc, vc, pos, layer.window, layer.theta, layer.p, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert out.dtype == torch.bfloat16
+    ref = oracle.decode(to_oracle(q), to_oracle(kc), None if vc is None else to_oracle(vc),
+                        pos.cpu().numpy(), layer.window, layer.theta, layer.p)
+    got = out.float().cpu().double().numpy()
+    assert np.all(np.abs(got - ref) <= 1e-2 + 2.0 ** -8 * np.abs(ref))
+
+
+def test_decode_ring_bad_positions_nan():
+    """The ring path finishes rows in place: a negative position gives NaN there too."""
+    layer = inputs.DecodeLayer("local", 3, 4, 2, 256, 512, 512, 1e4, 1.0)
+    q, kc, vc, pos, _ = inputs.decode_inputs(layer, 99, 0, torch.bfloat16, DEV,
+                                             torch.tensor([10, 600, 3]))
+    pos = torch.tensor([-1, 599, -7], dtype=torch.int32, device=DEV)
+    out = g4.decode(q, kc, vc, pos, 512, 1e4, 1.0)
+    torch.cuda.synchronize()
+    assert torch.isnan(out[0]).all() and torch.isfinite(out[1]).all() and torch.isnan(out[2]).all()
+
+
+@pytest.mark.parametrize("S", [1, 31, 33])
+def test_prefill_short_sequences(S):
+    for layer in (inputs.Layer("global", 2, S, 8, 1, 512, 0, 1e6, 0.25),
+                  inputs.Layer("local", 2, S, 4, 2, 256, 16, 1e4, 1.0)):
+        out, (q, k, v, pos, W) = run_prefill(layer, torch.bfloat16, wl=94)
+        assert_parity(out, oracle_prefill(layer, q, k, v, pos, W), torch.bfloat16, str(layer))
 
 
 def test_decode_bad_positions_nan():
