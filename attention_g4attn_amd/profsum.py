@@ -19,6 +19,7 @@ import statistics
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 KERNEL_SOURCES = ["attention_g4attn_amd/csrc/prefill.hpp", "attention_g4attn_amd/csrc/common.hpp",
                   "attention_g4attn_amd/csrc/prefill_kv512.hip"]
+DECODE_SOURCES = ["attention_g4attn_amd/csrc/decode_bf16.hip", "attention_g4attn_amd/csrc/common.hpp"]
 
 
 def source_hash(files=KERNEL_SOURCES):
@@ -79,8 +80,8 @@ def traffic(args):
         f"hbm_read_bytes_per_launch: {fb:.6e}",
         f"hbm_write_bytes_per_launch: {wb:.6e}",
         f"hbm_bytes_per_launch: {fb + wb:.6e}",
-        f"source_sha256: {source_hash()}",
-        "sources: " + ", ".join(KERNEL_SOURCES),
+        f"source_sha256: {source_hash(args.sources)}",
+        "sources: " + ", ".join(args.sources),
     ]
     open(args.out, "w").write("\n".join(lines) + "\n")
 
@@ -100,6 +101,8 @@ def main():
     t.add_argument("--cmd-fetch", required=True)
     t.add_argument("--cmd-write", required=True)
     t.add_argument("--out", required=True)
+    t.add_argument("--sources", nargs="+", default=KERNEL_SOURCES,
+                   help="files whose sha256 identifies the kernel version")
     a = ap.parse_args()
     stats(a) if a.what == "stats" else traffic(a)
 

@@ -43,19 +43,22 @@ def parse():
     return ap.parse_args()
 
 
-TRAFFIC_SUMMARY = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
-                               "prefill_global_kv512_s262144_hbm_traffic.txt")
-def measured_traffic():
-    """HBM bytes per launch of the global prefill kernel, from the committed
-    rocprofv3 counter summary, or None when the kernel sources changed since."""
+PROFILES = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles")
+TRAFFIC_SUMMARY = os.path.join(PROFILES, "prefill_global_kv512_s262144_hbm_traffic.txt")
+DECODE_TRAFFIC_SUMMARY = os.path.join(PROFILES, "decode_global_kv512_b64_hbm_traffic.txt")
+def measured_traffic(path=TRAFFIC_SUMMARY):
+    """HBM bytes per launch of a kernel, from a committed rocprofv3 counter
+    summary, or None when the kernel sources it names changed since."""
     try:
-        text = open(TRAFFIC_SUMMARY).read()
+        text = open(path).read()
     except OSError:
         return None
     vals = dict(line.split(":", 1) for line in text.splitlines()
-                if ":" in line and line.split(":", 1)[0] in ("source_sha256", "hbm_bytes_per_launch"))
+                if ":" in line and line.split(":", 1)[0] in ("source_sha256", "hbm_bytes_per_launch",
+                                                            "sources"))
     from attention_g4attn_amd.profsum import source_hash
-    if vals.get("source_sha256", "").strip() != source_hash():
+    sources = [f.strip() for f in vals.get("sources", "").split(",") if f.strip()]
+    if not sources or vals.get("source_sha256", "").strip() != source_hash(sources):
         return None
     try:
         return float(vals["hbm_bytes_per_launch"])
@@ -225,7 +228,8 @@ def main():
         ach = bdg / tg / 1e6
         roof_dec = {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": ach / HBM_PEAK_GBS, "bytes_per_launch": bdg,
-                    "kernel": "decode_split_kernel<512,8,KV=V> + merge"}
+                    "traffic": measured_traffic(DECODE_TRAFFIC_SUMMARY),
+                    "kernel": "g4a::decode_split_kernel<512, 8, true, 4, 4, false> + decode_merge_kernel"}
 
     cpu = None
     if not args.no_cpu_baseline and run_global and run_local:
