@@ -236,6 +236,11 @@ __global__ void __launch_bounds__(NW * 64, 1) prefill_kernel(PrefillArgs a) {
   static_assert(SW >= 128 && SW <= D && NDS % 8 == 0 && NSS % 8 == 0, "tile shape");
   static_assert(L::STAGE % (1024 * NW) == 0, "stage = whole direct loads per wave");
   static_assert(NST == 2 || NST == 3, "ring");
+  // With two query blocks per wave the score and output accumulators leave
+  // few registers: the lane parts of LDS offsets are then recomputed per tile
+  // from an opaque copy of the lane id instead of staying live across the
+  // loop. With one block they fit and stay live.
+  constexpr bool RECOMP = MB == 2;
   __shared__ __attribute__((aligned(16))) unsigned char st0[L::STAGE];
   __shared__ __attribute__((aligned(16))) unsigned char st1[L::STAGE];
   __shared__ __attribute__((aligned(16))) unsigned char st2[NST == 3 ? L::STAGE : 16];
@@ -311,12 +316,10 @@ __global__ void __launch_bounds__(NW * 64, 1) prefill_kernel(PrefillArgs a) {
     constexpr int RPI = 1024 / RB;            // rows per direct load
     constexpr int LPW = BN / RPI / NW;        // direct loads per wave
     const __amdgpu_buffer_rsrc_t rs = make_rsrc(base, rows * rbytes - (rbytes - RB));
-    // the lane id is laundered so the offsets below are recomputed here (two
-    // or three instructions) instead of being held across the loop
     int ln = lane;
     int wl = __builtin_amdgcn_readfirstlane(w);
     uint32_t rb = __builtin_amdgcn_readfirstlane(rbytes);
-    asm volatile("" : "+v"(ln), "+s"(wl), "+s"(rb));
+    if constexpr (RECOMP) asm volatile("" : "+v"(ln), "+s"(wl), "+s"(rb));
 #pragma unroll
     for (int n = 0; n < LPW; ++n) {
       const int r0 = (wl * LPW + n) * RPI;  // first row of this load, wave-uniform
@@ -362,10 +365,8 @@ __global__ void __launch_bounds__(NW * 64, 1) prefill_kernel(PrefillArgs a) {
   // ---- scores S^T = K~ Q~^T of one tile (fragments stream in groups of FG, one group ahead) ----
   auto scores = [&](auto stage, f32x16 (&sacc)[MB]) {
     unsigned char* sp = stp(stage);
-    // Lane parts of the fragment offsets, recomputed per tile from a laundered
-    // lane id (cheap) so they do not occupy registers across the loop.
     int ln = lane;
-    asm volatile("" : "+v"(ln));
+    if constexpr (RECOMP) asm volatile("" : "+v"(ln));
     const int l32 = ln & 31, hl = ln >> 5;
     // score operand (key l32, chunk c = 2s + hl): chunk position
     // c ^ swz(l32) = 16*(s/8) + ((2*(s%8) + hl) ^ swz(l32))
@@ -450,7 +451,7 @@ __global__ void __launch_bounds__(NW * 64, 1) prefill_kernel(PrefillArgs a) {
   auto values = [&](auto stage, const u32x4 (&pf)[MB][2]) {
     unsigned char* sp = stp(stage);
     int ln = lane;
-    asm volatile("" : "+v"(ln));
+    if constexpr (RECOMP) asm volatile("" : "+v"(ln));
     // value operand by transpose reads: lane (g = ln/16, i = ln%16) reads row
     // 4*(g/2) + i/4 (then +8 rows for the upper 4 keys, +16*k2) at dims
     // 32*db + 16*(g%2) + 4*(i%4), i.e. chunk 4*db + tr_x, byte 8*(i%2)
