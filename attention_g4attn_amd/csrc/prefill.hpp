@@ -61,6 +61,13 @@ __device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
+// max of x over lanes l and l ^ 32, in registers (v_permlane32_swap exchanges
+// the upper half of one operand with the lower half of the other)
+__device__ __forceinline__ float max_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 __device__ __forceinline__ u32x2 lds_read_tr16(const unsigned char* p) {
   const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
   return __builtin_bit_cast(u32x2, v);
@@ -223,7 +230,11 @@ __device__ __noinline__ void exact_row(const uint16_t* qp, const uint16_t* kp, c
 // s < SW/16 read the slab, the others the raw key tile.
 // NST = LDS ring depth (2 or 3): each tile is computed whole (scores,
 // softmax, value product) while the next one or two tiles load.
-template <int D, int G, bool KVS, bool OBF, int SW, int NST, int MB>
+// SPREAD: the loads of tile kt+2 are issued one at a time inside the score
+// products of tile kt instead of all at once before them.  Every wave must then
+// compute every tile that holds a visible key for any wave of the workgroup,
+// which holds without a window when a workgroup's tokens fit in one tile.
+template <int D, int G, bool KVS, bool OBF, int SW, int NST, int MB, bool SPREAD>
 __global__ void __launch_bounds__(NW * 64, 1) prefill_kernel(PrefillArgs a) {
   constexpr int RW = 32 * MB;          // rows per wave
   constexpr int M = NW * RW;           // rows per workgroup
@@ -236,6 +247,7 @@ __global__ void __launch_bounds__(NW * 64, 1) prefill_kernel(PrefillArgs a) {
   static_assert(SW >= 128 && SW <= D && NDS % 8 == 0 && NSS % 8 == 0, "tile shape");
   static_assert(L::STAGE % (1024 * NW) == 0, "stage = whole direct loads per wave");
   static_assert(NST == 2 || NST == 3, "ring");
+  static_assert(!SPREAD || (NST == 3 && TQ <= BN), "spread loads need the 3-deep ring and TQ <= BN");
   // With two query blocks per wave the score and output accumulators leave
   // few registers: the lane parts of LDS offsets are then recomputed per tile
   // from an opaque copy of the lane id instead of staying live across the
@@ -307,37 +319,59 @@ __global__ void __launch_bounds__(NW * 64, 1) prefill_kernel(PrefillArgs a) {
   const uint16_t* kbase = static_cast<const uint16_t*>(a.k) + ((size_t)b * S * a.Hkv + hkv) * D;
   const uint16_t* vbase = static_cast<const uint16_t*>(a.v) + ((size_t)b * S * a.Hkv + hkv) * D;
   const uint16_t* sbase_g = static_cast<const uint16_t*>(a.ws) + ((size_t)b * S * a.Hkv + hkv) * SW;
-  // one tensor's tile: rows of RB bytes in HBM (stride rbytes), placed at dst
-  // with 16-byte chunks swizzled by row
-  auto load_tensor = [&](auto rbc, const uint16_t* base, uint32_t rbytes, int rows,
-                         unsigned char* dst) {
-    constexpr int RB = decltype(rbc)::value;  // bytes per row in LDS
-    constexpr int CPR = RB / 16;              // chunks per row
-    constexpr int RPI = 1024 / RB;            // rows per direct load
-    constexpr int LPW = BN / RPI / NW;        // direct loads per wave
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(base, rows * rbytes - (rbytes - RB));
-    int ln = lane;
-    int wl = __builtin_amdgcn_readfirstlane(w);
-    uint32_t rb = __builtin_amdgcn_readfirstlane(rbytes);
-    if constexpr (RECOMP) asm volatile("" : "+v"(ln), "+s"(wl), "+s"(rb));
-#pragma unroll
-    for (int n = 0; n < LPW; ++n) {
-      const int r0 = (wl * LPW + n) * RPI;  // first row of this load, wave-uniform
-      const int r = r0 + ln / CPR;
-      const uint32_t voff = (uint32_t)r * rb + ((uint32_t)((ln % CPR) ^ swz(r)) << 4);
-      lds_dma16(rs, voff, 0, dst + r0 * RB);
-    }
+  // The loads of one tile: buffer resources over its rows (scalar, made once
+  // per tile), then one 16-byte-per-lane direct load per call, so that the
+  // loads can be spread over the tile's score products instead of queueing
+  // behind each other at the address unit all at once.
+  struct TileSrc {
+    __amdgpu_buffer_rsrc_t s, k, v;
   };
-  auto issue_loads = [&](int kt, auto stage) {
-    unsigned char* sp = stp(stage);
+  auto tile_src = [&](int kt) {
     // padding tiles past the sequence reload its last tile: finite data whose
     // keys are all masked for this workgroup's rows
     const int kv0 = min(kt * BN, ((S - 1) / BN) * BN);
     const int rows = min(S - kv0, BN);  // >= 1
     const size_t toff = (size_t)kv0 * a.Hkv;
-    load_tensor(IC<2 * SW>{}, sbase_g + toff * SW, srow_bytes, rows, sp);
-    if constexpr (KVS || SW < D) load_tensor(IC<2 * D>{}, kbase + toff * D, row_bytes, rows, sp + L::KOFF);
-    if constexpr (!KVS) load_tensor(IC<2 * D>{}, vbase + toff * D, row_bytes, rows, sp + L::VOFF);
+    TileSrc t;
+    t.s = make_rsrc(sbase_g + toff * SW, rows * srow_bytes - (srow_bytes - 2 * SW));
+    t.k = make_rsrc(kbase + toff * D, rows * row_bytes - (row_bytes - 2 * D));
+    t.v = make_rsrc(vbase + toff * D, rows * row_bytes - (row_bytes - 2 * D));
+    return t;
+  };
+  // direct load n of this wave for one tensor: rows of RB bytes in HBM
+  // (stride rbytes), placed at dst with 16-byte chunks swizzled by row
+  auto load_part = [&](auto rbc, const __amdgpu_buffer_rsrc_t& rs, uint32_t rbytes, int n,
+                       unsigned char* dst) {
+    constexpr int RB = decltype(rbc)::value;  // bytes per row in LDS
+    constexpr int CPR = RB / 16;              // chunks per row
+    constexpr int RPI = 1024 / RB;            // rows per direct load
+    constexpr int LPW = BN / RPI / NW;        // direct loads per wave
+    int ln = lane;
+    int wl = w;
+    uint32_t rb = __builtin_amdgcn_readfirstlane(rbytes);
+    if constexpr (RECOMP) asm volatile("" : "+v"(ln), "+s"(wl), "+s"(rb));
+    const int r0 = (wl * LPW + n) * RPI;  // first row of this load, wave-uniform
+    const int r = r0 + ln / CPR;
+    const uint32_t voff = (uint32_t)r * rb + ((uint32_t)((ln % CPR) ^ swz(r)) << 4);
+    lds_dma16(rs, voff, 0, dst + r0 * RB);
+  };
+  // loads per wave per tile: slab, raw keys (when the slab does not hold
+  // every key dimension, or keys are values), raw values (separate caches)
+  constexpr int NL_S = BN / (1024 / (2 * SW)) / NW;
+  constexpr int NL_K = (KVS || SW < D) ? BN / (1024 / (2 * D)) / NW : 0;
+  constexpr int NL_V = !KVS ? BN / (1024 / (2 * D)) / NW : 0;
+  static_assert(NL_S + NL_K + NL_V == L::NLD, "loads per wave");
+  // load j (0 <= j < L::NLD) of a tile; j is a constant after unrolling
+  auto load_one = [&](const TileSrc& t, auto stage, int j) {
+    unsigned char* sp = stp(stage);
+    if (j < NL_S) load_part(IC<2 * SW>{}, t.s, srow_bytes, j, sp);
+    else if (j < NL_S + NL_K) load_part(IC<2 * D>{}, t.k, row_bytes, j - NL_S, sp + L::KOFF);
+    else load_part(IC<2 * D>{}, t.v, row_bytes, j - NL_S - NL_K, sp + L::VOFF);
+  };
+  auto issue_loads = [&](int kt, auto stage) {
+    const TileSrc t = tile_src(kt);
+#pragma unroll
+    for (int j = 0; j < L::NLD; ++j) load_one(t, stage, j);
   };
 
   f32x16 oacc[MB][NDB];
@@ -363,7 +397,7 @@ __global__ void __launch_bounds__(NW * 64, 1) prefill_kernel(PrefillArgs a) {
   const float cs = a.scale_log2e;
 
   // ---- scores S^T = K~ Q~^T of one tile (fragments stream in groups of FG, one group ahead) ----
-  auto scores = [&](auto stage, f32x16 (&sacc)[MB]) {
+  auto scores = [&](auto stage, f32x16 (&sacc)[MB], auto&& side) {
     unsigned char* sp = stp(stage);
     int ln = lane;
     if constexpr (RECOMP) asm volatile("" : "+v"(ln));
@@ -398,8 +432,11 @@ __global__ void __launch_bounds__(NW * 64, 1) prefill_kernel(PrefillArgs a) {
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
           sacc[mb] = mfma32x32x16(kf[g & 1][i], qf[mb][FG * g + i], sacc[mb]);
+      if (g < L::NLD) side(g);
       __builtin_amdgcn_sched_barrier(0);
     }
+#pragma unroll
+    for (int j = NG; j < L::NLD; ++j) side(j);
   };
 
   // ---- causal / band mask of tile kt (edge tiles only) ----
@@ -423,10 +460,12 @@ __global__ void __launch_bounds__(NW * 64, 1) prefill_kernel(PrefillArgs a) {
   auto softmax = [&](const f32x16 (&sacc)[MB], u32x4 (&pf)[MB][2]) {
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
-      float mx = sacc[mb][0];
-#pragma unroll
-      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sacc[mb][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      // balanced tree over the lane's 16 scores, then the other half-wave
+      const f32x16& v = sacc[mb];
+      const float a0 = fmaxf(fmaxf(v[0], v[1]), v[2]), a1 = fmaxf(fmaxf(v[3], v[4]), v[5]);
+      const float a2 = fmaxf(fmaxf(v[6], v[7]), v[8]), a3 = fmaxf(fmaxf(v[9], v[10]), v[11]);
+      const float a4 = fmaxf(fmaxf(v[12], v[13]), v[14]);
+      const float mx = max_xor32(fmaxf(fmaxf(fmaxf(a0, a1), a2), fmaxf(fmaxf(a3, a4), v[15])));
       const float m_tile = mx * cs;  // -inf when the row sees no key here
       m_seen[mb] = fmaxf(m_seen[mb], m_tile);
       m_ref[mb] = m_ref[mb] == UNSET ? fmaxf(m_tile, UNSET) : m_ref[mb];
@@ -448,7 +487,9 @@ __global__ void __launch_bounds__(NW * 64, 1) prefill_kernel(PrefillArgs a) {
   };
 
   // ---- O^T += V^T P^T, V^T fragments by transpose reads of the raw value tile ----
-  auto values = [&](auto stage, const u32x4 (&pf)[MB][2]) {
+  // make_p(pf) produces P^T; it runs after the first value reads are issued,
+  // so their LDS latency passes under the softmax
+  auto values = [&](auto stage, auto&& make_p) {
     unsigned char* sp = stp(stage);
     int ln = lane;
     if constexpr (RECOMP) asm volatile("" : "+v"(ln));
@@ -476,6 +517,10 @@ __global__ void __launch_bounds__(NW * 64, 1) prefill_kernel(PrefillArgs a) {
     u32x4 vf[2][FG];
 #pragma unroll
     for (int i = 0; i < FG; ++i) vf[0][i] = vfrag(i >> 1, i & 1);
+    __builtin_amdgcn_sched_barrier(0);
+    u32x4 pf[MB][2];
+    make_p(pf);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
       if (g + 1 < NG) {
@@ -497,20 +542,17 @@ __global__ void __launch_bounds__(NW * 64, 1) prefill_kernel(PrefillArgs a) {
   };
 
   // one whole tile
-  auto compute = [&](int kt, auto stage) {
+  auto compute = [&](int kt, auto stage, auto&& side) {
     f32x16 sacc[MB];
-    u32x4 pf[MB][2];
-    scores(stage, sacc);
+    scores(stage, sacc, side);
     mask(kt, sacc);
-    softmax(sacc, pf);
-    __builtin_amdgcn_sched_barrier(0);
-    values(stage, pf);
+    values(stage, [&](u32x4 (&pf)[MB][2]) { softmax(sacc, pf); });
   };
   // a wave skips tiles where none of its rows sees a key (past its last
   // token, before its window, or padding)
   auto visible = [&](int kt) {
     const int kv0 = kt * BN;
-    return wave_ok && kv0 <= tw1 && !(W > 0 && kv0 + BN - 1 <= tw0 - W);
+    return (SPREAD || wave_ok) && kv0 <= tw1 && !(W > 0 && kv0 + BN - 1 <= tw0 - W);
   };
 
   // ---- KV loop, unrolled by the ring depth so every stage is a fixed object ----
@@ -527,8 +569,17 @@ __global__ void __launch_bounds__(NW * 64, 1) prefill_kernel(PrefillArgs a) {
     auto step = [&](int kt, auto s) {
       constexpr int S0 = decltype(s)::value;
       const bool more = kt + 2 <= ktp;
-      if (more) issue_loads(kt + 2, IC<(S0 + 2) % 3>{});
-      if (visible(kt)) compute(kt, s);
+      if constexpr (SPREAD) {
+        // Without a window and with TQ <= BN, a tile is invisible to a wave
+        // only past the last token, where no further tile is needed; the
+        // loads past the end repeat the last tile (clamped) into the free
+        // stage and are drained by the final wait.
+        const TileSrc t = tile_src(kt + 2);
+        if (visible(kt)) compute(kt, s, [&](int j) { load_one(t, IC<(S0 + 2) % 3>{}, j); });
+      } else {
+        if (more) issue_loads(kt + 2, IC<(S0 + 2) % 3>{});
+        if (visible(kt)) compute(kt, s, [](int) {});
+      }
       if (more) wait_vmcnt<L::NLD>();
       else wait_vmcnt<0>();
       __syncthreads();
@@ -545,7 +596,7 @@ __global__ void __launch_bounds__(NW * 64, 1) prefill_kernel(PrefillArgs a) {
     auto step = [&](int kt, auto s) {
       constexpr int S0 = decltype(s)::value;
       if (kt + 1 <= ktp) issue_loads(kt + 1, IC<1 - S0>{});
-      if (visible(kt)) compute(kt, s);
+      if (visible(kt)) compute(kt, s, [](int) {});
       wait_vmcnt<0>();
       __syncthreads();
     };
@@ -601,7 +652,7 @@ __global__ void __launch_bounds__(NW * 64, 1) prefill_kernel(PrefillArgs a) {
 }
 
 // Rotated key slab for slab width SW, then the attention kernel, on stream st.
-template <int D, int G, bool KVS, bool OBF, int SW, int NST, int MB>
+template <int D, int G, bool KVS, bool OBF, int SW, int NST, int MB, bool SPREAD = false>
 hipError_t launch(const PrefillArgs& a, hipStream_t st) {
   constexpr int TQ = NW * 32 * MB / G;
   PrefillArgs x = a;
@@ -616,7 +667,8 @@ hipError_t launch(const PrefillArgs& a, hipStream_t st) {
                      dim3(256), 0, st, static_cast<const uint16_t*>(a.k),
                      static_cast<uint16_t*>(a.ws), a.pos, nchunks, a.Hkv, D, a.n_rot,
                      a.log2_theta);
-  hipLaunchKernelGGL((prefill_kernel<D, G, KVS, OBF, SW, NST, MB>), dim3((unsigned)nblk),
+  if (SPREAD && a.window != 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((prefill_kernel<D, G, KVS, OBF, SW, NST, MB, SPREAD>), dim3((unsigned)nblk),
                      dim3(NW * 64), 0, st, x);
   return hipGetLastError();
 }

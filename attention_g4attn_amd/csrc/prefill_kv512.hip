@@ -7,6 +7,10 @@ namespace g4a {
 
 template <int G, bool OBF>
 static hipError_t kv512(const PrefillArgs& a, hipStream_t st) {
+  // without a window, 4 or 8 query heads per KV head put a workgroup's tokens
+  // in one key tile, and the tile loads can be spread over the products
+  if constexpr (G >= 4)
+    if (a.n_rot <= 64 && a.window == 0) return pf::launch<512, G, true, OBF, 128, 3, 1, true>(a, st);
   if (a.n_rot <= 64) return pf::launch<512, G, true, OBF, 128, 3, 1>(a, st);
   return pf::launch<512, G, true, OBF, 512, 2, 1>(a, st);
 }

@@ -56,6 +56,8 @@ SMALL = [
     inputs.Layer("local", 1, 100, 4, 4, 256, 0, 1e4, 0.25),
     inputs.Layer("local", 1, 170, 4, 2, 512, 70, 1e4, 0.5),   # separate K/V, d=512, 128 pairs turn
     inputs.Layer("global", 1, 140, 8, 1, 512, 0, 1e6, 1.0),   # K=V, every pair turns
+    inputs.Layer("global", 1, 203, 8, 2, 512, 0, 1e6, 0.25),  # G=4: 32 tokens per workgroup
+    inputs.Layer("global", 1, 211, 8, 1, 512, 96, 1e6, 0.25),  # window on the K=V path
 ]
 
 
