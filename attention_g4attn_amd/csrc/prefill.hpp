@@ -457,9 +457,13 @@ __global__ void __launch_bounds__(NW * 64, 1) prefill_kernel(PrefillArgs a) {
   };
 
   // ---- softmax of masked scores -> P^T as B operands of the value product ----
-  auto softmax = [&](const f32x16 (&sacc)[MB], u32x4 (&pf)[MB][2]) {
+  // half k2 computes P for keys 16*k2 .. 16*k2+15 of the tile (the row max
+  // and the reference with the first half)
+  auto softmax = [&](const f32x16 (&sacc)[MB], u32x4 (&pf)[MB][2], auto k2c) {
+    constexpr int K2 = decltype(k2c)::value;
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
+      if constexpr (K2 == 0) {
       // balanced tree over the lane's 16 scores, then the other half-wave
       const f32x16& v = sacc[mb];
       const float a0 = fmaxf(fmaxf(v[0], v[1]), v[2]), a1 = fmaxf(fmaxf(v[3], v[4]), v[5]);
@@ -470,25 +474,26 @@ __global__ void __launch_bounds__(NW * 64, 1) prefill_kernel(PrefillArgs a) {
       m_seen[mb] = fmaxf(m_seen[mb], m_tile);
       m_ref[mb] = m_ref[mb] == UNSET ? fmaxf(m_tile, UNSET) : m_ref[mb];
       ovf |= (m_tile > m_ref[mb] + 64.f) << mb;
+      }
       const float mr = m_ref[mb] == UNSET ? 0.f : m_ref[mb];
       float lsum = 0.f;
 #pragma unroll
-      for (int k2 = 0; k2 < 2; ++k2)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[mb][8 * k2 + 2 * i], cs, -mr));
-          const float p1 =
-              __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[mb][8 * k2 + 2 * i + 1], cs, -mr));
-          lsum += p0 + p1;
-          pf[mb][k2][i] = pack_bf16(p0, p1);
-        }
+      for (int i = 0; i < 4; ++i) {
+        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[mb][8 * K2 + 2 * i], cs, -mr));
+        const float p1 =
+            __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[mb][8 * K2 + 2 * i + 1], cs, -mr));
+        lsum += p0 + p1;
+        pf[mb][K2][i] = pack_bf16(p0, p1);
+      }
       l_run[mb] += lsum;
     }
   };
 
   // ---- O^T += V^T P^T, V^T fragments by transpose reads of the raw value tile ----
-  // make_p(pf) produces P^T; it runs after the first value reads are issued,
-  // so their LDS latency passes under the softmax
+  // make_p(pf, IC<k2>) produces P^T for keys 16*k2 .. +15.  The products go
+  // key half by key half (fragment f: keys 16*(f/NDB).., dims 32*(f%NDB)..):
+  // the first half of P is made after the first value reads are issued, the
+  // second half under the first group's products.
   auto values = [&](auto stage, auto&& make_p) {
     unsigned char* sp = stp(stage);
     int ln = lane;
@@ -514,12 +519,13 @@ __global__ void __launch_bounds__(NW * 64, 1) prefill_kernel(PrefillArgs a) {
       return u32x4{lo[0], lo[1], hi[0], hi[1]};
     };
     constexpr int NG = 2 * NDB / FG;
+    static_assert(NDB % FG == 0, "a group stays within one key half");
     u32x4 vf[2][FG];
 #pragma unroll
-    for (int i = 0; i < FG; ++i) vf[0][i] = vfrag(i >> 1, i & 1);
+    for (int i = 0; i < FG; ++i) vf[0][i] = vfrag(i % NDB, i / NDB);
     __builtin_amdgcn_sched_barrier(0);
     u32x4 pf[MB][2];
-    make_p(pf);
+    make_p(pf, IC<0>{});
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
@@ -527,7 +533,7 @@ __global__ void __launch_bounds__(NW * 64, 1) prefill_kernel(PrefillArgs a) {
 #pragma unroll
         for (int i = 0; i < FG; ++i) {
           const int f = FG * (g + 1) + i;
-          vf[(g + 1) & 1][i] = vfrag(f >> 1, f & 1);
+          vf[(g + 1) & 1][i] = vfrag(f % NDB, f / NDB);
         }
       }
 #pragma unroll
@@ -535,8 +541,9 @@ __global__ void __launch_bounds__(NW * 64, 1) prefill_kernel(PrefillArgs a) {
         const int f = FG * g + i;
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
-          oacc[mb][f >> 1] = mfma32x32x16(vf[g & 1][i], pf[mb][f & 1], oacc[mb][f >> 1]);
+          oacc[mb][f % NDB] = mfma32x32x16(vf[g & 1][i], pf[mb][f / NDB], oacc[mb][f % NDB]);
       }
+      if (g == 0) make_p(pf, IC<1>{});
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -546,7 +553,7 @@ __global__ void __launch_bounds__(NW * 64, 1) prefill_kernel(PrefillArgs a) {
     f32x16 sacc[MB];
     scores(stage, sacc, side);
     mask(kt, sacc);
-    values(stage, [&](u32x4 (&pf)[MB][2]) { softmax(sacc, pf); });
+    values(stage, [&](u32x4 (&pf)[MB][2], auto k2c) { softmax(sacc, pf, k2c); });
   };
   // a wave skips tiles where none of its rows sees a key (past its last
   // token, before its window, or padding)
