@@ -112,6 +112,7 @@ decode_split_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char tv2[KREG ? NW * KB : 16];  // second V slot per wave
   __shared__ double gtab[D / 2];
   __shared__ float mls[NW][16][2];
+  __shared__ int tnext;  // next unclaimed tile of the chunk (NW > 1)
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -135,10 +136,12 @@ decode_split_kernel(DecodeArgs a) {
   const int r0 = ch * a.chunk;
   if (r0 > last) return;
   const int r1 = min(r0 + a.chunk, last + 1);  // exclusive
-  // this wave's rows: a TR-aligned share of the chunk (possibly empty)
-  const int per = (a.chunk / NW + TR - 1) / TR * TR;
-  const int wr0 = min(r0 + w * per, r1), wr1 = min(wr0 + per, r1);
-  const int ntiles = (wr1 - wr0 + TR - 1) / TR;
+  // Tile t of the chunk holds rows r0 + TR*t .. (clipped at r1).  With several
+  // waves, wave w starts on tile w (and, where keys run two tiles ahead, on
+  // w + NW) and claims every further tile from a workgroup counter, so waves
+  // that stream faster take more tiles and all finish together.  A wave's
+  // tiles increase, so its loads are issued in tile order.
+  const int nt = (r1 - r0 + TR - 1) / TR;
   const int n_rot = a.n_rot;
   unsigned char* kt = tk + (KREG ? 0 : w * KB);
   unsigned char* vt0 = tv + (KVS ? 0 : w * KB);
@@ -158,10 +161,10 @@ decode_split_kernel(DecodeArgs a) {
   const uint16_t* kbase = static_cast<const uint16_t*>(a.k) + hoff;
   const uint16_t* vbase = static_cast<const uint16_t*>(a.v) + hoff;
 
-  // 16 rows of tile i of one tensor into an LDS tile; rows past wr1 read as zeros
+  // 16 rows of tile i of one tensor into an LDS tile; rows past r1 read as zeros
   auto issue = [&](const uint16_t* base, int i, unsigned char* dst) {
-    const int rr0 = wr0 + i * TR;
-    const uint32_t bytes = (uint32_t)min(TR, wr1 - rr0) * (2 * D);
+    const int rr0 = r0 + i * TR;
+    const uint32_t bytes = (uint32_t)min(TR, r1 - rr0) * (2 * D);
     const __amdgpu_buffer_rsrc_t rs = make_rsrc(base + (size_t)rr0 * D, bytes);
     constexpr int CPR = D / 8;       // chunks per row
     constexpr int RPI = 64 / CPR;    // rows per direct load
@@ -179,12 +182,22 @@ decode_split_kernel(DecodeArgs a) {
   // before the first tile is requested; a single wave reads its own LDS
   // writes in order and needs no barrier, so its query and tile loads overlap.
   for (int t = threadIdx.x; t < D / 2; t += 64 * NW) gtab[t] = rope_rev_per_pos(t, D, a.log2_theta);
-  if constexpr (NW > 1) __syncthreads();
+  if constexpr (NW > 1) {
+    if (threadIdx.x == 0) tnext = (KREG ? 2 : 1) * NW;
+    __syncthreads();
+  }
+  // next tile for this wave (wave-uniform; only used with several waves)
+  auto claim = [&]() -> int {
+    int t = 0;
+    if (lane == 0) t = atomicAdd(&tnext, 1);
+    return __builtin_amdgcn_readfirstlane(t);
+  };
+  const int tA = NW > 1 ? w : 0, tB = NW > 1 ? w + NW : 1;  // first two tiles of this wave
   // keys of tile i into registers, lane (row = l % 16, gq = l / 16) holding
-  // dims 32*s + 8*gq .. +7 of its row for every k-step s; rows past wr1 read as zeros
+  // dims 32*s + 8*gq .. +7 of its row for every k-step s; rows past r1 read as zeros
   auto load_keys = [&](int i, u32x4 (&kr)[NS]) {
-    const int rr0 = wr0 + i * TR;
-    const uint32_t bytes = (uint32_t)min(TR, wr1 - rr0) * (2 * D);
+    const int rr0 = r0 + i * TR;
+    const uint32_t bytes = (uint32_t)min(TR, r1 - rr0) * (2 * D);
     const __amdgpu_buffer_rsrc_t rs = make_rsrc(kbase + (size_t)rr0 * D, bytes);
     int ln = lane;
     asm volatile("" : "+v"(ln));
@@ -194,12 +207,12 @@ decode_split_kernel(DecodeArgs a) {
       kr[s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, base + 64 * s, 0, 0));
   };
   u32x4 kr0[KREG ? NS : 1], kr1[KREG ? NS : 1], kr2[KREG ? NS : 1];
-  if (ntiles > 0) {
-    if constexpr (KREG) load_keys(0, kr0);
-    else issue(kbase, 0, kt);
-    if constexpr (!KVS) issue(vbase, 0, vt0);
+  if (tA < nt) {
+    if constexpr (KREG) load_keys(tA, kr0);
+    else issue(kbase, tA, kt);
+    if constexpr (!KVS) issue(vbase, tA, vt0);
     if constexpr (KREG)
-      if (ntiles > 1) load_keys(1, kr1);
+      if (tB < nt) load_keys(tB, kr1);
   }
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
@@ -216,11 +229,11 @@ decode_split_kernel(DecodeArgs a) {
   // scores of tile i from the key tile (or, kr non-null, from key registers):
   // S^T register j = key 4*gq + j of column l16
   auto scores = [&](int i, const u32x4* kr) -> f32x4 {
-    const int rr0 = wr0 + i * TR;
+    const int rr0 = r0 + i * TR;
     int ln = lane;
     asm volatile("" : "+v"(ln));
     const int row = ln & 15, gq = ln >> 4;
-    const int r = min(rr0 + row, wr1 - 1);  // rows past the tile end are masked
+    const int r = min(rr0 + row, r1 - 1);  // rows past the tile end are masked
     const int tpos = W > 0 ? P - (P - r) % W : r;
     // chunk c = 4*s + gq of row `row` is stored at 16*(s/4) + ((4*(s%4) + gq) ^ dswz(row))
     const int dsw = dswz(row);
@@ -239,7 +252,7 @@ decode_split_kernel(DecodeArgs a) {
   };
   // softmax update of the columns; returns P^T as the B operand of the value product
   auto softmax = [&](int i, f32x4 sacc) -> u32x2 {
-    const int nrows = min(TR, wr1 - (wr0 + i * TR));
+    const int nrows = min(TR, r1 - (r0 + i * TR));
     float mx = -INFINITY;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -289,43 +302,61 @@ decode_split_kernel(DecodeArgs a) {
   if constexpr (KVS) {
     // one tile slot: the previous tile's LDS reads have completed (its
     // products consumed them) before the next tile's loads are requested
-    for (int i = 0; i < ntiles; ++i) {
-      if (i > 0) issue(kbase, i, kt);
+    for (int t = tA; t < nt;) {
+      const int tn = claim();
       wait_vmcnt<0>();
-      const u32x2 pf = softmax(i, scores(i, nullptr));
+      const u32x2 pf = softmax(t, scores(t, nullptr));
       values(kt, pf);
+      if (tn < nt) issue(kbase, tn, kt);
+      t = tn;
     }
   } else if constexpr (KREG) {
-    // step i requests the values of tile i+1, then the keys of tile i+2, and
-    // computes tile i.  Issue order is V_i, K_(i+1), V_(i+1), K_(i+2), so
-    // waiting until only the last three groups are in flight means keys and
-    // values of tile i have landed.  Key sets rotate over 3 registers blocks
-    // and value slots over 2, so the loop is unrolled by 6.
-    auto step = [&](int i, u32x4 (&kc)[NS], u32x4 (&kn2)[NS], unsigned char* vc,
-                    unsigned char* vn) {
-      if (i + 1 < ntiles) issue(vbase, i + 1, vn);
-      if (i + 2 < ntiles) load_keys(i + 2, kn2);
-      if (i + 2 < ntiles) wait_vmcnt<2 * NS + NLD>();
-      else if (i + 1 < ntiles) wait_vmcnt<NS + NLD>();
+    // The wave's tiles are c, n1, n2, ... in increasing order.  A step
+    // requests the values of n1, then the keys of n2, and computes c.  Issue
+    // order is V_c, K_n1, V_n1, K_n2, so waiting until only the last three
+    // groups are in flight means keys and values of c have landed.  Key sets
+    // rotate over 3 register blocks and value slots over 2, so the loop is
+    // unrolled by 6; the tile after n2 is claimed when n2 is.
+    auto step = [&](int c, int n1, int n2, u32x4 (&kc)[NS], u32x4 (&kn2)[NS],
+                    unsigned char* vc, unsigned char* vn) {
+      if (n1 < nt) issue(vbase, n1, vn);
+      if (n2 < nt) load_keys(n2, kn2);
+      if (n2 < nt) wait_vmcnt<2 * NS + NLD>();
+      else if (n1 < nt) wait_vmcnt<NS + NLD>();
       else wait_vmcnt<0>();
-      const u32x2 pf = softmax(i, scores(i, kc));
+      const u32x2 pf = softmax(c, scores(c, kc));
       values(vc, pf);
     };
-    for (int i = 0; i < ntiles; i += 6) {
-      step(i, kr0, kr2, vt0, vt1);
-      if (i + 1 < ntiles) step(i + 1, kr1, kr0, vt1, vt0);
-      if (i + 2 < ntiles) step(i + 2, kr2, kr1, vt0, vt1);
-      if (i + 3 < ntiles) step(i + 3, kr0, kr2, vt1, vt0);
-      if (i + 4 < ntiles) step(i + 4, kr1, kr0, vt0, vt1);
-      if (i + 5 < ntiles) step(i + 5, kr2, kr1, vt1, vt0);
+    int t0 = tA, t1 = tB, t2;
+    for (;;) {
+      if (t0 >= nt) break;
+      t2 = claim();
+      step(t0, t1, t2, kr0, kr2, vt0, vt1);
+      if (t1 >= nt) break;
+      t0 = claim();
+      step(t1, t2, t0, kr1, kr0, vt1, vt0);
+      if (t2 >= nt) break;
+      t1 = claim();
+      step(t2, t0, t1, kr2, kr1, vt0, vt1);
+      if (t0 >= nt) break;
+      t2 = claim();
+      step(t0, t1, t2, kr0, kr2, vt1, vt0);
+      if (t1 >= nt) break;
+      t0 = claim();
+      step(t1, t2, t0, kr1, kr0, vt0, vt1);
+      if (t2 >= nt) break;
+      t1 = claim();
+      step(t2, t0, t1, kr2, kr1, vt1, vt0);
     }
   } else {
-    // keys of tile i+1 load during the softmax and value product of tile i,
-    // values of tile i+1 during the scores of tile i+1
-    for (int i = 0; i < ntiles; ++i) {
+    // one wave takes the chunk's tiles in order: keys of tile i+1 load during
+    // the softmax and value product of tile i, values of tile i+1 during the
+    // scores of tile i+1
+    static_assert(NW == 1, "single wave");
+    for (int i = 0; i < nt; ++i) {
       wait_vmcnt<NLD>();  // keys of tile i (its values may still be in flight)
       const f32x4 sacc = scores(i, nullptr);
-      const bool more = i + 1 < ntiles;
+      const bool more = i + 1 < nt;
       if (more) issue(kbase, i + 1, kt);
       const u32x2 pf = softmax(i, sacc);
       if (more) wait_vmcnt<NLD>();  // values of tile i (next keys may be in flight)
