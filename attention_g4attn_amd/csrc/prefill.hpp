@@ -61,6 +61,23 @@ __device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
+// Score products with the accumulator in VGPRs.  The compiler puts every MFMA
+// result of a kernel in AGPRs once the output accumulators need them, and the
+// 16 score registers then push an output block out of the AGPRs on every
+// tile.  Written as instructions, the score chain keeps its accumulator in
+// VGPRs, where the softmax reads it directly.  A dependent chain needs no
+// wait states between its products; a VALU read of the result needs 12 on
+// gfx950 (the compiler's own figure for this product), given by score_ready.
+__device__ __forceinline__ void score_first(f32x16& c, u32x4 a, u32x4 b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(c) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void score_next(f32x16& c, u32x4 a, u32x4 b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void score_ready(f32x16& c) {
+  asm volatile("s_nop 7\n\ts_nop 7" : "+v"(c));
+}
+
 // max of x over lanes l and l ^ 32, in registers (v_permlane32_swap exchanges
 // the upper half of one operand with the lower half of the other)
 __device__ __forceinline__ float max_xor32(float x) {
@@ -410,8 +427,6 @@ __global__ void __launch_bounds__(NW * 64, 1) prefill_kernel(PrefillArgs a) {
     for (int i = 0; i < 8; ++i) soff[i] = ((2 * i + hl) ^ sw_n) << 4;
     const int kbase_off = L::KOFF + l32 * (2 * D);
     const int sbase_off = l32 * (2 * SW);
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) sacc[mb] = f32x16{};
     // k-step s lives in the slab for s < NSS, in the raw key tile otherwise
     auto frag = [&](int s) -> u32x4 {
       if (s < NSS) return lds_at<u32x4>(sp, sbase_off + 256 * (s >> 3) + soff[s & 7]);
@@ -431,12 +446,15 @@ __global__ void __launch_bounds__(NW * 64, 1) prefill_kernel(PrefillArgs a) {
       for (int i = 0; i < FG; ++i)
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
-          sacc[mb] = mfma32x32x16(kf[g & 1][i], qf[mb][FG * g + i], sacc[mb]);
+          if (g == 0 && i == 0) score_first(sacc[mb], kf[g & 1][i], qf[mb][FG * g + i]);
+          else score_next(sacc[mb], kf[g & 1][i], qf[mb][FG * g + i]);
       if (g < L::NLD) side(g);
       __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
     for (int j = NG; j < L::NLD; ++j) side(j);
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) score_ready(sacc[mb]);
   };
 
   // ---- causal / band mask of tile kt (edge tiles only) ----
