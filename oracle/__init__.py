@@ -8,6 +8,8 @@ softmax); this module only marshals numpy arrays into it.
 Array conventions (row-major, contiguous):
   prefill  q [B,S,Hq,d], k/v [B,S,Hkv,d], pos [B,S] int32
   decode   q [B,Hq,d], k_cache/v_cache [B,Hkv,C,d], pos [B] int32
+  decode_multi q [B,L,Hq,d], caches as decode, pos [B] (last query's position)
+  fill_cache k/v [B,S,Hkv,d], pos [B,S] -> caches [B,Hkv,C,d]
 Inputs are float32, or bf16 given as their uint16 bit patterns; outputs fp64.
 """
 import ctypes
@@ -29,6 +31,10 @@ def load(path):
     lib.g4o_prefill.restype = I
     lib.g4o_decode.argtypes = [P, P, P, I, P, I, I, I, I, I, I, D, D, P]
     lib.g4o_decode.restype = I
+    lib.g4o_decode_multi.argtypes = [P, P, P, I, P, I, I, I, I, I, I, I, D, D, P]
+    lib.g4o_decode_multi.restype = I
+    lib.g4o_fill_cache.argtypes = [P, P, I, P, I, I, I, I, I, I, P, P]
+    lib.g4o_fill_cache.restype = I
     lib.g4o_probs.argtypes = [P, P, I, P, I, I, I, I, I, I, D, D, I, I, I, P]
     lib.g4o_probs.restype = I
     lib.g4o_rope.argtypes = [P, I, I, D, D]
@@ -141,3 +147,46 @@ def decode(q, k_cache, v_cache, pos, window, theta, p, lib=None):
     if rc != 0:
         raise ValueError(f"g4o_decode failed ({rc})")
     return out
+
+
+def decode_multi(q, k_cache, v_cache, pos, window, theta, p, lib=None):
+    """L query tokens per sequence (q [B,L,Hq,d]; pos [B] = last query's position)."""
+    q, dt = _in(q)
+    k_cache, dk = _in(k_cache)
+    if v_cache is not None:
+        v_cache, dv = _in(v_cache)
+        assert dv == dk and v_cache.shape == k_cache.shape
+    assert dt == dk
+    B, L, Hq, d = q.shape
+    _, Hkv, C, _ = k_cache.shape
+    pos = np.ascontiguousarray(pos, dtype=np.int32)
+    assert pos.shape == (B,)
+    out = np.empty((B, L, Hq, d), np.float64)
+    rc = _lib(lib).g4o_decode_multi(_ptr(q), _ptr(k_cache), _ptr(v_cache), dt, _ptr(pos), B, L,
+                                    Hq, Hkv, d, C, int(window), float(theta), float(p), _ptr(out))
+    if rc != 0:
+        raise ValueError(f"g4o_decode_multi failed ({rc})")
+    return out
+
+
+def fill_cache(k, v, pos, k_cache, v_cache, window, lib=None):
+    """Copies of k_cache (and v_cache) with the prefill rows k, v [B,S,Hkv,d] written in."""
+    k, dk = _in(k)
+    kc = np.array(k_cache, copy=True, order="C")
+    assert kc.dtype == k.dtype
+    vc = None
+    if v is not None:
+        v, dv = _in(v)
+        assert dv == dk and v.shape == k.shape
+        vc = np.array(v_cache, copy=True, order="C")
+        assert vc.dtype == v.dtype and vc.shape == kc.shape
+    B, S, Hkv, d = k.shape
+    _, Hkv2, C, d2 = kc.shape
+    assert (Hkv2, d2) == (Hkv, d) and kc.shape[0] == B
+    pos = np.ascontiguousarray(pos, dtype=np.int32)
+    assert pos.shape == (B, S)
+    rc = _lib(lib).g4o_fill_cache(_ptr(k), _ptr(v), k.dtype.itemsize, _ptr(pos), B, S, Hkv, d, C,
+                                  int(window), _ptr(kc), _ptr(vc))
+    if rc != 0:
+        raise ValueError(f"g4o_fill_cache failed ({rc})")
+    return kc, vc

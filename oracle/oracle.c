@@ -353,3 +353,121 @@ int g4o_decode(const void* q, const void* kc, const void* vc, int dtype, const i
   }
   return err ? G4O_ENOMEM : G4O_OK;
 }
+
+/*
+ * Cache fill: the raw k (and v) rows of a prefill, written into the decode
+ * cache layout so that decoding continues where the prefill ended (the KV
+ * cache grows with prompt and generated tokens: "Visao geral do modelo
+ * Gemma 4", section "Principais Consideracoes para o planejamento de
+ * memoria").
+ *   k, v [B, S, Hkv, d] (v NULL: K=V, only k_cache is written), esize bytes
+ *   per element; pos [B, S]; k_cache, v_cache [B, Hkv, capacity, d].
+ *   window > 0 (ring): the last min(S, capacity) tokens i of each sequence
+ *     go to slot pos[b,i] mod capacity;
+ *   window = 0 (linear): every token with 0 <= pos[b,i] < capacity goes to
+ *     row pos[b,i].
+ * Tokens with a negative position are not written.  Bytes are copied
+ * unchanged; slots not written keep their contents.
+ */
+int g4o_fill_cache(const void* k, const void* v, int esize, const int32_t* pos, int B, int S,
+                   int Hkv, int d, int capacity, int window, void* k_cache, void* v_cache) {
+  if (B < 0 || S < 0 || Hkv <= 0 || d <= 0 || capacity <= 0 || window < 0) return G4O_EINVAL;
+  if ((esize != 2 && esize != 4) || !k || !pos || !k_cache || (v && !v_cache)) return G4O_EINVAL;
+  const size_t row = (size_t)d * esize;
+  for (int b = 0; b < B; ++b) {
+    const int first = window > 0 && S > capacity ? S - capacity : 0;
+    for (int i = first; i < S; ++i) {
+      const int64_t P = pos[(size_t)b * S + i];
+      if (P < 0 || (window == 0 && P >= capacity)) continue;
+      const int64_t slot = window > 0 ? P % capacity : P;
+      for (int g = 0; g < Hkv; ++g) {
+        const size_t src = (((size_t)b * S + i) * Hkv + g) * row;
+        const size_t dst = (((size_t)b * Hkv + g) * capacity + slot) * row;
+        memcpy((char*)k_cache + dst, (const char*)k + src, row);
+        if (v) memcpy((char*)v_cache + dst, (const char*)v + src, row);
+      }
+    }
+  }
+  return G4O_OK;
+}
+
+/*
+ * Decode of L query tokens per sequence at once, the verify step of
+ * speculative decoding (every model carries a draft model for it: "Visao
+ * geral do modelo Gemma 4", section "Recursos"); L = 1 is ordinary decode.
+ *   q [B, L, Hq, d]; k_cache, v_cache [B, Hkv, capacity, d] of raw rows
+ *   (v_cache NULL: K=V); pos [B]: position P of the last query token.  Query
+ *   token j sits at Pj = P - L + 1 + j, and the keys of all L tokens are
+ *   already cached.
+ *   window > 0: ring, position t in slot t mod capacity.  The ring holds
+ *     positions P-capacity+1 .. P, so capacity >= window + L - 1 is required
+ *     for the first query to find its whole window.  Query j sees positions
+ *     max(0, Pj-window+1) .. Pj.
+ *   window = 0: linear cache, row t holds position t; query j sees 0 .. Pj.
+ * Rows of a query with Pj < 0, and every row of a sequence with P >= capacity
+ * in a linear cache, are NaN.  Row j equals row Pj of the prefill over the
+ * sequence the cache holds.
+ */
+int g4o_decode_multi(const void* q, const void* kc, const void* vc, int dtype, const int32_t* pos,
+                     int B, int L, int Hq, int Hkv, int d, int capacity, int window, double theta,
+                     double p, double* out) {
+  int rc = g4o_check(B, 1, Hq, Hkv, d, window, theta, p);
+  if (rc) return rc;
+  if (!q || !kc || !pos || !out || capacity <= 0 || L < 1 || (dtype != 0 && dtype != 1))
+    return G4O_EINVAL;
+  if (window > 0 && capacity < window + L - 1) return G4O_EINVAL;
+  if (!vc) vc = kc;
+  const int G = Hq / Hkv, n_rot = g4o_nrot(d, p);
+  const double scale = 1.0 / sqrt((double)d);
+  int err = 0;
+#pragma omp parallel
+  {
+    double* qr = (double*)malloc(sizeof(double) * d);
+    double* kr = (double*)malloc(sizeof(double) * d);
+    double* sc = (double*)malloc(sizeof(double) * (size_t)capacity);
+    if (!qr || !kr || !sc) {
+#pragma omp atomic write
+      err = 1;
+    } else {
+#pragma omp for schedule(dynamic, 1)
+      for (int64_t task = 0; task < (int64_t)B * L * Hq; ++task) {
+        const int b = (int)(task / ((int64_t)L * Hq));
+        const int j = (int)(task / Hq % L), h = (int)(task % Hq), g = h / G;
+        const int64_t P = pos[b], Pj = P - L + 1 + j;
+        double* o = out + (((size_t)b * L + j) * Hq + h) * (size_t)d;
+        if (P < 0 || Pj < 0 || (window == 0 && P >= capacity)) {
+          for (int e = 0; e < d; ++e) o[e] = NAN;
+          continue;
+        }
+        const int64_t t0 = g4o_first_key(Pj, window), nk = Pj - t0 + 1;
+        const size_t qoff = (((size_t)b * L + j) * Hq + h) * (size_t)d;
+        for (int e = 0; e < d; ++e) qr[e] = g4o_in(q, dtype, qoff + e);
+        g4o_rope(qr, d, n_rot, theta, (double)Pj);
+        for (int64_t jj = 0; jj < nk; ++jj) {
+          const int64_t t = t0 + jj;
+          const int64_t slot = window > 0 ? t % capacity : t;
+          const size_t koff = (((size_t)b * Hkv + g) * capacity + slot) * (size_t)d;
+          for (int e = 0; e < d; ++e) kr[e] = g4o_in(kc, dtype, koff + e);
+          g4o_rope(kr, d, n_rot, theta, (double)t);
+          double s = 0.0;
+          for (int e = 0; e < d; ++e) s += qr[e] * kr[e];
+          sc[jj] = s * scale;
+        }
+        double m = -INFINITY;
+        for (int64_t jj = 0; jj < nk; ++jj) if (sc[jj] > m) m = sc[jj];
+        double l = 0.0;
+        for (int64_t jj = 0; jj < nk; ++jj) { sc[jj] = exp(sc[jj] - m); l += sc[jj]; }
+        for (int e = 0; e < d; ++e) o[e] = 0.0;
+        for (int64_t jj = 0; jj < nk; ++jj) {
+          const int64_t t = t0 + jj;
+          const int64_t slot = window > 0 ? t % capacity : t;
+          const size_t voff = (((size_t)b * Hkv + g) * capacity + slot) * (size_t)d;
+          for (int e = 0; e < d; ++e) o[e] += sc[jj] * g4o_in(vc, dtype, voff + e);
+        }
+        for (int e = 0; e < d; ++e) o[e] /= l;
+      }
+    }
+    free(qr); free(kr); free(sc);
+  }
+  return err ? G4O_ENOMEM : G4O_OK;
+}

@@ -11,7 +11,9 @@
   rotation is orthogonal and additive in the position; outputs are invariant
   under a common position shift; probability rows sum to 1 with exactly the
   window's keys non-zero; decode equals the last prefill row; a ring cache
-  equals a linear one;
+  equals a linear one; writing a prefill's rows into a cache (in two parts, as
+  a prompt and then new tokens) and decoding the last L tokens at once
+  reproduces those prefill rows; one query token equals ordinary decode;
 - mutants: plausible mistakes planted in a copy of oracle.c must fail a pin.
 """
 import json
@@ -282,6 +284,95 @@ def test_decode_bad_positions_give_nan_rows():
     assert np.isnan(out[0]).all() and np.isnan(out[1]).all() and np.isfinite(out[2]).all()
 
 
+# --- cache fill + decode of several query tokens ---------------------------------
+
+def _closed_loop(B, S, L, Hq, Hkv, d, W, C, theta, p, kv_shared, seed, lib=None):
+    """prefill rows S-L..S-1 and the same rows from fill_cache + decode_multi."""
+    q, k, v = _sequence(B, S, Hq, Hkv, d, seed)
+    if kv_shared:
+        v = k
+    pos = np.arange(S, dtype=np.int32)[None].repeat(B, 0)
+    pre = oracle.prefill(q, k, v, pos, W, theta, p, lib=lib)
+    kc = np.full((B, Hkv, C, d), np.nan, np.float32)  # rows never written stay NaN
+    vc = None if kv_shared else np.full((B, Hkv, C, d), np.nan, np.float32)
+    # the prompt, then the L new tokens, as a decoding loop appends them
+    kc, vc = oracle.fill_cache(k[:, :S - L], None if kv_shared else v[:, :S - L], pos[:, :S - L],
+                               kc, vc, W, lib=lib)
+    kc, vc = oracle.fill_cache(k[:, S - L:], None if kv_shared else v[:, S - L:], pos[:, S - L:],
+                               kc, vc, W, lib=lib)
+    got = oracle.decode_multi(q[:, S - L:], kc, vc, np.full(B, S - 1, np.int32), W, theta, p,
+                              lib=lib)
+    return got, pre[:, S - L:]
+
+
+@pytest.mark.parametrize("L", [1, 3, 8])
+@pytest.mark.parametrize("kind", ["ring-min", "ring-large", "linear-kv"])
+def test_fill_cache_then_decode_several_tokens_equals_prefill_rows(L, kind):
+    if kind == "ring-min":      # local layer, capacity exactly window + L - 1
+        args = dict(B=2, S=37, Hq=4, Hkv=2, d=16, W=8, C=8 + L - 1, theta=1e4, p=1.0,
+                    kv_shared=False)
+    elif kind == "ring-large":  # a ring larger than needed
+        args = dict(B=1, S=41, Hq=2, Hkv=1, d=8, W=6, C=20, theta=1e4, p=1.0, kv_shared=False)
+    else:                       # global layer: linear K=V cache, p-RoPE
+        args = dict(B=2, S=23, Hq=8, Hkv=1, d=32, W=0, C=30, theta=1e6, p=0.25, kv_shared=True)
+    got, want = _closed_loop(L=L, seed=300 + L, **args)
+    np.testing.assert_allclose(got, want, rtol=0, atol=1e-13)
+
+
+def test_one_query_token_equals_decode():
+    B, Hq, Hkv, d, C = 3, 4, 2, 16, 12
+    q = rnd((B, 1, Hq, d), 5)
+    kc, vc = rnd((B, Hkv, C, d), 6), rnd((B, Hkv, C, d), 7)
+    for W, pos in ((C, np.array([3, 11, 40], np.int32)), (0, np.array([0, 5, 11], np.int32))):
+        a = oracle.decode_multi(q, kc, vc, pos, W, 1e4, 1.0)
+        b = oracle.decode(q[:, 0], kc, vc, pos, W, 1e4, 1.0)
+        np.testing.assert_allclose(a[:, 0], b, rtol=0, atol=1e-13)
+
+
+def test_fill_cache_ring_slots_hold_the_newest_tokens():
+    """Slot s holds the newest token whose position is s mod C (searched per
+    slot), as exact bf16 bytes; slots no token maps to keep their contents."""
+    B, S, Hkv, d, C = 2, 23, 3, 8, 7
+    k = to_bf16_bits(rnd((B, S, Hkv, d), 8))
+    pos = (np.arange(S, dtype=np.int32) + 3)[None].repeat(B, 0)
+    sentinel = np.full((B, Hkv, C, d), 0x7FC1, np.uint16)
+    kc, vc = oracle.fill_cache(k, None, pos, sentinel, None, C)
+    assert vc is None
+    for b in range(B):
+        for s_ in range(C):
+            owners = [i for i in range(S) if pos[b, i] % C == s_]
+            assert owners
+            i = max(owners, key=lambda i: pos[b, i])
+            assert np.array_equal(kc[b, :, s_], k[b, i]), (b, s_)
+    # a short prefill leaves the other slots alone
+    kc2, _ = oracle.fill_cache(k[:, :3], None, pos[:, :3], sentinel, None, C)
+    touched = {int(x) % C for x in pos[0, :3]}
+    for s_ in range(C):
+        if s_ not in touched:
+            assert (kc2[:, :, s_] == 0x7FC1).all()
+
+
+def test_fill_cache_linear_skips_positions_outside_the_cache():
+    B, S, Hkv, d, C = 1, 6, 1, 4, 5
+    k = rnd((B, S, Hkv, d), 9)
+    pos = np.array([[-2, 0, 1, 4, 5, 9]], np.int32)
+    kc, _ = oracle.fill_cache(k, None, pos, np.zeros((B, Hkv, C, d), np.float32), None, 0)
+    want = np.zeros((B, Hkv, C, d), np.float32)
+    want[0, 0, 0], want[0, 0, 1], want[0, 0, 4] = k[0, 1, 0], k[0, 2, 0], k[0, 3, 0]
+    np.testing.assert_array_equal(kc, want)
+
+
+def test_decode_several_tokens_bad_positions_and_small_ring():
+    B, L, Hq, Hkv, d, C = 3, 3, 2, 1, 8, 10
+    q = rnd((B, L, Hq, d), 10)
+    kc = rnd((B, Hkv, C, d), 11)
+    out = oracle.decode_multi(q, kc, None, np.array([1, 10, 9], np.int32), 0, 1e4, 1.0)
+    assert np.isnan(out[0, 0]).all() and np.isfinite(out[0, 1:]).all()  # query 0 at -1
+    assert np.isnan(out[1]).all() and np.isfinite(out[2]).all()        # P beyond the cache
+    with pytest.raises(ValueError):  # ring smaller than window + L - 1
+        oracle.decode_multi(q, kc, None, np.array([20, 20, 20], np.int32), 9, 1e4, 1.0)
+
+
 def test_invalid_arguments_rejected():
     q, k = rnd((1, 4, 3, 8), 1), rnd((1, 4, 2, 8), 2)
     pos = np.arange(4, dtype=np.int32)[None]
@@ -306,6 +397,11 @@ MUTANTS = {
     "key_rotated_with_table_sign": ("kr[2 * t + 1] = x0 * c[2 * t + 1] + x1 * c[2 * t];",
                                     "kr[2 * t + 1] = -x0 * c[2 * t + 1] + x1 * c[2 * t];"),
     "rotated_values": ("o[e] += w * g4o_in(v, dtype, voff + e);", "o[e] += w * kr[e];"),
+    "multi_query_position": ("Pj = P - L + 1 + j;", "Pj = P - L + j;"),
+    "multi_ring_slot_by_window": ("const int64_t slot = window > 0 ? t % capacity : t;\n          const size_t koff",
+                                  "const int64_t slot = window > 0 ? t % window : t;\n          const size_t koff"),
+    "fill_ring_slot_by_window": ("const int64_t slot = window > 0 ? P % capacity : P;",
+                                 "const int64_t slot = window > 0 ? P % window : P;"),
 }
 
 
@@ -344,4 +440,9 @@ def test_mutant_is_caught(name, mutant_dir):
     x[3] = 1.0
     y = oracle.rope(x, 1e4, 1.0, 1, lib=lib)
     caught |= not np.allclose(y[2:4], [-math.sin(0.1), math.cos(0.1)], atol=1e-12)
+    # cache fill + several query tokens: the closed loop against the prefill
+    for L, C, W, S in ((3, 10, 8, 37), (2, 12, 6, 17)):
+        got, want = _closed_loop(B=1, S=S, L=L, Hq=4, Hkv=2, d=16, W=W, C=C, theta=1e4, p=1.0,
+                                 kv_shared=False, seed=77, lib=lib)
+        caught |= not np.allclose(got, want, rtol=0, atol=1e-12, equal_nan=False)
     assert caught, f"mutant {name} survived the pins"
