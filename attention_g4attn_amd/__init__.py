@@ -139,5 +139,46 @@ def decode(q, k_cache, v_cache, pos, window, theta, p, out=None, workspace=None,
     return out
 
 
+def decode_multi_workspace_bytes(B, q_len, Hq, Hkv, d, capacity, window):
+    return _g4lib().g4attn_decode_multi_workspace_bytes(B, q_len, Hq, Hkv, d, capacity,
+                                                        int(window))
+
+
+def decode_multi(q, k_cache, v_cache, pos, window, theta, p, out=None, workspace=None,
+                 out_dtype=None):
+    """q_len query tokens per sequence at once (g4attn_decode_multi).
+
+    q is [B, q_len, Hq, d]; pos [B] is the position of the last token; a ring
+    (window > 0) needs capacity >= window + q_len - 1.
+    """
+    torch = _torch()
+    _dev(q, k_cache, v_cache, pos, out, workspace)
+    B, L, Hq, d = q.shape
+    _, Hkv, C, _ = k_cache.shape
+    out = _out((B, L, Hq, d), out, out_dtype, q.device)
+    workspace = _workspace(decode_multi_workspace_bytes(B, L, Hq, Hkv, d, C, window), workspace,
+                           q.device)
+    nbytes = _nbytes(workspace)
+    rc = _g4lib().g4attn_decode_multi(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out), _ptr(pos),
+                                    B, L, Hq, Hkv, d, C, int(window), float(theta), float(p),
+                                    _code(q), _code(out), _ptr(workspace), nbytes, _stream())
+    _check(rc, "g4attn_decode_multi")
+    return out
+
+
+def fill_cache(k, v, pos, k_cache, v_cache, window):
+    """Write prefill rows k, v [B, S, Hkv, d] into the caches (g4attn_fill_cache).
+
+    v None means K=V (only k_cache is written); window > 0 is a ring.
+    """
+    _dev(k, v, pos, k_cache, v_cache)
+    B, S, Hkv, d = k.shape
+    C = k_cache.shape[2]
+    rc = _g4lib().g4attn_fill_cache(_ptr(k), _ptr(v), _ptr(pos), B, S, Hkv, d, _ptr(k_cache),
+                                  _ptr(v_cache), C, int(window), _code(k), _stream())
+    _check(rc, "g4attn_fill_cache")
+    return k_cache, v_cache
+
+
 def strerror(status):
     return _g4lib().g4attn_strerror(int(status)).decode()

@@ -17,6 +17,9 @@ SIGNATURES = {
     "g4attn_global_prefill": ([P, P, P, P, I, I, I, I, I, I, F, F, I, I, P, Z, P], I),
     "g4attn_decode": ([P, P, P, P, P, I, I, I, I, I, I, F, F, I, I, P, Z, P], I),
     "g4attn_decode_workspace_bytes": ([I, I, I, I, I, I], Z),
+    "g4attn_decode_multi": ([P, P, P, P, P, I, I, I, I, I, I, I, F, F, I, I, P, Z, P], I),
+    "g4attn_decode_multi_workspace_bytes": ([I, I, I, I, I, I, I], Z),
+    "g4attn_fill_cache": ([P, P, P, I, I, I, I, P, P, I, I, I, P], I),
     "g4attn_strerror": ([I], ctypes.c_char_p),
     "g4attn_last_hip_error": ([], I),
 }

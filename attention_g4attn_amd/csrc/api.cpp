@@ -118,21 +118,32 @@ G4A_API int g4attn_global_prefill(const void* q, const void* kv, void* out, cons
                  workspace, workspace_bytes, stream, true);
 }
 
-G4A_API size_t g4attn_decode_workspace_bytes(int B, int Hq, int Hkv, int d, int capacity,
-                                             int window) {
-  if (B < 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || capacity <= 0 || window < 0) return 0;
-  if (window > 0 && capacity != window) return 0;
+namespace {
+
+// Ring rule: plain decode keeps capacity == window; several query tokens need
+// capacity >= window + q_len - 1 (the first token's window must still be held).
+bool ring_ok(int capacity, int window, int q_len, bool multi) {
+  if (window == 0) return true;
+  return multi ? capacity >= window + q_len - 1 : capacity == window;
+}
+
+size_t decode_ws_bytes(int B, int q_len, int Hq, int Hkv, int d, int capacity, int window,
+                       bool multi) {
+  if (B < 0 || q_len < 1 || q_len > 8 || Hq <= 0 || Hkv <= 0 || d <= 0 || capacity <= 0 ||
+      window < 0)
+    return 0;
+  if (!ring_ok(capacity, window, q_len, multi)) return 0;
   const size_t nch = (size_t)g4a::decode_num_chunks(d, capacity, window, false);
-  const size_t bytes = (size_t)B * Hq * nch * ((size_t)d + 2) * sizeof(float);
+  const size_t bytes = (size_t)B * q_len * Hq * nch * ((size_t)d + 2) * sizeof(float);
   return bytes > 0 ? bytes : 16;
 }
 
-G4A_API int g4attn_decode(const void* q, const void* k_cache, const void* v_cache, void* out,
-                          const int32_t* pos, int B, int Hq, int Hkv, int d, int capacity,
-                          int window, float theta, float p, int in_dtype, int out_dtype,
-                          void* workspace, size_t workspace_bytes, void* stream) {
-  if (B < 0 || capacity <= 0) return G4A_EINVAL;
-  if (window > 0 && capacity != window) return G4A_EINVAL;
+int decode(const void* q, const void* k_cache, const void* v_cache, void* out,
+           const int32_t* pos, int B, int q_len, int Hq, int Hkv, int d, int capacity,
+           int window, float theta, float p, int in_dtype, int out_dtype, void* workspace,
+           size_t workspace_bytes, void* stream, bool multi) {
+  if (B < 0 || capacity <= 0 || q_len < 1 || q_len > 8) return G4A_EINVAL;
+  if (!ring_ok(capacity, window, q_len, multi)) return G4A_EINVAL;
   int rc = check_common(Hq, Hkv, d, window, theta, p, in_dtype, out_dtype);
   if (rc) return rc;
   if (B == 0) return G4A_OK;
@@ -155,6 +166,8 @@ G4A_API int g4attn_decode(const void* q, const void* k_cache, const void* v_cach
   a.capacity = capacity;
   a.window = window;
   a.n_rot = rotated_pairs(d, p);
+  a.q_len = q_len;
+  a.ncb = ((Hq / Hkv) * q_len + 15) / 16;
   a.log2_theta = log2((double)theta);
   a.scale = (float)(1.0 / sqrt((double)d));
   a.scale_log2e = (float)(1.4426950408889634 / sqrt((double)d));
@@ -162,14 +175,72 @@ G4A_API int g4attn_decode(const void* q, const void* k_cache, const void* v_cach
   a.nchunk = g4a::decode_num_chunks(d, capacity, window, f32);
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (f32) return finish(g4a::launch_decode_f32(a, st));
-  const size_t need = g4attn_decode_workspace_bytes(B, Hq, Hkv, d, capacity, window);
+  const size_t need = decode_ws_bytes(B, q_len, Hq, Hkv, d, capacity, window, multi);
   if (!workspace || workspace_bytes < need) return G4A_EWORKSPACE;
   if (misaligned(workspace)) return G4A_EALIGN;
-  if ((double)B * Hkv * a.nchunk > 2.0e9) return G4A_EINVAL;
+  if ((double)B * Hkv * a.ncb * a.nchunk > 2.0e9) return G4A_EINVAL;
   a.part_o = static_cast<float*>(workspace);
-  a.part_ml = a.part_o + (size_t)B * Hq * a.nchunk * d;
+  a.part_ml = a.part_o + (size_t)B * q_len * Hq * a.nchunk * d;
   return finish(g4a::launch_decode_bf16(a, v_cache == nullptr || v_cache == k_cache,
                                         out_dtype == G4A_BF16, st));
+}
+
+}  // namespace
+
+G4A_API size_t g4attn_decode_workspace_bytes(int B, int Hq, int Hkv, int d, int capacity,
+                                             int window) {
+  return decode_ws_bytes(B, 1, Hq, Hkv, d, capacity, window, false);
+}
+
+G4A_API size_t g4attn_decode_multi_workspace_bytes(int B, int q_len, int Hq, int Hkv, int d,
+                                                   int capacity, int window) {
+  return decode_ws_bytes(B, q_len, Hq, Hkv, d, capacity, window, true);
+}
+
+G4A_API int g4attn_decode(const void* q, const void* k_cache, const void* v_cache, void* out,
+                          const int32_t* pos, int B, int Hq, int Hkv, int d, int capacity,
+                          int window, float theta, float p, int in_dtype, int out_dtype,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  return decode(q, k_cache, v_cache, out, pos, B, 1, Hq, Hkv, d, capacity, window, theta, p,
+                in_dtype, out_dtype, workspace, workspace_bytes, stream, false);
+}
+
+G4A_API int g4attn_decode_multi(const void* q, const void* k_cache, const void* v_cache,
+                                void* out, const int32_t* pos, int B, int q_len, int Hq, int Hkv,
+                                int d, int capacity, int window, float theta, float p,
+                                int in_dtype, int out_dtype, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  return decode(q, k_cache, v_cache, out, pos, B, q_len, Hq, Hkv, d, capacity, window, theta, p,
+                in_dtype, out_dtype, workspace, workspace_bytes, stream, true);
+}
+
+G4A_API int g4attn_fill_cache(const void* k, const void* v, const int32_t* pos, int B, int S,
+                              int Hkv, int d, void* k_cache, void* v_cache, int capacity,
+                              int window, int dtype, void* stream) {
+  if (B < 0 || S < 0 || Hkv <= 0 || d <= 0 || capacity <= 0 || window < 0) return G4A_EINVAL;
+  if (dtype != G4A_F32 && dtype != G4A_BF16) return G4A_EUNSUPPORTED;
+  const int esize = dtype == G4A_F32 ? 4 : 2;
+  if (((long long)d * esize) % 16) return G4A_EUNSUPPORTED;
+  if (B == 0 || S == 0) return G4A_OK;
+  if (!k || !pos || !k_cache || (v && !v_cache)) return G4A_EINVAL;
+  if (misaligned(k) || (v && misaligned(v)) || misaligned(pos) || misaligned(k_cache) ||
+      (v && misaligned(v_cache)))
+    return G4A_EALIGN;
+  g4a::FillArgs a{};
+  a.k = k;
+  a.v = v;
+  a.pos = pos;
+  a.k_cache = k_cache;
+  a.v_cache = v ? v_cache : nullptr;
+  a.B = B;
+  a.S = S;
+  a.Hkv = Hkv;
+  a.capacity = capacity;
+  a.window = window;
+  a.row_chunks = (int)((long long)d * esize / 16);
+  const int nw = window > 0 ? (S < capacity ? S : capacity) : S;
+  if ((double)B * nw * Hkv * a.row_chunks > 2.0e9) return G4A_EINVAL;
+  return finish(g4a::launch_fill_cache(a, static_cast<hipStream_t>(stream)));
 }
 
 G4A_API const char* g4attn_strerror(int status) {

@@ -28,13 +28,13 @@ struct SeqKeys {
   __device__ int kpos(int j) const { return pos[pbase + j]; }
 };
 
-// Decode keys: index j -> position t0 + j, cache slot t mod window (ring) or t.
+// Decode keys: index j -> position t0 + j, cache slot t mod capacity (ring) or t.
 struct CacheKeys {
   const float* k;
   const float* v;
   size_t base;  // ((b * Hkv) + hkv) * capacity, in rows
-  int D, window, t0;
-  __device__ int slot(int j) const { return window > 0 ? (t0 + j) % window : t0 + j; }
+  int D, window, capacity, t0;
+  __device__ int slot(int j) const { return window > 0 ? (t0 + j) % capacity : t0 + j; }
   __device__ const float* krow(int j) const { return k + (base + slot(j)) * D; }
   __device__ const float* vrow(int j) const { return v + (base + slot(j)) * D; }
   __device__ int kpos(int j) const { return t0 + j; }
@@ -156,34 +156,38 @@ __global__ void __launch_bounds__(64) prefill_f32_kernel(PrefillArgs a) {
   attend_f32<D, G>(src, i - lo + 1, qs, ps, gt, a.n_rot, a.scale, outp);
 }
 
+// One wave per (b, kv head, query token j); token j sits at P - q_len + 1 + j.
 template <int D, int G>
 __global__ void __launch_bounds__(64) decode_f32_kernel(DecodeArgs a) {
   __shared__ float qs[G][D];
   __shared__ float ps[G][64];
   __shared__ double gt[D / 2];
   const int lane = threadIdx.x;
-  const int b = blockIdx.x / a.Hkv, hkv = blockIdx.x % a.Hkv;
-  const int P = a.pos[b];
-  const size_t qrow = ((size_t)b * a.Hq + hkv * G) * D;
+  const int j = blockIdx.x % a.q_len;
+  const int bh = blockIdx.x / a.q_len;
+  const int b = bh / a.Hkv, hkv = bh % a.Hkv;
+  const int P = a.pos[b], Pj = P - a.q_len + 1 + j;
+  const size_t qrow = (((size_t)b * a.q_len + j) * a.Hq + hkv * G) * D;
   float* outp[G];
 #pragma unroll
   for (int h = 0; h < G; ++h) outp[h] = static_cast<float*>(a.out) + qrow + (size_t)h * D;
-  if (P < 0 || (a.window == 0 && P >= a.capacity)) {
+  if (P < 0 || Pj < 0 || (a.window == 0 && P >= a.capacity)) {
     for (int idx = lane; idx < G * D; idx += 64) outp[idx / D][idx % D] = __builtin_nanf("");
     return;
   }
   for (int t = lane; t < D / 2; t += 64) gt[t] = rope_rev_per_pos(t, D, a.log2_theta);
   __syncthreads();
-  load_queries<D, G>(static_cast<const float*>(a.q) + qrow, qs, gt, a.n_rot, P);
-  const int t0 = a.window > 0 ? max(0, P - a.window + 1) : 0;
+  load_queries<D, G>(static_cast<const float*>(a.q) + qrow, qs, gt, a.n_rot, Pj);
+  const int t0 = a.window > 0 ? max(0, Pj - a.window + 1) : 0;
   CacheKeys src;
   src.k = static_cast<const float*>(a.k);
   src.v = static_cast<const float*>(a.v);
   src.base = ((size_t)b * a.Hkv + hkv) * a.capacity;
   src.D = D;
   src.window = a.window;
+  src.capacity = a.capacity;
   src.t0 = t0;
-  attend_f32<D, G>(src, P - t0 + 1, qs, ps, gt, a.n_rot, a.scale, outp);
+  attend_f32<D, G>(src, Pj - t0 + 1, qs, ps, gt, a.n_rot, a.scale, outp);
 }
 
 template <int D>
@@ -203,8 +207,9 @@ hipError_t prefill_g(const PrefillArgs& a, hipStream_t st) {
 
 template <int D>
 hipError_t decode_g(const DecodeArgs& a, hipStream_t st) {
-  const long long n = (long long)a.B * a.Hkv;
+  const long long n = (long long)a.B * a.Hkv * a.q_len;
   if (n == 0) return hipSuccess;
+  if (n > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   switch (a.Hq / a.Hkv) {
     case 1: hipLaunchKernelGGL((decode_f32_kernel<D, 1>), dim3(n), dim3(64), 0, st, a); break;
     case 2: hipLaunchKernelGGL((decode_f32_kernel<D, 2>), dim3(n), dim3(64), 0, st, a); break;

@@ -118,21 +118,33 @@ decode_split_kernel(DecodeArgs a) {
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l16 = lane & 15, g4 = lane >> 4;
   const int ch = blockIdx.x % a.nchunk;
-  const int bh = blockIdx.x / a.nchunk;
+  const int rest = blockIdx.x / a.nchunk;
+  const int cb = rest % a.ncb;  // block of 16 (query token, head) columns
+  const int bh = rest / a.ncb;
   const int b = bh / a.Hkv, hkv = bh % a.Hkv;
   const int P = a.pos[b];
-  const int W = a.window, C = a.capacity;
+  const int W = a.window, C = a.capacity, QL = a.q_len;
+  // Column n of the block is (token, head) pair c = 16*cb + n: query token
+  // c / G at position P - QL + 1 + c / G, query head hkv*G + c % G.
+  const int ncol = min(16, G * QL - 16 * cb);  // columns in use
+  auto col_out = [&](int n) -> size_t {          // output row of column n
+    const int c = 16 * cb + n;
+    return (((size_t)b * QL + c / G) * a.Hq + hkv * G + c % G) * D;
+  };
+  auto col_pos = [&](int n) { return P - QL + 1 + (16 * cb + n) / G; };
+  const bool col_ok = l16 < ncol;
+  const int Pq = col_pos(col_ok ? l16 : 0);  // this lane's column position
   const bool direct = NW > 1 && a.nchunk == 1;  // this workgroup writes the output
   if (P < 0 || (W == 0 && P >= C)) {  // bad position: NaN rows (else the merge writes them)
     if (direct)
-      for (int idx = threadIdx.x; idx < G * D; idx += 64 * NW) {
-        const size_t o = ((size_t)b * a.Hq + hkv * G) * D + idx;
+      for (int idx = threadIdx.x; idx < ncol * D; idx += 64 * NW) {
+        const size_t o = col_out(idx / D) + idx % D;
         if constexpr (OBF) static_cast<uint16_t*>(a.out)[o] = 0x7fc0;
         else static_cast<float*>(a.out)[o] = __builtin_nanf("");
       }
     return;
   }
-  const int last = W > 0 ? min(P, W - 1) : P;  // highest row index that may be visible
+  const int last = W > 0 ? min(P, C - 1) : P;  // highest row index that may be visible
   const int r0 = ch * a.chunk;
   if (r0 > last) return;
   const int r1 = min(r0 + a.chunk, last + 1);  // exclusive
@@ -151,8 +163,7 @@ decode_split_kernel(DecodeArgs a) {
   // are zero); loaded first, so waiting for them leaves the tile loads below in flight
   u32x4 qf[NS];
   {
-    const int h = hkv * G + (l16 < G ? l16 : 0);
-    const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + ((size_t)b * a.Hq + h) * D;
+    const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + col_out(col_ok ? l16 : 0);
 #pragma unroll
     for (int s = 0; s < NS; ++s) qf[s] = *reinterpret_cast<const u32x4*>(qrow + 8 * (4 * s + g4));
   }
@@ -216,8 +227,8 @@ decode_split_kernel(DecodeArgs a) {
   }
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
-    qf[s] = l16 < G ? qf[s] : u32x4{0, 0, 0, 0};
-    if (s < RK) qf[s] = rotate_chunk_bf16(qf[s], 4 * s + g4, P, n_rot, gtab);
+    qf[s] = col_ok ? qf[s] : u32x4{0, 0, 0, 0};
+    if (s < RK) qf[s] = rotate_chunk_bf16(qf[s], 4 * s + g4, Pq, n_rot, gtab);
   }
 
   f32x4 oacc[NB];
@@ -234,7 +245,7 @@ decode_split_kernel(DecodeArgs a) {
     asm volatile("" : "+v"(ln));
     const int row = ln & 15, gq = ln >> 4;
     const int r = min(rr0 + row, r1 - 1);  // rows past the tile end are masked
-    const int tpos = W > 0 ? P - (P - r) % W : r;
+    const int tpos = W > 0 ? P - (P - r) % C : r;
     // chunk c = 4*s + gq of row `row` is stored at 16*(s/4) + ((4*(s%4) + gq) ^ dswz(row))
     const int dsw = dswz(row);
     int koff[4];
@@ -253,27 +264,37 @@ decode_split_kernel(DecodeArgs a) {
   // softmax update of the columns; returns P^T as the B operand of the value product
   auto softmax = [&](int i, f32x4 sacc) -> u32x2 {
     const int nrows = min(TR, r1 - (r0 + i * TR));
-    float mx = -INFINITY;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      sacc[j] = 4 * g4 + j < nrows ? sacc[j] : -INFINITY;
-      mx = fmaxf(mx, sacc[j]);
+    for (int j = 0; j < 4; ++j) sacc[j] = 4 * g4 + j < nrows ? sacc[j] : -INFINITY;
+    if (QL > 1) {  // wave-uniform: each column sees keys up to its own position
+      const int rk = r0 + i * TR + 4 * g4;   // this lane's first key row
+      const int m0 = W > 0 ? (P - rk) % C : 0;  // (P - row) mod C of that row
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int mj = m0 - j;
+        const int tp = W > 0 ? P - (mj >= 0 ? mj : mj + C) : rk + j;  // key position
+        const bool vis = tp <= Pq && (W == 0 || tp > Pq - W);
+        sacc[j] = vis ? sacc[j] : -INFINITY;
+      }
     }
+    float mx = fmaxf(fmaxf(sacc[0], sacc[1]), fmaxf(sacc[2], sacc[3]));
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     const float mt = mx * cs;
     if (__any(mt > m_run + 8.f)) {  // wave-uniform; rare after the first tile
       const float mn = fmaxf(m_run, mt);
-      const float al = __builtin_amdgcn_exp2f(m_run - mn);
+      // a column that has seen no key yet holds zeros (scaled by 0, not NaN)
+      const float al = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - mn);
 #pragma unroll
       for (int db = 0; db < NB; ++db) oacc[db] *= al;
       l_run *= al;
       m_run = mn;
     }
+    const float mr = m_run == -INFINITY ? 0.f : m_run;  // no key seen: every p is 0
     float p[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      p[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[j], cs, -m_run));
+      p[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[j], cs, -mr));
       l_run += p[j];
     }
     return u32x2{pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3])};
@@ -366,12 +387,12 @@ decode_split_kernel(DecodeArgs a) {
     }
   }
 
-  // ---- partial (m, l, O) of this chunk for the G query heads ----
+  // ---- partial (m, l, O) of this chunk for the block's columns ----
   l_run += __shfl_xor(l_run, 16);
   l_run += __shfl_xor(l_run, 32);
   if constexpr (NW == 1) {
-    if (l16 < G) {
-      const size_t prow = ((size_t)b * a.Hq + hkv * G + l16) * a.nchunk + ch;
+    if (col_ok) {
+      const size_t prow = (col_out(l16) / D) * a.nchunk + ch;
       float* po = a.part_o + prow * D + 4 * g4;
 #pragma unroll
       for (int db = 0; db < NB; ++db) *reinterpret_cast<f32x4*>(po + 16 * db) = oacc[db];
@@ -381,73 +402,85 @@ decode_split_kernel(DecodeArgs a) {
       }
     }
   } else {
-    // merge the NW waves through LDS (the tile slots are free now): wave w
-    // leaves O[w][n][dim] (G x D floats fit in its tile) and (m, l) per column
-    __syncthreads();
+    // Merge the NW waves through LDS (the tile slots are free now).  A wave's
+    // slot holds 8 columns of D floats, so the columns go in passes of 8:
+    // wave w leaves O[w][n - c0][dim] and (m, l) per column.
+    constexpr int MC = 8;
     float* ow = reinterpret_cast<float*>(KREG ? tv : tk);
-    if (l16 < G) {
-#pragma unroll
-      for (int db = 0; db < NB; ++db)
-        *reinterpret_cast<f32x4*>(ow + ((size_t)w * G + l16) * D + 16 * db + 4 * g4) = oacc[db];
-      if (g4 == 0) {
-        mls[w][l16][0] = m_run;
-        mls[w][l16][1] = l_run;
-      }
+    if (col_ok && g4 == 0) {
+      mls[w][l16][0] = m_run;
+      mls[w][l16][1] = l_run;
     }
-    __syncthreads();
-    for (int idx = threadIdx.x; idx < G * D / 4; idx += 64 * NW) {
-      const int n = idx / (D / 4), e = 4 * (idx % (D / 4));
-      float M = -INFINITY;
+    for (int c0 = 0; c0 < ncol; c0 += MC) {
+      __syncthreads();
+      if (col_ok && l16 >= c0 && l16 < c0 + MC) {
 #pragma unroll
-      for (int v = 0; v < NW; ++v) M = fmaxf(M, mls[v][n][0]);
-      f32x4 o = {};
-      float l = 0.f;
-#pragma unroll
-      for (int v = 0; v < NW; ++v) {
-        const float f = __builtin_amdgcn_exp2f(mls[v][n][0] - M);  // 0 for a wave with no rows
-        o += f * *reinterpret_cast<const f32x4*>(ow + ((size_t)v * G + n) * D + e);
-        l += f * mls[v][n][1];
+        for (int db = 0; db < NB; ++db)
+          *reinterpret_cast<f32x4*>(ow + ((size_t)w * MC + l16 - c0) * D + 16 * db + 4 * g4) =
+              oacc[db];
       }
-      if (direct) {
-        o *= 1.f / l;
-        const size_t orow = ((size_t)b * a.Hq + hkv * G + n) * D + e;
-        if constexpr (OBF) {
-          const u32x2 pk = {pack_bf16(o[0], o[1]), pack_bf16(o[2], o[3])};
-          *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.out) + orow) = pk;
-        } else {
-          *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + orow) = o;
+      __syncthreads();
+      const int nc = min(MC, ncol - c0);
+      for (int idx = threadIdx.x; idx < nc * D / 4; idx += 64 * NW) {
+        const int n = c0 + idx / (D / 4), e = 4 * (idx % (D / 4));
+        float M = -INFINITY;
+#pragma unroll
+        for (int v = 0; v < NW; ++v) M = fmaxf(M, mls[v][n][0]);
+        f32x4 o = {};
+        float l = 0.f;
+#pragma unroll
+        for (int v = 0; v < NW; ++v) {
+          // 0 for a wave that saw no key of this column (and for all, if none did)
+          const float f = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mls[v][n][0] - M);
+          o += f * *reinterpret_cast<const f32x4*>(ow + ((size_t)v * MC + n - c0) * D + e);
+          l += f * mls[v][n][1];
         }
-      } else {
-        const size_t prow = ((size_t)b * a.Hq + hkv * G + n) * a.nchunk + ch;
-        *reinterpret_cast<f32x4*>(a.part_o + prow * D + e) = o;
-        if (e == 0) {
-          a.part_ml[prow * 2 + 0] = M;
-          a.part_ml[prow * 2 + 1] = l;
+        if (direct) {
+          // every column sees its own key unless its position is negative
+          o = col_pos(n) >= 0 ? o * (1.f / l) : f32x4{__builtin_nanf(""), __builtin_nanf(""),
+                                                        __builtin_nanf(""), __builtin_nanf("")};
+          const size_t orow = col_out(n) + e;
+          if constexpr (OBF) {
+            const u32x2 pk = {pack_bf16(o[0], o[1]), pack_bf16(o[2], o[3])};
+            *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.out) + orow) = pk;
+          } else {
+            *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + orow) = o;
+          }
+        } else {
+          const size_t prow = (col_out(n) / D) * a.nchunk + ch;
+          *reinterpret_cast<f32x4*>(a.part_o + prow * D + e) = o;
+          if (e == 0) {
+            a.part_ml[prow * 2 + 0] = M;
+            a.part_ml[prow * 2 + 1] = l;
+          }
         }
       }
     }
   }
 }
 
-// Combine the chunk partials of query head (b, h): weights 2^(m_c - M).  Each
-// of the 128 threads owns 4 dims; the chunk loop keeps 4 loads in flight.
+// Combine the chunk partials of query head h of token j of sequence b:
+// weights 2^(m_c - M); a chunk with no visible key has m_c = -inf and weight 0.
+// Each of the 128 threads owns 4 dims; the chunk loop keeps 4 loads in flight.
 template <bool OBF>
 __global__ void __launch_bounds__(128) decode_merge_kernel(DecodeArgs a) {
   __shared__ float red[2][2];
-  const int b = blockIdx.x / a.Hq, h = blockIdx.x % a.Hq;
+  const int h = blockIdx.x % a.Hq;
+  const int tok = blockIdx.x / a.Hq % a.q_len;
+  const int b = blockIdx.x / a.Hq / a.q_len;
   const int D = a.D, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int P = a.pos[b];
-  const size_t orow = ((size_t)b * a.Hq + h) * D;
-  if (P < 0 || (a.window == 0 && P >= a.capacity)) {
+  const size_t orow = (((size_t)b * a.q_len + tok) * a.Hq + h) * D;
+  if (P < 0 || P - a.q_len + 1 + tok < 0 || (a.window == 0 && P >= a.capacity)) {
     for (int e = tid; e < D; e += 128) {
       if constexpr (OBF) static_cast<uint16_t*>(a.out)[orow + e] = 0x7fc0;
       else static_cast<float*>(a.out)[orow + e] = __builtin_nanf("");
     }
     return;
   }
-  const int last = a.window > 0 ? min(P, a.window - 1) : P;
+  const int last = a.window > 0 ? min(P, a.capacity - 1) : P;
   const int nch = last / a.chunk + 1;
-  const size_t prow = ((size_t)b * a.Hq + h) * a.nchunk;
+  const size_t prow = (((size_t)b * a.q_len + tok) * a.Hq + h) * a.nchunk;
   const float* ml = a.part_ml + prow * 2;
   float M = -INFINITY;
   for (int c = tid; c < nch; c += 128) M = fmaxf(M, ml[2 * c]);
@@ -494,7 +527,7 @@ constexpr int split_waves(int D, bool kv_shared) { return (kv_shared || D == 256
 template <int D, int G, bool KVS, bool OBF>
 hipError_t launch_split(const DecodeArgs& a, hipStream_t st) {
   constexpr int NW = split_waves(D, KVS);
-  const long long n = (long long)a.B * a.Hkv * a.nchunk;
+  const long long n = (long long)a.B * a.Hkv * a.ncb * a.nchunk;
   if (n > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   if (a.n_rot <= 64)
     hipLaunchKernelGGL((decode_split_kernel<D, G, KVS, 4, NW, OBF>), dim3((unsigned)n),
@@ -528,7 +561,7 @@ hipError_t launch_split_d(const DecodeArgs& a, bool kv_shared, hipStream_t st) {
 int decode_chunk_rows(int D, int capacity, int window, bool f32) {
   (void)D;
   if (f32) return capacity;
-  if (window > 0) return 512;  // ring: one 4-wave workgroup per 512 slots
+  if (window > 0) return (capacity + TR - 1) / TR * TR;  // ring: one 4-wave workgroup per ring
   return 1024;
 }
 
@@ -545,7 +578,8 @@ hipError_t launch_decode_bf16(const DecodeArgs& a, bool kv_shared, bool out_bf16
   if (e != hipSuccess) return e;
   // a single chunk per (b, kv head) split over several waves is finished in place
   if (a.nchunk == 1 && split_waves(a.D, kv_shared) > 1) return hipSuccess;
-  const long long n = (long long)a.B * a.Hq;
+  const long long n = (long long)a.B * a.q_len * a.Hq;
+  if (n > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   if (out_bf16) hipLaunchKernelGGL(decode_merge_kernel<true>, dim3((unsigned)n), dim3(128), 0, st, a);
   else hipLaunchKernelGGL(decode_merge_kernel<false>, dim3((unsigned)n), dim3(128), 0, st, a);
   return hipGetLastError();

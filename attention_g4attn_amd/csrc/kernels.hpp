@@ -21,6 +21,9 @@ struct PrefillArgs {
   int nq, nheads;     // filled in by the launcher
 };
 
+// Decode of q_len query tokens per sequence: q, out [B, q_len, Hq, D]; pos[b]
+// is the position P of the last token, token j sits at P - q_len + 1 + j.  A
+// ring (window > 0) keeps position t in slot t mod capacity.
 struct DecodeArgs {
   const void* q;
   const void* k;
@@ -28,13 +31,26 @@ struct DecodeArgs {
   void* out;
   const int32_t* pos;
   int B, Hq, Hkv, D, capacity, window, n_rot;
+  int q_len;    // query tokens per sequence (1 = ordinary decode)
+  int ncb;      // 16-column blocks over the q_len * G (token, head) columns
   double log2_theta;
   float scale_log2e;
   float scale;
   int chunk;    // cache rows per workgroup
   int nchunk;   // chunks per (b, kv head)
-  float* part_o;   // [B, Hq, nchunk, D]
-  float* part_ml;  // [B, Hq, nchunk, 2]
+  float* part_o;   // [B, q_len, Hq, nchunk, D]
+  float* part_ml;  // [B, q_len, Hq, nchunk, 2]
+};
+
+// Raw key/value rows of a prefill into the decode cache layout.
+struct FillArgs {
+  const void* k;
+  const void* v;   // null for K=V (only k_cache is written)
+  const int32_t* pos;
+  void* k_cache;
+  void* v_cache;
+  int B, S, Hkv, capacity, window;
+  int row_chunks;  // 16-byte chunks per cache row (d * element size / 16)
 };
 
 // bf16 inputs, matrix-core path; D in {256, 512}, G in {1, 2, 4, 8}.
@@ -55,6 +71,7 @@ hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t st);
 hipError_t launch_decode_bf16(const DecodeArgs& a, bool kv_shared, bool out_bf16,
                               hipStream_t st);
 hipError_t launch_decode_f32(const DecodeArgs& a, hipStream_t st);
+hipError_t launch_fill_cache(const FillArgs& a, hipStream_t st);
 
 // rows of the cache one decode workgroup covers, and chunks per (b, kv head)
 int decode_chunk_rows(int D, int capacity, int window, bool f32);

@@ -144,6 +144,64 @@ int g4attn_decode(const void* q, const void* k_cache, const void* v_cache, void*
 /* Workspace bytes g4attn_decode needs for these sizes (0 on invalid sizes). */
 size_t g4attn_decode_workspace_bytes(int B, int Hq, int Hkv, int d, int capacity, int window);
 
+/*
+ * Cache fill: write the raw key (and value) rows of a prefill into the decode
+ * cache layout, so decoding continues where the prefill ended (the KV cache
+ * grows with the prompt and the generated tokens: "Visao geral do modelo
+ * Gemma 4", section "Principais Consideracoes para o planejamento de
+ * memoria").  New tokens are appended the same way, with S = their count.
+ *   k        [B, S, Hkv, d]           dtype
+ *   v        [B, S, Hkv, d]           dtype, or NULL for K=V (only k_cache
+ *                                     is written)
+ *   pos      [B, S] int32 positions of the tokens
+ *   k_cache, v_cache [B, Hkv, capacity, d]  dtype (v_cache unused for K=V)
+ *   window > 0: ring; the last min(S, capacity) tokens of each sequence go
+ *            to slot pos mod capacity.
+ *   window == 0: linear; a token with 0 <= pos < capacity goes to row pos.
+ *   Tokens with negative positions are not written; cache rows not written
+ *   keep their contents.  Positions written in one call must differ modulo
+ *   capacity (consecutive positions do); otherwise which row lands in a
+ *   shared slot is unspecified.
+ *   dtype: G4A_F32 or G4A_BF16; d * element size must be a multiple of 16.
+ * Bytes are copied unchanged.  Returns G4A_OK or a negative status.
+ */
+int g4attn_fill_cache(const void* k, const void* v, const int32_t* pos, int B, int S, int Hkv,
+                      int d, void* k_cache, void* v_cache, int capacity, int window, int dtype,
+                      void* stream);
+
+/*
+ * Decode of q_len query tokens per sequence at once: the verify step of
+ * speculative decoding, where a draft model proposes tokens and the model
+ * checks them in one pass (every Gemma 4 size ships a draft model: "Visao
+ * geral do modelo Gemma 4", section "Recursos").  q_len = 1 is
+ * g4attn_decode.
+ *   q        [B, q_len, Hq, d]       in_dtype
+ *   k_cache, v_cache                 as for g4attn_decode (NULL v: K=V)
+ *   out      [B, q_len, Hq, d]       out_dtype
+ *   pos      [B] int32: position P of the LAST query token; token j sits at
+ *            P - q_len + 1 + j, and the keys/values of all q_len tokens must
+ *            already be in the cache.  Token j sees positions
+ *            max(0, Pj - window + 1) .. Pj (window 0: 0 .. Pj).
+ *   window > 0: ring; position t lives in slot t mod capacity, and capacity
+ *            must be at least window + q_len - 1 so that the ring still holds
+ *            the whole window of the first token.
+ *   window == 0: linear cache, row t holds position t.
+ *   1 <= q_len <= 8.  Rows of a token with a negative position, and every row
+ *   of a sequence with P >= capacity in a linear cache, are NaN.
+ *   workspace: at least g4attn_decode_multi_workspace_bytes(...) bytes, as
+ *   for g4attn_decode.
+ * Returns G4A_OK or a negative status.
+ */
+int g4attn_decode_multi(const void* q, const void* k_cache, const void* v_cache, void* out,
+                        const int32_t* pos, int B, int q_len, int Hq, int Hkv, int d,
+                        int capacity, int window, float theta, float p, int in_dtype,
+                        int out_dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes g4attn_decode_multi needs for these sizes (0 on invalid
+ * sizes). */
+size_t g4attn_decode_multi_workspace_bytes(int B, int q_len, int Hq, int Hkv, int d, int capacity,
+                                           int window);
+
 /* Static text for a status code. */
 const char* g4attn_strerror(int status);
 

@@ -126,3 +126,54 @@ def test_workspace_size():
     assert f(64, 16, 8, 256, 512, 512) == 64 * 16 * 1 * (256 + 2) * 4  # one 512-slot chunk
     assert f(1, 16, 8, 256, 1024, 512) == 0  # ring capacity must equal the window
     assert f(1, 0, 8, 256, 512, 512) == 0
+
+
+def decm(**kw):
+    args = dict(q=A, k=2 * A, v=3 * A, out=4 * A, pos=5 * A, B=2, q_len=4, Hq=16, Hkv=8, d=256,
+                capacity=515, window=512, theta=1e4, p=1.0, i=1, o=0, ws=6 * A,
+                ws_bytes=1 << 30, stream=None)
+    args.update(kw)
+    return L.lib().g4attn_decode_multi(*args.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q_len=0), -1), (dict(q_len=9), -1), (dict(capacity=514), -1),  # ring < W + q_len - 1
+    (dict(capacity=0), -1), (dict(q=None), -1), (dict(pos=None), -1), (dict(B=-1), -1),
+    (dict(d=96), -2), (dict(Hq=48), -2), (dict(ws=None), -4), (dict(ws_bytes=100), -4),
+    (dict(out=4 * A + 4), -3),
+])
+def test_decode_multi_validation(kw, code):
+    assert decm(**kw) == code
+
+
+def test_decode_multi_workspace_size():
+    f = L.lib().g4attn_decode_multi_workspace_bytes
+    g = L.lib().g4attn_decode_workspace_bytes
+    # one token equals plain decode; a ring is one chunk of its whole capacity
+    assert f(64, 1, 16, 2, 512, 65536, 0) == g(64, 16, 2, 512, 65536, 0)
+    assert f(64, 4, 16, 8, 256, 515, 512) == 64 * 4 * 16 * 1 * (256 + 2) * 4
+    assert f(2, 3, 16, 2, 512, 4096, 0) == 2 * 3 * 16 * 4 * (512 + 2) * 4
+    assert f(2, 4, 16, 8, 256, 514, 512) == 0  # ring too small for 4 tokens
+    assert f(2, 9, 16, 8, 256, 600, 512) == 0  # at most 8 tokens
+
+
+def fill(**kw):
+    args = dict(k=A, v=2 * A, pos=3 * A, B=1, S=16, Hkv=8, d=256, kc=4 * A, vc=5 * A,
+                capacity=512, window=512, dtype=1, stream=None)
+    args.update(kw)
+    return L.lib().g4attn_fill_cache(*args.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(k=None), -1), (dict(pos=None), -1), (dict(kc=None), -1), (dict(vc=None), -1),
+    (dict(B=-1), -1), (dict(Hkv=0), -1), (dict(capacity=0), -1), (dict(window=-1), -1),
+    (dict(dtype=5), -2), (dict(d=4), -2),  # 8 bytes a row: not whole 16-byte chunks
+    (dict(k=A + 2), -3), (dict(kc=4 * A + 8), -3),
+])
+def test_fill_cache_validation(kw, code):
+    assert fill(**kw) == code
+
+
+def test_fill_cache_empty_is_noop():
+    assert fill(S=0, k=None, v=None, pos=None, kc=None, vc=None) == 0
+    assert fill(B=0, k=None, v=None, pos=None, kc=None, vc=None) == 0

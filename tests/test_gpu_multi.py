@@ -1,0 +1,164 @@
+"""Cache fill and decode of several query tokens per sequence, through the C ABI,
+against the fp64 oracle (GPU).
+
+- g4attn_fill_cache is a byte copy: compared bit for bit with oracle.fill_cache.
+- g4attn_decode_multi is compared element by element with oracle.decode_multi on
+  the same caches, across ring and linear caches, K=V and separate K/V, the
+  one-wave d = 512 path, one to four 16-column blocks (G * q_len up to 64),
+  several cache chunks (merge kernel), fp32 inputs and bf16 outputs.
+- Closed loop: prefill, fill the cache with the prompt and then the new
+  tokens, decode the new tokens at once: equals the oracle's prefill rows.
+Tolerances as for the other parity tests (bf16: max 1e-2, mean 1e-3; f32 1e-4).
+"""
+import numpy as np
+import pytest
+import torch
+
+import attention_g4attn_amd as g4
+import oracle
+from attention_g4attn_amd import inputs
+from tests.helpers import assert_parity, to_oracle
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def _cache_pair(layer, dtype, seed_):
+    shape = (layer.B, layer.Hkv, layer.capacity, layer.d)
+    k = inputs.randn(shape, seed_, dtype, DEV)
+    v = None if layer.kind == "global" else inputs.randn(shape, seed_ + 1, dtype, DEV)
+    return k, v
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
+@pytest.mark.parametrize("case", ["ring", "ring-wrap", "linear", "linear-kv"])
+def test_fill_cache_bit_exact(case, dtype):
+    B, Hkv, d = 2, 3, 256
+    if case == "ring":        # short prompt into a larger ring
+        S, C, W, off, kv = 40, 64, 64, 0, False
+    elif case == "ring-wrap": # more tokens than slots: the last C land, wrapped
+        S, C, W, off, kv = 150, 64, 60, 37, False
+    elif case == "linear":    # some positions past the cache and negative ones skipped
+        S, C, W, off, kv = 50, 45, 0, -3, False
+    else:
+        S, C, W, off, kv = 33, 80, 0, 10, True
+    k = inputs.randn((B, S, Hkv, d), 501, dtype, DEV)
+    v = None if kv else inputs.randn((B, S, Hkv, d), 502, dtype, DEV)
+    pos = inputs.positions(B, S, DEV, off)
+    kc = torch.full((B, Hkv, C, d), 7.0, dtype=dtype, device=DEV)
+    vc = None if kv else torch.full((B, Hkv, C, d), -3.0, dtype=dtype, device=DEV)
+    want_k, want_v = oracle.fill_cache(to_oracle(k), None if kv else to_oracle(v),
+                                       pos.cpu().numpy(), to_oracle(kc),
+                                       None if kv else to_oracle(vc), W)
+    print(f"fill_cache {case} {dtype}", flush=True)
+    g4.fill_cache(k, v, pos, kc, vc, W)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_oracle(kc), want_k)
+    if not kv:
+        assert np.array_equal(to_oracle(vc), want_v)
+
+
+def _run_multi(layer, L, dtype, lengths, seed_, out_dtype=None):
+    kc, vc = _cache_pair(layer, dtype, seed_)
+    if layer.window == 0:  # rows past each sequence are never read
+        for b in range(layer.B):
+            kc[b, :, int(lengths[b]):] = float("nan")
+    q = inputs.randn((layer.B, L, layer.Hq, layer.d), seed_ + 2, dtype, DEV)
+    pos = (lengths - 1).to(torch.int32).to(DEV)
+    print(f"decode_multi {layer} L={L} {dtype} lengths={lengths.tolist()}", flush=True)
+    out = g4.decode_multi(q, kc, vc, pos, layer.window, layer.theta, layer.p,
+                          out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    ref = oracle.decode_multi(to_oracle(q), to_oracle(kc), None if vc is None else to_oracle(vc),
+                              pos.cpu().numpy(), layer.window, layer.theta, layer.p)
+    return out, ref
+
+
+# kind, B, Hq, Hkv, d, capacity, window, theta, p
+MULTI = [
+    # local ring, G = 2: capacity exactly window + L - 1
+    ("local-ring-min", lambda L: inputs.DecodeLayer("local", 3, 16, 8, 256, 64 + L - 1, 64,
+                                                    1e4, 1.0), (1, 3, 8)),
+    # local ring of 512 slots plus room for the draft tokens
+    ("local-ring-512", lambda L: inputs.DecodeLayer("local", 2, 16, 8, 256, 519, 512, 1e4, 1.0),
+     (4, 8)),
+    # global K=V linear cache, G = 8: 1 to 4 column blocks, several 1024-row chunks
+    ("global-kv", lambda L: inputs.DecodeLayer("global", 2, 16, 2, 512, 3000, 0, 1e6, 0.25),
+     (1, 2, 3, 8)),
+    # separate K/V at d = 512 (one-wave path), G = 4, every pair turning
+    ("local-sep512", lambda L: inputs.DecodeLayer("local", 2, 8, 2, 512, 300, 0, 1e4, 1.0),
+     (4, 5)),
+]
+CASES = [(name, mk, L) for name, mk, Ls in MULTI for L in Ls]
+
+
+@pytest.mark.parametrize("name,mk,L", CASES, ids=[f"{c[0]}-L{c[2]}" for c in CASES])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
+def test_decode_multi_parity(name, mk, L, dtype):
+    layer = mk(L)
+    if layer.window > 0:
+        lengths = torch.tensor([L, layer.capacity - 1, 5 * layer.capacity + 3][:layer.B])
+    else:
+        lengths = torch.tensor([L + 1, layer.capacity, 1700][:layer.B])
+    out, ref = _run_multi(layer, L, dtype, lengths, 700 + 10 * L)
+    assert_parity(out, ref, dtype, f"{name} L={L}")
+
+
+def test_decode_multi_bf16_output():
+    layer = inputs.DecodeLayer("global", 2, 16, 2, 512, 2100, 0, 1e6, 0.25)
+    out, ref = _run_multi(layer, 3, torch.bfloat16, torch.tensor([2100, 40]), 900,
+                          out_dtype=torch.bfloat16)
+    assert out.dtype == torch.bfloat16
+    got = out.float().cpu().double().numpy()
+    assert np.all(np.abs(got - ref) <= 1e-2 + 2.0 ** -8 * np.abs(ref))
+
+
+@pytest.mark.parametrize("window", [0, 32])
+def test_decode_multi_negative_token_positions_nan(window):
+    """pos = 1 with 4 tokens: tokens 0 and 1 sit at -2 and -1 and give NaN rows."""
+    C = 40 if window else 100
+    layer = inputs.DecodeLayer("local", 2, 4, 2, 256, C, window, 1e4, 1.0)
+    kc, vc = _cache_pair(layer, torch.bfloat16, 950)
+    q = inputs.randn((2, 4, 4, 256), 951, torch.bfloat16, DEV)
+    pos = torch.tensor([1, 30], dtype=torch.int32, device=DEV)
+    out = g4.decode_multi(q, kc, vc, pos, window, 1e4, 1.0)
+    torch.cuda.synchronize()
+    assert torch.isnan(out[0, :2]).all() and torch.isfinite(out[0, 2:]).all()
+    assert torch.isfinite(out[1]).all()
+    ref = oracle.decode_multi(to_oracle(q), to_oracle(kc), to_oracle(vc), pos.cpu().numpy(),
+                              window, 1e4, 1.0)
+    assert_parity(out[0, 2:], ref[0, 2:], torch.bfloat16, "valid tokens")
+
+
+@pytest.mark.parametrize("kind", ["local", "global"])
+def test_prefill_fill_cache_decode_closed_loop(kind):
+    """Prefill S tokens; fill the cache with the first S-L as a prompt and the
+    last L as new tokens; decoding the L tokens at once gives the prefill rows."""
+    L = 4
+    if kind == "local":
+        layer = inputs.Layer("local", 2, 300, 16, 8, 256, 64, 1e4, 1.0)
+        C = layer.window + L - 1
+    else:
+        layer = inputs.Layer("global", 1, 300, 16, 2, 512, 0, 1e6, 0.25)
+        C = 512
+    q, k, v, pos = inputs.prefill_inputs(layer, 97, 0, torch.bfloat16, DEV)
+    S = layer.S
+    kv = kind == "global"
+    kc = torch.full((layer.B, layer.Hkv, C, layer.d), float("nan"), dtype=torch.bfloat16,
+                    device=DEV)
+    vc = None if kv else torch.full_like(kc, float("nan"))
+    print(f"closed loop {layer} C={C}", flush=True)
+    g4.fill_cache(k[:, :S - L].contiguous(), None if kv else v[:, :S - L].contiguous(),
+                  pos[:, :S - L].contiguous(), kc, vc, layer.window)
+    g4.fill_cache(k[:, S - L:].contiguous(), None if kv else v[:, S - L:].contiguous(),
+                  pos[:, S - L:].contiguous(), kc, vc, layer.window)
+    out = g4.decode_multi(q[:, S - L:].contiguous(), kc, vc,
+                          torch.full((layer.B,), S - 1, dtype=torch.int32, device=DEV),
+                          layer.window, layer.theta, layer.p)
+    torch.cuda.synchronize()
+    rows = np.array([b * S + i for b in range(layer.B) for i in range(S - L, S)], np.int64)
+    ref = oracle.prefill(to_oracle(q), to_oracle(k), to_oracle(v), pos.cpu().numpy(),
+                         layer.window, layer.theta, layer.p, rows=rows)
+    ref = ref.reshape(layer.B, L, layer.Hq, layer.d)
+    assert_parity(out, ref, torch.bfloat16, f"closed loop {kind}")

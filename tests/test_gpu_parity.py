@@ -158,7 +158,7 @@ DEC = [
     inputs.DecodeLayer("local", 4, 16, 8, 256, 512, 512, 1e4, 1.0),
     inputs.DecodeLayer("local", 3, 8, 4, 256, 96, 96, 1e4, 1.0),
     inputs.DecodeLayer("global", 3, 8, 1, 512, 700, 0, 1e6, 0.25),
-    # two 512-row chunks of a 1024-slot ring (merge kernel), G = 1
+    # a 1024-slot ring: one chunk of 64 tiles for four waves, G = 1
     inputs.DecodeLayer("local", 4, 4, 4, 256, 1024, 1024, 1e4, 1.0),
     # separate K and V at d = 512 (one-wave path), every pair turning, G = 4
     inputs.DecodeLayer("local", 3, 8, 2, 512, 256, 256, 1e4, 1.0),
