@@ -117,10 +117,19 @@ decode_split_kernel(DecodeArgs a) {
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l16 = lane & 15, g4 = lane >> 4;
-  const int ch = blockIdx.x % a.nchunk;
-  const int rest = blockIdx.x / a.nchunk;
-  const int cb = rest % a.ncb;  // block of 16 (query token, head) columns
-  const int bh = rest / a.ncb;
+  // Units (b, kv head, chunk) go in groups of 8; the column blocks of the
+  // units of a group take grid indices 8 apart (r apart in a last, smaller
+  // group of r units).  Workgroups are dealt to the 8 XCDs in grid order, so
+  // every column block of a chunk runs on the same XCD at about the same time
+  // and its later reads of the chunk hit that XCD's L2.
+  const int nunit = a.B * a.Hkv * a.nchunk;
+  const int grp = blockIdx.x / (8 * a.ncb);
+  const int gsz = min(8, nunit - 8 * grp);  // units in this group
+  const int within = blockIdx.x - grp * 8 * a.ncb;
+  const int cb = within / gsz;  // block of 16 (query token, head) columns
+  const int unit = 8 * grp + within % gsz;
+  const int ch = unit % a.nchunk;
+  const int bh = unit / a.nchunk;
   const int b = bh / a.Hkv, hkv = bh % a.Hkv;
   const int P = a.pos[b];
   const int W = a.window, C = a.capacity, QL = a.q_len;

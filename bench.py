@@ -185,6 +185,7 @@ def main():
             per_kind["global_decode"].append(next(it))
     print(f"# timed {args.steps} steps in {wall:.2f}s", file=sys.stderr, flush=True)
     extra = {} if args.no_configs else time_configs(g4, inputs, torch)
+    nxt = {} if args.no_configs else time_next(g4, inputs, torch)
 
     fl_loc, fl_glo = prefill_flops(loc), prefill_flops(glo)
     (fdl, bdl), (fdg, bdg) = decode_cost(dloc, lengths), decode_cost(dglo, lengths)
@@ -255,6 +256,7 @@ def main():
                    "only": args.only},
         "kinds": kind_rep,
         "configs": extra,
+        "next": nxt,
         "roofline": roof,
         "roofline_decode": roof_dec,
         "cpu_baseline": cpu,
@@ -302,6 +304,75 @@ def time_configs(g4, inputs, torch, reps=5):
         res[name] = {"ms": ms, "tflops": fl / ms / 1e9,
                      "frac_mfma": fl / ms / 1e9 / MFMA_BF16_PEAK_TFLOPS}
         del q, k, v, pos, out, ws
+    return res
+
+
+def _event_time(torch, call, reps):
+    """Mean ms of reps calls on the current stream, after one warm-up call."""
+    call(0)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for r in range(reps):
+        call(r)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def time_next(g4, inputs, torch, q_len=4, reps=8):
+    """The steps on either side of the path: filling the decode caches from a
+    prefill, and decoding q_len tokens per sequence at once (the verify step
+    of speculative decoding), at the decode and group shapes.  Rates count
+    every cache row once (the algorithmic bytes)."""
+    res = {}
+    # local: a ring of window + q_len - 1 slots per (sequence, kv head); four
+    # distinct caches in turn, as distinct layers are (beyond the last-level cache)
+    base = inputs.DECODE_LOCAL
+    loc = inputs.DecodeLayer(base.kind, base.B, base.Hq, base.Hkv, base.d,
+                             base.window + q_len - 1, base.window, base.theta, base.p)
+    caches = [inputs.decode_inputs(loc, 60 + i, 0, torch.bfloat16, "cuda")[1:3] for i in range(4)]
+    q = inputs.randn((loc.B, q_len, loc.Hq, loc.d), 6001, torch.bfloat16, "cuda")
+    pos = torch.full((loc.B,), 100000, dtype=torch.int32, device="cuda")
+    out = torch.empty(q.shape, dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(16, g4.decode_multi_workspace_bytes(loc.B, q_len, loc.Hq, loc.Hkv, loc.d,
+                                                              loc.capacity, loc.window)),
+                     dtype=torch.uint8, device="cuda")
+    ms = _event_time(torch, lambda r: g4.decode_multi(q, caches[r % 4][0], caches[r % 4][1], pos,
+                                                      loc.window, loc.theta, loc.p, out=out,
+                                                      workspace=ws), reps)
+    byts = loc.B * loc.Hkv * loc.capacity * loc.d * 2 * 2 + q.numel() * (2 + 4)
+    res[f"decode_multi_local_q{q_len}"] = {"us": ms * 1e3, "GBps": byts / ms / 1e6,
+                                          "frac_hbm": byts / ms / 1e6 / HBM_PEAK_GBS,
+                                          "tok_per_s": loc.B * q_len / ms * 1e3}
+    del caches, q, out, ws
+    # global: the K=V linear cache of the decode shape, lengths as there
+    glo = inputs.DECODE_GLOBAL
+    _, kc, _, pos, lengths = inputs.decode_inputs(glo, 61, 0, torch.bfloat16, "cuda")
+    q = inputs.randn((glo.B, q_len, glo.Hq, glo.d), 6101, torch.bfloat16, "cuda")
+    out = torch.empty(q.shape, dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(16, g4.decode_multi_workspace_bytes(glo.B, q_len, glo.Hq, glo.Hkv, glo.d,
+                                                              glo.capacity, 0)),
+                     dtype=torch.uint8, device="cuda")
+    ms = _event_time(torch, lambda r: g4.decode_multi(q, kc, None, pos, 0, glo.theta, glo.p,
+                                                      out=out, workspace=ws), reps)
+    byts = int(lengths.sum()) * glo.Hkv * glo.d * 2 + q.numel() * (2 + 4)
+    res[f"decode_multi_global_q{q_len}"] = {"us": ms * 1e3, "GBps": byts / ms / 1e6,
+                                           "frac_hbm": byts / ms / 1e6 / HBM_PEAK_GBS,
+                                           "tok_per_s": glo.B * q_len / ms * 1e3,
+                                           "column_blocks": (glo.Hq // glo.Hkv * q_len + 15) // 16}
+    del kc, q, out, ws
+    # cache fill of the group's global prefill rows (K=V, linear cache)
+    gl = inputs.global_(1, inputs.GROUP_S)
+    k = inputs.randn((gl.B, gl.S, gl.Hkv, gl.d), 6201, torch.bfloat16, "cuda")
+    p = inputs.positions(gl.B, gl.S, "cuda")
+    kc = torch.empty((gl.B, gl.Hkv, gl.S, gl.d), dtype=torch.bfloat16, device="cuda")
+    ms = _event_time(torch, lambda r: g4.fill_cache(k, None, p, kc, None, 0), reps)
+    byts = 2 * k.numel() * 2 + p.numel() * 4
+    res["fill_cache_global_s262144"] = {"us": ms * 1e3, "GBps": byts / ms / 1e6,
+                                        "frac_hbm": byts / ms / 1e6 / HBM_PEAK_GBS}
+    del k, p, kc
     return res
 
 
