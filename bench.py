@@ -214,6 +214,9 @@ def main():
                                      "tok_per_s": dglo.B / tg * 1e3}
         kind_rep["group_decode_tok_per_s"] = dloc.B / (5 * tl + tg) * 1e3
 
+    if not args.no_configs:
+        nxt["schedules"] = time_schedules(g4, inputs, torch, kind_rep)
+
     roof = None
     if run_global:
         t = mean(per_kind["global_prefill"])
@@ -373,6 +376,66 @@ def time_next(g4, inputs, torch, q_len=4, reps=8):
     res["fill_cache_global_s262144"] = {"us": ms * 1e3, "GBps": byts / ms / 1e6,
                                         "frac_hbm": byts / ms / 1e6 / HBM_PEAK_GBS}
     del k, p, kc
+    return res
+
+
+# Full-depth attention schedules of the pages' model sizes ("Guia visual do
+# Gemma 4", section "Intercalacao de camadas de atencao": window 512 for
+# E2B/E4B and 1024 for the large models, 4:1 interleave for E2B and 5:1 for
+# the others, the last layer always global; layer counts 35 (E2B), 42 (E4B)
+# and 60 (31B) from the same page and the techtoday page; context 128K for the
+# small models and 256K for the medium ones: "Visao geral do modelo Gemma 4",
+# section "Recursos").  The pages give no head counts for these sizes, so the
+# layers use this block's head geometry.
+SCHEDULES = {
+    "e2b_128k": dict(layers=35, ratio=4, window=512, S=131072),
+    "e4b_128k": dict(layers=42, ratio=5, window=512, S=131072),
+    "31b_256k": dict(layers=60, ratio=5, window=1024, S=262144),
+}
+
+
+def time_schedules(g4, inputs, torch, kinds, reps=2):
+    """Prefill and one decode step of every layer of each schedule, from
+    per-layer timings: the layers of a kind at one context cost the same."""
+    res, cache = {}, {}
+
+    def prefill_ms(layer):
+        key = (layer.kind, layer.S, layer.window)
+        if key not in cache:
+            q, k, v, pos = inputs.prefill_inputs(layer, 80, 0, torch.bfloat16, "cuda")
+            out = torch.empty(q.shape, dtype=torch.float32, device="cuda")
+            ws = torch.empty(max(16, g4.prefill_workspace_bytes(layer.B, layer.S, layer.Hkv,
+                                                                layer.d, layer.p)),
+                             dtype=torch.uint8, device="cuda")
+            if layer.kind == "global":
+                f = lambda r: g4.global_prefill(q, k, pos, 0, layer.theta, layer.p, out=out,
+                                                workspace=ws)
+            else:
+                f = lambda r: g4.local_prefill(q, k, v, pos, layer.window, layer.theta, layer.p,
+                                               out=out, workspace=ws)
+            cache[key] = _event_time(torch, f, reps)
+            del q, k, v, pos, out, ws
+        return cache[key]
+
+    for name, sc in SCHEDULES.items():
+        n_glob = sc["layers"] // (sc["ratio"] + 1)
+        n_loc = sc["layers"] - n_glob
+        loc = inputs.local(1, sc["S"], window=sc["window"])
+        glo = inputs.global_(1, sc["S"])
+        t_pre = n_loc * prefill_ms(loc) + n_glob * prefill_ms(glo)
+        fl = n_loc * prefill_flops(loc) + n_glob * prefill_flops(glo)
+        entry = {"layers": sc["layers"], "local_layers": n_loc, "global_layers": n_glob,
+                 "window": sc["window"], "context": sc["S"], "prefill_ms": t_pre,
+                 "prefill_tflops": fl / t_pre / 1e9}
+        # decode: local layers are 512-slot rings at window 512 (measured in
+        # the step); a 1024-slot ring reads twice the bytes at the same rate
+        if "local_decode" in kinds and "global_decode" in kinds:
+            tl = kinds["local_decode"]["us"] * sc["window"] / 512
+            tg = kinds["global_decode"]["us"]
+            step = n_loc * tl + n_glob * tg
+            entry.update({"decode_step_us": step, "decode_tok_per_s": 64 / step * 1e6,
+                          "decode_note": "batch 64; local time scaled by window / 512"})
+        res[name] = entry
     return res
 
 

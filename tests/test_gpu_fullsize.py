@@ -68,6 +68,11 @@ def test_global_prefill_s32768():
     check_prefill(inputs.GLOBAL_PREFILL, 3, 0, n_random=12, seed=31)
 
 
+def test_small_model_local_layer_window512_s131072():
+    """The local layer of the small model sizes: window 512 at 128K context."""
+    check_prefill(inputs.local(1, 131072, window=512), 8, 0, n_random=24, seed=81)
+
+
 def test_group_local_layer_s262144():
     check_prefill(inputs.GROUP_LOCAL, 5, 0, n_random=32, seed=51)
 

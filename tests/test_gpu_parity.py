@@ -58,6 +58,7 @@ SMALL = [
     inputs.Layer("global", 1, 140, 8, 1, 512, 0, 1e6, 1.0),   # K=V, every pair turns
     inputs.Layer("global", 1, 203, 8, 2, 512, 0, 1e6, 0.25),  # G=4: 32 tokens per workgroup
     inputs.Layer("global", 1, 211, 8, 1, 512, 96, 1e6, 0.25),  # window on the K=V path
+    inputs.Layer("local", 1, 1100, 8, 4, 256, 512, 1e4, 1.0),  # small-model window 512
 ]
 
 
