@@ -10,6 +10,7 @@ Array conventions (row-major, contiguous):
   decode   q [B,Hq,d], k_cache/v_cache [B,Hkv,C,d], pos [B] int32
   decode_multi q [B,L,Hq,d], caches as decode, pos [B] (last query's position)
   fill_cache k/v [B,S,Hkv,d], pos [B,S] -> caches [B,Hkv,C,d]
+  fp8 caches  uint8 E4M3 codes [B,Hkv,C,d] with float32 scales [Hkv]
 Inputs are float32, or bf16 given as their uint16 bit patterns; outputs fp64.
 """
 import ctypes
@@ -41,6 +42,12 @@ def load(path):
     lib.g4o_rope.restype = None
     lib.g4o_nrot.argtypes = [I, D]
     lib.g4o_nrot.restype = I
+    lib.g4o_e4m3_value.argtypes = [I]
+    lib.g4o_e4m3_value.restype = D
+    lib.g4o_e4m3_encode.argtypes = [ctypes.c_float]
+    lib.g4o_e4m3_encode.restype = I
+    lib.g4o_quantize_e4m3.argtypes = [P, I, P, L, I, I, P]
+    lib.g4o_quantize_e4m3.restype = I
     return lib
 
 
@@ -57,13 +64,16 @@ def _lib(lib=None):
     return _LIB
 
 
-def _in(a):
-    """Return (contiguous array, dtype code): 0 = float32, 1 = bf16 bits."""
+def _in(a, f64=False):
+    """Return (contiguous array, dtype code): 0 = float32, 1 = bf16 bits, 2 = float64
+    (float64 only where f64 is set: decode of dequantized caches)."""
     a = np.ascontiguousarray(a)
     if a.dtype == np.float32:
         return a, 0
     if a.dtype == np.uint16:
         return a, 1
+    if f64 and a.dtype == np.float64:
+        return a, 2
     raise TypeError(f"oracle inputs must be float32 or uint16 (bf16 bits), got {a.dtype}")
 
 
@@ -151,10 +161,10 @@ def decode(q, k_cache, v_cache, pos, window, theta, p, lib=None):
 
 def decode_multi(q, k_cache, v_cache, pos, window, theta, p, lib=None):
     """L query tokens per sequence (q [B,L,Hq,d]; pos [B] = last query's position)."""
-    q, dt = _in(q)
-    k_cache, dk = _in(k_cache)
+    q, dt = _in(q, f64=True)
+    k_cache, dk = _in(k_cache, f64=True)
     if v_cache is not None:
-        v_cache, dv = _in(v_cache)
+        v_cache, dv = _in(v_cache, f64=True)
         assert dv == dk and v_cache.shape == k_cache.shape
     assert dt == dk
     B, L, Hq, d = q.shape
@@ -170,14 +180,16 @@ def decode_multi(q, k_cache, v_cache, pos, window, theta, p, lib=None):
 
 
 def fill_cache(k, v, pos, k_cache, v_cache, window, lib=None):
-    """Copies of k_cache (and v_cache) with the prefill rows k, v [B,S,Hkv,d] written in."""
-    k, dk = _in(k)
+    """Copies of k_cache (and v_cache) with the prefill rows k, v [B,S,Hkv,d] written in
+    (float32, bf16 bits, or uint8 E4M3 codes; bytes are copied unchanged)."""
+    k = np.ascontiguousarray(k)
+    assert k.dtype in (np.float32, np.uint16, np.uint8), k.dtype
     kc = np.array(k_cache, copy=True, order="C")
     assert kc.dtype == k.dtype
     vc = None
     if v is not None:
-        v, dv = _in(v)
-        assert dv == dk and v.shape == k.shape
+        v = np.ascontiguousarray(v)
+        assert v.dtype == k.dtype and v.shape == k.shape
         vc = np.array(v_cache, copy=True, order="C")
         assert vc.dtype == v.dtype and vc.shape == kc.shape
     B, S, Hkv, d = k.shape
@@ -190,3 +202,60 @@ def fill_cache(k, v, pos, k_cache, v_cache, window, lib=None):
     if rc != 0:
         raise ValueError(f"g4o_fill_cache failed ({rc})")
     return kc, vc
+
+
+def e4m3_values(lib=None):
+    """fp64 value of every E4M3 code 0..255 (NaN for 0x7F and 0xFF)."""
+    L = _lib(lib)
+    return np.array([L.g4o_e4m3_value(c) for c in range(256)], np.float64)
+
+
+def e4m3_encode(x, lib=None):
+    """E4M3 code of each float32 value of x (round to nearest even, saturating)."""
+    L = _lib(lib)
+    x = np.asarray(x, np.float32)
+    return np.array([L.g4o_e4m3_encode(float(v)) for v in x.ravel()],
+                    np.int64).astype(np.uint8).reshape(x.shape)
+
+
+def quantize_e4m3(x, scale, lib=None):
+    """E4M3 codes of x [..., Hkv, d] (float32 or bf16 bits) divided by scale[Hkv]."""
+    x, dt = _in(x)
+    scale = np.ascontiguousarray(scale, np.float32)
+    Hkv, d = x.shape[-2:]
+    assert scale.shape == (Hkv,)
+    out = np.empty(x.shape, np.uint8)
+    rc = _lib(lib).g4o_quantize_e4m3(_ptr(x), dt, _ptr(scale), x.size // (Hkv * d), Hkv, d,
+                                     _ptr(out))
+    if rc != 0:
+        raise ValueError(f"g4o_quantize_e4m3 failed ({rc})")
+    return out
+
+
+def dequantize_e4m3(codes, scale, lib=None):
+    """fp64 values code_value * scale[h] of an E4M3 cache [B, Hkv, C, d] (exact)."""
+    scale = np.asarray(scale, np.float32).astype(np.float64)
+    return e4m3_values(lib)[np.asarray(codes, np.uint8)] * scale[None, :, None, None]
+
+
+def fill_cache_fp8(k, v, pos, k_cache, v_cache, window, k_scale, v_scale, lib=None):
+    """fill_cache into E4M3 caches: the rows are quantized with the per-KV-head
+    scales, then written as the plain fill writes bytes."""
+    kq = quantize_e4m3(k, k_scale, lib)
+    vq = None if v is None else quantize_e4m3(v, v_scale, lib)
+    return fill_cache(kq, vq, pos, k_cache, v_cache, window, lib=lib)
+
+
+def decode_fp8(q, k_codes, v_codes, k_scale, v_scale, pos, window, theta, p, lib=None):
+    """decode_multi over E4M3 caches (v_codes None: K=V, values use k_scale):
+    the caches are dequantized exactly in fp64 and decoded as raw caches."""
+    kc = dequantize_e4m3(k_codes, k_scale, lib)
+    vc = None if v_codes is None else dequantize_e4m3(v_codes, v_scale, lib)
+    qf = np.asarray(q)
+    qf = bf16_bits_to_f64(qf) if qf.dtype == np.uint16 else qf.astype(np.float64)
+    return decode_multi(qf, kc, vc, pos, window, theta, p, lib=lib)
+
+
+def bf16_bits_to_f64(bits):
+    """Exact fp64 values of bf16 bit patterns."""
+    return (np.asarray(bits, np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)

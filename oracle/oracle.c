@@ -61,9 +61,10 @@
 #define G4O_EINVAL (-1)
 #define G4O_ENOMEM (-2)
 
-/* element idx of an input array of dtype 0 (fp32) or 1 (bf16 bits) */
+/* element idx of an input array of dtype 0 (fp32), 1 (bf16 bits) or 2 (fp64) */
 static double g4o_in(const void* base, int dtype, size_t idx) {
   if (dtype == 0) return (double)((const float*)base)[idx];
+  if (dtype == 2) return ((const double*)base)[idx];
   uint32_t bits = ((uint32_t)((const uint16_t*)base)[idx]) << 16;
   float f;
   memcpy(&f, &bits, sizeof f);
@@ -361,7 +362,7 @@ int g4o_decode(const void* q, const void* kc, const void* vc, int dtype, const i
  * Gemma 4", section "Principais Consideracoes para o planejamento de
  * memoria").
  *   k, v [B, S, Hkv, d] (v NULL: K=V, only k_cache is written), esize bytes
- *   per element; pos [B, S]; k_cache, v_cache [B, Hkv, capacity, d].
+ *   per element (1 for fp8 codes already quantized by g4o_quantize_e4m3); pos [B, S]; k_cache, v_cache [B, Hkv, capacity, d].
  *   window > 0 (ring): the last min(S, capacity) tokens i of each sequence
  *     go to slot pos[b,i] mod capacity;
  *   window = 0 (linear): every token with 0 <= pos[b,i] < capacity goes to
@@ -372,7 +373,8 @@ int g4o_decode(const void* q, const void* kc, const void* vc, int dtype, const i
 int g4o_fill_cache(const void* k, const void* v, int esize, const int32_t* pos, int B, int S,
                    int Hkv, int d, int capacity, int window, void* k_cache, void* v_cache) {
   if (B < 0 || S < 0 || Hkv <= 0 || d <= 0 || capacity <= 0 || window < 0) return G4O_EINVAL;
-  if ((esize != 2 && esize != 4) || !k || !pos || !k_cache || (v && !v_cache)) return G4O_EINVAL;
+  if ((esize != 1 && esize != 2 && esize != 4) || !k || !pos || !k_cache || (v && !v_cache))
+    return G4O_EINVAL;
   const size_t row = (size_t)d * esize;
   for (int b = 0; b < B; ++b) {
     const int first = window > 0 && S > capacity ? S - capacity : 0;
@@ -413,7 +415,7 @@ int g4o_decode_multi(const void* q, const void* kc, const void* vc, int dtype, c
                      double p, double* out) {
   int rc = g4o_check(B, 1, Hq, Hkv, d, window, theta, p);
   if (rc) return rc;
-  if (!q || !kc || !pos || !out || capacity <= 0 || L < 1 || (dtype != 0 && dtype != 1))
+  if (!q || !kc || !pos || !out || capacity <= 0 || L < 1 || dtype < 0 || dtype > 2)
     return G4O_EINVAL;
   if (window > 0 && capacity < window + L - 1) return G4O_EINVAL;
   if (!vc) vc = kc;
@@ -470,4 +472,71 @@ int g4o_decode_multi(const void* q, const void* kc, const void* vc, int dtype, c
     free(qr); free(kr); free(sc);
   }
   return err ? G4O_ENOMEM : G4O_OK;
+}
+
+/*
+ * Low-precision KV cache: FP8 E4M3 codes with a scale per KV head.
+ *
+ * The pages name optimized KV caches among the memory savings of the mobile
+ * checkpoints and say the cache grows with every token ("Visao geral do modelo
+ * Gemma 4", sections "Treinamento com reconhecimento de quantizacao (QAT)" and
+ * "Principais Consideracoes para o planejamento de memoria"); they give no
+ * format.  Reading taken: one byte per element in the OCP 8-bit floating-point
+ * format E4M3 (1 sign bit, 4 exponent bits with bias 7, 3 mantissa bits,
+ * subnormals at exponent 0, no infinities, S.1111.111 the only NaN), the
+ * cached value being code value x scale[kv head].
+ */
+
+/* Value of E4M3 code c (0..255), from the format's definition. */
+double g4o_e4m3_value(int c) {
+  const int sign = (c >> 7) & 1, e = (c >> 3) & 15, m = c & 7;
+  double v;
+  if (e == 15 && m == 7) return NAN;
+  if (e == 0) v = ldexp((double)m, -9);          /* subnormal: m/8 * 2^(1-7) */
+  else v = ldexp(1.0 + (double)m / 8.0, e - 7);  /* normal: (1 + m/8) * 2^(e-7) */
+  return sign ? -v : v;
+}
+
+/* E4M3 code of x: the nearest value of the format, a tie going to the one with
+ * the even mantissa (round to nearest even); |x| at or beyond the largest value
+ * 448 (infinities included) gives +-448; zero keeps its sign; NaN gives 0x7F. */
+int g4o_e4m3_encode(float x) {
+  if (isnan(x)) return 0x7F;
+  const int sign = signbit(x) ? 0x80 : 0;
+  double a = fabs((double)x);
+  if (a >= 448.0) return sign | 0x7E;
+  if (a == 0.0) return sign;
+  int e2;
+  frexp(a, &e2);      /* a = f * 2^e2, f in [0.5, 1): a lies in binade [2^(e2-1), 2^e2) */
+  int E = e2 - 1;
+  if (E < -6) E = -6; /* below 2^-6 the subnormal spacing 2^-9 applies */
+  /* the format has 8 values per binade: spacing 2^(E-3) */
+  const double quantum = ldexp(1.0, E - 3);
+  const double n = nearbyint(a / quantum); /* default rounding: ties to even */
+  const double v = n * quantum;
+  /* the code holding v (v <= 448 since a < 448 rounds to at most 448) */
+  for (int c = 0; c < 0x7F; ++c)
+    if (g4o_e4m3_value(c) == v) return sign | c;
+  return -1;
+}
+
+/*
+ * Quantize rows of a [rows, Hkv, d] tensor to E4M3 codes:
+ *   out[r, h, e] = encode( fp32(x[r, h, e]) / scale[h] )
+ * with the quotient rounded once to fp32 (IEEE division).  dtype: 0 fp32 or
+ * 1 bf16 bits.
+ */
+int g4o_quantize_e4m3(const void* x, int dtype, const float* scale, int64_t rows, int Hkv, int d,
+                      uint8_t* out) {
+  if (!x || !scale || !out || rows < 0 || Hkv <= 0 || d <= 0 || (dtype != 0 && dtype != 1))
+    return G4O_EINVAL;
+  for (int64_t r = 0; r < rows; ++r)
+    for (int h = 0; h < Hkv; ++h)
+      for (int e = 0; e < d; ++e) {
+        const size_t i = ((size_t)r * Hkv + h) * d + e;
+        const float xf = (float)g4o_in(x, dtype, i); /* exact: the input is fp32 or bf16 */
+        const float y = xf / scale[h];
+        out[i] = (uint8_t)g4o_e4m3_encode(y);
+      }
+  return G4O_OK;
 }
