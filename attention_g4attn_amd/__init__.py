@@ -7,7 +7,8 @@ every step of the computation runs in the library's HIP kernels.  There is no
 CPU or PyTorch fallback: if the library is missing, calls raise.
 
 Layouts (contiguous): prefill q/out [B,S,Hq,d], k/v/kv [B,S,Hkv,d], pos [B,S]
-int32; decode q/out [B,Hq,d], caches [B,Hkv,capacity,d], pos [B] int32.
+int32; decode q/out [B,Hq,d], caches [B,Hkv,capacity,d], pos [B] int32; fp8
+caches hold one E4M3 code per element with float32 scales [Hkv].
 """
 from ._lib import lib as _g4lib
 
@@ -178,6 +179,68 @@ def fill_cache(k, v, pos, k_cache, v_cache, window):
                                   _ptr(v_cache), C, int(window), _code(k), _stream())
     _check(rc, "g4attn_fill_cache")
     return k_cache, v_cache
+
+
+def _fp8_cache(t):
+    if t is not None and t.element_size() != 1:
+        raise TypeError(f"fp8 caches hold one byte per element (uint8 or float8_e4m3fn), got {t.dtype}")
+
+
+def _scales(*ts):
+    torch = _torch()
+    for t in ts:
+        if t is not None and t.dtype != torch.float32:
+            raise TypeError(f"scales must be float32, got {t.dtype}")
+
+
+def fill_cache_fp8(k, v, pos, k_cache, v_cache, window, k_scale, v_scale=None):
+    """Quantize prefill rows k, v [B, S, Hkv, d] (bf16 or f32) into E4M3 caches
+    [B, Hkv, capacity, d] (g4attn_fill_cache_fp8): code = E4M3(x / scale[h]).
+
+    v None means K=V (only k_cache is written, v_scale unused).
+    """
+    _dev(k, v, pos, k_cache, v_cache, k_scale, v_scale)
+    _fp8_cache(k_cache)
+    _fp8_cache(v_cache)
+    _scales(k_scale, v_scale)
+    B, S, Hkv, d = k.shape
+    C = k_cache.shape[2]
+    rc = _g4lib().g4attn_fill_cache_fp8(_ptr(k), _ptr(v), _ptr(k_scale), _ptr(v_scale), _ptr(pos),
+                                        B, S, Hkv, d, _ptr(k_cache), _ptr(v_cache), C,
+                                        int(window), _code(k), _stream())
+    _check(rc, "g4attn_fill_cache_fp8")
+    return k_cache, v_cache
+
+
+def decode_fp8_workspace_bytes(B, q_len, Hq, Hkv, d, capacity, window):
+    return int(_g4lib().g4attn_decode_fp8_workspace_bytes(B, q_len, Hq, Hkv, d, capacity, window))
+
+
+def decode_fp8(q, k_cache, v_cache, k_scale, v_scale, pos, window, theta, p, out=None,
+               workspace=None, out_dtype=None):
+    """Decode of q_len query tokens over E4M3 caches (g4attn_decode_fp8).
+
+    q is bf16 [B, q_len, Hq, d]; caches [B, Hkv, capacity, d] hold one code
+    per element (uint8 or float8_e4m3fn); k_scale, v_scale are float32 [Hkv];
+    v_cache None means K=V (values are k_cache with k_scale).
+    """
+    _dev(q, k_cache, v_cache, k_scale, v_scale, pos, out, workspace)
+    _fp8_cache(k_cache)
+    _fp8_cache(v_cache)
+    _scales(k_scale, v_scale)
+    if _code(q) != BF16:
+        raise TypeError("decode_fp8 takes a bfloat16 query")
+    B, L, Hq, d = q.shape
+    _, Hkv, C, _ = k_cache.shape
+    out = _out((B, L, Hq, d), out, out_dtype, q.device)
+    workspace = _workspace(decode_fp8_workspace_bytes(B, L, Hq, Hkv, d, C, window), workspace,
+                           q.device)
+    rc = _g4lib().g4attn_decode_fp8(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale),
+                                    _ptr(v_scale), _ptr(out), _ptr(pos), B, L, Hq, Hkv, d, C,
+                                    int(window), float(theta), float(p), _code(out),
+                                    _ptr(workspace), _nbytes(workspace), _stream())
+    _check(rc, "g4attn_decode_fp8")
+    return out
 
 
 def strerror(status):

@@ -16,7 +16,7 @@ CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libg4attn.so")
 BUILD = os.path.join(HERE, "_build")
 SOURCES = ["api.cpp", "prefill_kv512.hip", "prefill_d256.hip", "prefill_sep512.hip",
-           "decode_bf16.hip", "attn_f32.hip", "cache_fill.hip"]
+           "decode_bf16.hip", "decode_fp8.hip", "attn_f32.hip", "cache_fill.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 FLAGS = ["-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden", f"--offload-arch={ARCH}",

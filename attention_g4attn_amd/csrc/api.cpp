@@ -243,6 +243,107 @@ G4A_API int g4attn_fill_cache(const void* k, const void* v, const int32_t* pos, 
   return finish(g4a::launch_fill_cache(a, static_cast<hipStream_t>(stream)));
 }
 
+namespace {
+
+size_t decode_fp8_ws_bytes(int B, int q_len, int Hq, int Hkv, int d, int capacity, int window) {
+  if (B < 0 || q_len < 1 || q_len > 8 || Hq <= 0 || Hkv <= 0 || d <= 0 || capacity <= 0 ||
+      window < 0)
+    return 0;
+  if (!ring_ok(capacity, window, q_len, true)) return 0;
+  const size_t nch = (size_t)g4a::decode_fp8_num_chunks(capacity, window);
+  const size_t bytes = (size_t)B * q_len * Hq * nch * ((size_t)d + 2) * sizeof(float);
+  return bytes > 0 ? bytes : 16;
+}
+
+}  // namespace
+
+G4A_API size_t g4attn_decode_fp8_workspace_bytes(int B, int q_len, int Hq, int Hkv, int d,
+                                                 int capacity, int window) {
+  return decode_fp8_ws_bytes(B, q_len, Hq, Hkv, d, capacity, window);
+}
+
+G4A_API int g4attn_decode_fp8(const void* q, const void* k_cache, const void* v_cache,
+                              const float* k_scale, const float* v_scale, void* out,
+                              const int32_t* pos, int B, int q_len, int Hq, int Hkv, int d,
+                              int capacity, int window, float theta, float p, int out_dtype,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  if (B < 0 || capacity <= 0 || q_len < 1 || q_len > 8) return G4A_EINVAL;
+  if (!ring_ok(capacity, window, q_len, true)) return G4A_EINVAL;
+  int rc = check_common(Hq, Hkv, d, window, theta, p, G4A_BF16, out_dtype);
+  if (rc) return rc;
+  if (B == 0) return G4A_OK;
+  const bool kv_shared = v_cache == nullptr || v_cache == k_cache;
+  if (!q || !k_cache || !out || !pos || !k_scale || (!kv_shared && !v_scale)) return G4A_EINVAL;
+  if (misaligned(q) || misaligned(k_cache) || (v_cache && misaligned(v_cache)) ||
+      misaligned(out) || misaligned(pos) || misaligned(k_scale) ||
+      (!kv_shared && misaligned(v_scale)))
+    return G4A_EALIGN;
+  if ((double)B * Hkv * capacity * d > 9.0e18) return G4A_EINVAL;
+  g4a::DecodeArgs a{};
+  a.q = q;
+  a.k = k_cache;
+  a.v = kv_shared ? k_cache : v_cache;
+  a.out = out;
+  a.pos = pos;
+  a.B = B;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.D = d;
+  a.capacity = capacity;
+  a.window = window;
+  a.n_rot = rotated_pairs(d, p);
+  a.q_len = q_len;
+  a.ncb = ((Hq / Hkv) * q_len + 15) / 16;
+  a.log2_theta = log2((double)theta);
+  a.scale = (float)(1.0 / sqrt((double)d));
+  a.scale_log2e = (float)(1.4426950408889634 / sqrt((double)d));
+  a.chunk = g4a::decode_fp8_chunk_rows(capacity, window);
+  a.nchunk = g4a::decode_fp8_num_chunks(capacity, window);
+  a.k_scale = k_scale;
+  a.v_scale = kv_shared ? k_scale : v_scale;
+  const size_t need = decode_fp8_ws_bytes(B, q_len, Hq, Hkv, d, capacity, window);
+  if (!workspace || workspace_bytes < need) return G4A_EWORKSPACE;
+  if (misaligned(workspace)) return G4A_EALIGN;
+  if ((double)B * Hkv * a.ncb * a.nchunk > 2.0e9) return G4A_EINVAL;
+  a.part_o = static_cast<float*>(workspace);
+  a.part_ml = a.part_o + (size_t)B * q_len * Hq * a.nchunk * d;
+  return finish(g4a::launch_decode_fp8(a, kv_shared, out_dtype == G4A_BF16,
+                                       static_cast<hipStream_t>(stream)));
+}
+
+G4A_API int g4attn_fill_cache_fp8(const void* k, const void* v, const float* k_scale,
+                                  const float* v_scale, const int32_t* pos, int B, int S, int Hkv,
+                                  int d, void* k_cache, void* v_cache, int capacity, int window,
+                                  int in_dtype, void* stream) {
+  if (B < 0 || S < 0 || Hkv <= 0 || d <= 0 || capacity <= 0 || window < 0) return G4A_EINVAL;
+  if (in_dtype != G4A_F32 && in_dtype != G4A_BF16) return G4A_EUNSUPPORTED;
+  if (d % 16) return G4A_EUNSUPPORTED;
+  if (B == 0 || S == 0) return G4A_OK;
+  if (!k || !pos || !k_cache || !k_scale || (v && (!v_cache || !v_scale))) return G4A_EINVAL;
+  if (misaligned(k) || (v && misaligned(v)) || misaligned(pos) || misaligned(k_cache) ||
+      misaligned(k_scale) || (v && (misaligned(v_cache) || misaligned(v_scale))))
+    return G4A_EALIGN;
+  g4a::FillArgs a{};
+  a.k = k;
+  a.v = v;
+  a.pos = pos;
+  a.k_cache = k_cache;
+  a.v_cache = v ? v_cache : nullptr;
+  a.B = B;
+  a.S = S;
+  a.Hkv = Hkv;
+  a.capacity = capacity;
+  a.window = window;
+  a.row_chunks = d / 16;
+  a.in_f32 = in_dtype == G4A_F32;
+  a.d = d;
+  a.k_scale = k_scale;
+  a.v_scale = v ? v_scale : nullptr;
+  const int nw = window > 0 ? (S < capacity ? S : capacity) : S;
+  if ((double)B * nw * Hkv * a.row_chunks > 2.0e9) return G4A_EINVAL;
+  return finish(g4a::launch_fill_cache_fp8(a, static_cast<hipStream_t>(stream)));
+}
+
 G4A_API const char* g4attn_strerror(int status) {
   switch (status) {
     case G4A_OK: return "ok";

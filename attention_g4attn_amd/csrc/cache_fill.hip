@@ -4,7 +4,8 @@
 // "Principais Consideracoes para o planejamento de memoria").
 //
 // A plain copy, bound by HBM: one thread per 16-byte chunk, consecutive
-// threads along a row, so reads and writes are coalesced row by row.
+// threads along a row, so reads and writes are coalesced row by row.  The fp8
+// variant quantizes on the way (16 elements per thread).
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -34,7 +35,81 @@ __global__ void __launch_bounds__(256) fill_cache_kernel(FillArgs a, int first, 
   }
 }
 
+// E4M3 code of y, round to nearest even (the hardware conversion), after
+// saturating |y| >= 448 (infinities too) to +-448; NaN stays NaN.
+__device__ __forceinline__ float sat448(float y) {
+  return __builtin_fabsf(y) > 448.f ? __builtin_copysignf(448.f, y) : y;
+}
+
+// 4 values divided by the scale (IEEE division, rounded once to fp32) -> 4 codes
+__device__ __forceinline__ uint32_t quantize4(f32x4 x, float s) {
+  int pk = __builtin_amdgcn_cvt_pk_fp8_f32(sat448(x[0] / s), sat448(x[1] / s), 0, false);
+  pk = __builtin_amdgcn_cvt_pk_fp8_f32(sat448(x[2] / s), sat448(x[3] / s), pk, true);
+  return (uint32_t)pk;
+}
+
+// 16 input elements (bf16 or fp32) of row element offset e -> 16 codes
+template <bool F32>
+__device__ __forceinline__ u32x4 quantize16(const void* src, size_t e, float s) {
+  u32x4 out;
+  if constexpr (F32) {
+    const f32x4* p = reinterpret_cast<const f32x4*>(static_cast<const float*>(src) + e);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) out[j] = quantize4(p[j], s);
+  } else {
+    const u32x4* p = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(src) + e);
+    const u32x4 w0 = p[0], w1 = p[1];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t lo = j < 2 ? w0[2 * j] : w1[2 * j - 4];
+      const uint32_t hi = j < 2 ? w0[2 * j + 1] : w1[2 * j - 3];
+      out[j] = quantize4(f32x4{bf_lo(lo), bf_hi(lo), bf_lo(hi), bf_hi(hi)}, s);
+    }
+  }
+  return out;
+}
+
+// The same placement as fill_cache_kernel into a cache of OCP FP8 E4M3 codes
+// (cached value = code value * scale of the KV head; the pages leave the
+// format of their optimized KV caches open): each 16-byte chunk of codes is
+// quantized from 16 input elements, code = E4M3(x / scale).
+template <bool F32>
+__global__ void __launch_bounds__(256) fill_cache_fp8_kernel(FillArgs a, int first, int nw,
+                                                             int total) {
+  for (int idx = blockIdx.x * 256 + threadIdx.x; idx < total; idx += gridDim.x * 256) {
+    const int c = idx % a.row_chunks;
+    int r = idx / a.row_chunks;
+    const int g = r % a.Hkv;
+    r /= a.Hkv;
+    const int i = first + r % nw;
+    const int b = r / nw;
+    const int P = a.pos[(size_t)b * a.S + i];
+    if (P < 0 || (a.window == 0 && P >= a.capacity)) continue;
+    const int slot = a.window > 0 ? P % a.capacity : P;
+    const size_t src = ((((size_t)b * a.S + i) * a.Hkv + g) * a.row_chunks + c) * 16;  // element
+    const size_t dst = (((size_t)b * a.Hkv + g) * a.capacity + slot) * a.row_chunks + c;
+    static_cast<u32x4*>(a.k_cache)[dst] = quantize16<F32>(a.k, src, a.k_scale[g]);
+    if (a.v) static_cast<u32x4*>(a.v_cache)[dst] = quantize16<F32>(a.v, src, a.v_scale[g]);
+  }
+}
+
 }  // namespace
+
+hipError_t launch_fill_cache_fp8(const FillArgs& a, hipStream_t st) {
+  const int nw = a.window > 0 ? (a.S < a.capacity ? a.S : a.capacity) : a.S;
+  const long long total = (long long)a.B * nw * a.Hkv * a.row_chunks;
+  if (total == 0) return hipSuccess;
+  if (total > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  const long long blocks = (total + 255) / 256;
+  const dim3 grid((unsigned)(blocks < 65536 ? blocks : 65536));
+  if (a.in_f32)
+    hipLaunchKernelGGL(fill_cache_fp8_kernel<true>, grid, dim3(256), 0, st, a, a.S - nw, nw,
+                       (int)total);
+  else
+    hipLaunchKernelGGL(fill_cache_fp8_kernel<false>, grid, dim3(256), 0, st, a, a.S - nw, nw,
+                       (int)total);
+  return hipGetLastError();
+}
 
 hipError_t launch_fill_cache(const FillArgs& a, hipStream_t st) {
   // a ring keeps only the last `capacity` tokens of a sequence

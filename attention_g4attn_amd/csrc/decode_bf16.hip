@@ -31,11 +31,14 @@
 // the chunks of every query head with log-sum-exp weights.  Rows the query may
 // not see are never loaded (the load extent stops at the last visible row).
 #include "common.hpp"
+#include "decode_common.hpp"
 #include "kernels.hpp"
 
 namespace g4a {
 
 namespace {
+
+using namespace dec;
 
 constexpr int TR = 16;  // cache rows per tile
 
@@ -59,32 +62,6 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const unsigned char* p) {
 // bank groups; rows 0..7 map to even and rows 8..15 to odd values, so a
 // transpose read (32 lanes = 8 rows x 2 adjacent chunks) hits 16 as well.
 __device__ __forceinline__ int dswz(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  const uint64_t p = reinterpret_cast<uint64_t>(base);
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)p);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(p >> 32));
-  const uint32_t n = __builtin_amdgcn_readfirstlane(bytes);
-  void* u = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
-  return __builtin_amdgcn_make_buffer_rsrc(u, (short)0, (int)n, 0x00020000);
-}
-
-__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rs, uint32_t voff,
-                                          unsigned char* ldst) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(ldst),
-                                           16, voff, 0, 0, 0);
-}
-
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
-template <class T>
-__device__ __forceinline__ T& lds_at(unsigned char* base, int off) {
-  return *reinterpret_cast<T*>(base + off);
-}
 
 // RK = score k-steps (32 dims each) that may hold turning pairs: 4 when
 // n_rot <= 64 (dims < 128, e.g. p-RoPE at p = 0.25), else all of them.
@@ -117,20 +94,8 @@ decode_split_kernel(DecodeArgs a) {
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l16 = lane & 15, g4 = lane >> 4;
-  // Units (b, kv head, chunk) go in groups of 8; the column blocks of the
-  // units of a group take grid indices 8 apart (r apart in a last, smaller
-  // group of r units).  Workgroups are dealt to the 8 XCDs in grid order, so
-  // every column block of a chunk runs on the same XCD at about the same time
-  // and its later reads of the chunk hit that XCD's L2.
-  const int nunit = a.B * a.Hkv * a.nchunk;
-  const int grp = blockIdx.x / (8 * a.ncb);
-  const int gsz = min(8, nunit - 8 * grp);  // units in this group
-  const int within = blockIdx.x - grp * 8 * a.ncb;
-  const int cb = within / gsz;  // block of 16 (query token, head) columns
-  const int unit = 8 * grp + within % gsz;
-  const int ch = unit % a.nchunk;
-  const int bh = unit / a.nchunk;
-  const int b = bh / a.Hkv, hkv = bh % a.Hkv;
+  const Unit u = unit_of_block(a);  // XCD-aware grid order
+  const int cb = u.cb, ch = u.ch, b = u.b, hkv = u.hkv;
   const int P = a.pos[b];
   const int W = a.window, C = a.capacity, QL = a.q_len;
   // Column n of the block is (token, head) pair c = 16*cb + n: query token
@@ -145,12 +110,7 @@ decode_split_kernel(DecodeArgs a) {
   const int Pq = col_pos(col_ok ? l16 : 0);  // this lane's column position
   const bool direct = NW > 1 && a.nchunk == 1;  // this workgroup writes the output
   if (P < 0 || (W == 0 && P >= C)) {  // bad position: NaN rows (else the merge writes them)
-    if (direct)
-      for (int idx = threadIdx.x; idx < ncol * D; idx += 64 * NW) {
-        const size_t o = col_out(idx / D) + idx % D;
-        if constexpr (OBF) static_cast<uint16_t*>(a.out)[o] = 0x7fc0;
-        else static_cast<float*>(a.out)[o] = __builtin_nanf("");
-      }
+    if (direct) nan_columns<D, NW, OBF>(a, ncol, col_out);
     return;
   }
   const int last = W > 0 ? min(P, C - 1) : P;  // highest row index that may be visible
@@ -399,73 +359,8 @@ decode_split_kernel(DecodeArgs a) {
   // ---- partial (m, l, O) of this chunk for the block's columns ----
   l_run += __shfl_xor(l_run, 16);
   l_run += __shfl_xor(l_run, 32);
-  if constexpr (NW == 1) {
-    if (col_ok) {
-      const size_t prow = (col_out(l16) / D) * a.nchunk + ch;
-      float* po = a.part_o + prow * D + 4 * g4;
-#pragma unroll
-      for (int db = 0; db < NB; ++db) *reinterpret_cast<f32x4*>(po + 16 * db) = oacc[db];
-      if (g4 == 0) {
-        a.part_ml[prow * 2 + 0] = m_run;
-        a.part_ml[prow * 2 + 1] = l_run;
-      }
-    }
-  } else {
-    // Merge the NW waves through LDS (the tile slots are free now).  A wave's
-    // slot holds 8 columns of D floats, so the columns go in passes of 8:
-    // wave w leaves O[w][n - c0][dim] and (m, l) per column.
-    constexpr int MC = 8;
-    float* ow = reinterpret_cast<float*>(KREG ? tv : tk);
-    if (col_ok && g4 == 0) {
-      mls[w][l16][0] = m_run;
-      mls[w][l16][1] = l_run;
-    }
-    for (int c0 = 0; c0 < ncol; c0 += MC) {
-      __syncthreads();
-      if (col_ok && l16 >= c0 && l16 < c0 + MC) {
-#pragma unroll
-        for (int db = 0; db < NB; ++db)
-          *reinterpret_cast<f32x4*>(ow + ((size_t)w * MC + l16 - c0) * D + 16 * db + 4 * g4) =
-              oacc[db];
-      }
-      __syncthreads();
-      const int nc = min(MC, ncol - c0);
-      for (int idx = threadIdx.x; idx < nc * D / 4; idx += 64 * NW) {
-        const int n = c0 + idx / (D / 4), e = 4 * (idx % (D / 4));
-        float M = -INFINITY;
-#pragma unroll
-        for (int v = 0; v < NW; ++v) M = fmaxf(M, mls[v][n][0]);
-        f32x4 o = {};
-        float l = 0.f;
-#pragma unroll
-        for (int v = 0; v < NW; ++v) {
-          // 0 for a wave that saw no key of this column (and for all, if none did)
-          const float f = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mls[v][n][0] - M);
-          o += f * *reinterpret_cast<const f32x4*>(ow + ((size_t)v * MC + n - c0) * D + e);
-          l += f * mls[v][n][1];
-        }
-        if (direct) {
-          // every column sees its own key unless its position is negative
-          o = col_pos(n) >= 0 ? o * (1.f / l) : f32x4{__builtin_nanf(""), __builtin_nanf(""),
-                                                        __builtin_nanf(""), __builtin_nanf("")};
-          const size_t orow = col_out(n) + e;
-          if constexpr (OBF) {
-            const u32x2 pk = {pack_bf16(o[0], o[1]), pack_bf16(o[2], o[3])};
-            *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.out) + orow) = pk;
-          } else {
-            *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + orow) = o;
-          }
-        } else {
-          const size_t prow = (col_out(n) / D) * a.nchunk + ch;
-          *reinterpret_cast<f32x4*>(a.part_o + prow * D + e) = o;
-          if (e == 0) {
-            a.part_ml[prow * 2 + 0] = M;
-            a.part_ml[prow * 2 + 1] = l;
-          }
-        }
-      }
-    }
-  }
+  finish_chunk<D, NW, OBF>(a, oacc, m_run, l_run, ch, ncol, direct,
+                           reinterpret_cast<float*>(KREG ? tv : tk), mls, col_out, col_pos);
 }
 
 // Combine the chunk partials of query head h of token j of sequence b:
@@ -587,6 +482,10 @@ hipError_t launch_decode_bf16(const DecodeArgs& a, bool kv_shared, bool out_bf16
   if (e != hipSuccess) return e;
   // a single chunk per (b, kv head) split over several waves is finished in place
   if (a.nchunk == 1 && split_waves(a.D, kv_shared) > 1) return hipSuccess;
+  return launch_decode_merge(a, out_bf16, st);
+}
+
+hipError_t launch_decode_merge(const DecodeArgs& a, bool out_bf16, hipStream_t st) {
   const long long n = (long long)a.B * a.q_len * a.Hq;
   if (n > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   if (out_bf16) hipLaunchKernelGGL(decode_merge_kernel<true>, dim3((unsigned)n), dim3(128), 0, st, a);

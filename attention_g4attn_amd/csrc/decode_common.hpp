@@ -1,0 +1,154 @@
+// Pieces shared by the split-KV decode kernels (bf16 cache and fp8 cache):
+// buffer resources and 16-byte direct-to-LDS loads, the grid -> (column
+// block, chunk, sequence, KV head) mapping, and the end of a chunk (partial
+// (m, l, O) to the workspace, or the merge of a workgroup's waves in LDS).
+#pragma once
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace g4a {
+namespace dec {
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)p);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(p >> 32));
+  const uint32_t n = __builtin_amdgcn_readfirstlane(bytes);
+  void* u = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(u, (short)0, (int)n, 0x00020000);
+}
+
+// 16 bytes at voff of the resource into LDS at ldst + 16 * lane (reads past
+// the resource's size return zeros)
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rs, uint32_t voff,
+                                          unsigned char* ldst) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(ldst),
+                                           16, voff, 0, 0, 0);
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+template <class T>
+__device__ __forceinline__ T& lds_at(unsigned char* base, int off) {
+  return *reinterpret_cast<T*>(base + off);
+}
+
+// Work unit of a split workgroup: column block cb (16 (query token, head)
+// columns), chunk ch of the cache rows, sequence b, KV head hkv.
+struct Unit {
+  int cb, ch, b, hkv;
+};
+
+// Units (b, kv head, chunk) go in groups of 8; the column blocks of the units
+// of a group take grid indices 8 apart (r apart in a last, smaller group of r
+// units).  Workgroups are dealt to the 8 XCDs in grid order, so every column
+// block of a chunk runs on the same XCD at about the same time and its later
+// reads of the chunk hit that XCD's L2.
+__device__ __forceinline__ Unit unit_of_block(const DecodeArgs& a) {
+  const int nunit = a.B * a.Hkv * a.nchunk;
+  const int grp = blockIdx.x / (8 * a.ncb);
+  const int gsz = min(8, nunit - 8 * grp);  // units in this group
+  const int within = blockIdx.x - grp * 8 * a.ncb;
+  const int unit = 8 * grp + within % gsz;
+  const int bh = unit / a.nchunk;
+  return Unit{within / gsz, unit % a.nchunk, bh / a.Hkv, bh % a.Hkv};
+}
+
+// End of a chunk.  oacc holds O^T of this wave (lane (g4, l16): dims
+// 16*db + 4*g4 + r of column l16), m_run / l_run the column's running max
+// (base 2) and sum, already summed over the lanes of the column.
+//   NW == 1: the wave writes its partial (m, l, O) to the workspace.
+//   NW > 1: the waves merge through LDS (ow: NW * 8 * D floats, mls: (m, l)
+//   per wave and column); the merged chunk goes to the workspace, or, when
+//   `direct` (one chunk covers every row), is normalised into the output.
+// Columns go in passes of 8 so a wave's LDS share holds 8 columns of D floats.
+template <int D, int NW, bool OBF, class ColOut, class ColPos>
+__device__ __forceinline__ void finish_chunk(const DecodeArgs& a, const f32x4 (&oacc)[D / 16],
+                                             float m_run, float l_run, int ch, int ncol,
+                                             bool direct, float* ow, float (*mls)[16][2],
+                                             ColOut col_out, ColPos col_pos) {
+  constexpr int NB = D / 16;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int l16 = lane & 15, g4 = lane >> 4;
+  const bool col_ok = l16 < ncol;
+  if constexpr (NW == 1) {
+    if (col_ok) {
+      const size_t prow = (col_out(l16) / D) * a.nchunk + ch;
+      float* po = a.part_o + prow * D + 4 * g4;
+#pragma unroll
+      for (int db = 0; db < NB; ++db) *reinterpret_cast<f32x4*>(po + 16 * db) = oacc[db];
+      if (g4 == 0) {
+        a.part_ml[prow * 2 + 0] = m_run;
+        a.part_ml[prow * 2 + 1] = l_run;
+      }
+    }
+  } else {
+    constexpr int MC = 8;
+    if (col_ok && g4 == 0) {
+      mls[w][l16][0] = m_run;
+      mls[w][l16][1] = l_run;
+    }
+    for (int c0 = 0; c0 < ncol; c0 += MC) {
+      __syncthreads();
+      if (col_ok && l16 >= c0 && l16 < c0 + MC) {
+#pragma unroll
+        for (int db = 0; db < NB; ++db)
+          *reinterpret_cast<f32x4*>(ow + ((size_t)w * MC + l16 - c0) * D + 16 * db + 4 * g4) =
+              oacc[db];
+      }
+      __syncthreads();
+      const int nc = min(MC, ncol - c0);
+      for (int idx = threadIdx.x; idx < nc * D / 4; idx += 64 * NW) {
+        const int n = c0 + idx / (D / 4), e = 4 * (idx % (D / 4));
+        float M = -INFINITY;
+#pragma unroll
+        for (int v = 0; v < NW; ++v) M = fmaxf(M, mls[v][n][0]);
+        f32x4 o = {};
+        float l = 0.f;
+#pragma unroll
+        for (int v = 0; v < NW; ++v) {
+          // 0 for a wave that saw no key of this column (and for all, if none did)
+          const float f = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mls[v][n][0] - M);
+          o += f * *reinterpret_cast<const f32x4*>(ow + ((size_t)v * MC + n - c0) * D + e);
+          l += f * mls[v][n][1];
+        }
+        if (direct) {
+          // every column sees its own key unless its position is negative
+          o = col_pos(n) >= 0 ? o * (1.f / l) : f32x4{__builtin_nanf(""), __builtin_nanf(""),
+                                                        __builtin_nanf(""), __builtin_nanf("")};
+          const size_t orow = col_out(n) + e;
+          if constexpr (OBF) {
+            const u32x2 pk = {pack_bf16(o[0], o[1]), pack_bf16(o[2], o[3])};
+            *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.out) + orow) = pk;
+          } else {
+            *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + orow) = o;
+          }
+        } else {
+          const size_t prow = (col_out(n) / D) * a.nchunk + ch;
+          *reinterpret_cast<f32x4*>(a.part_o + prow * D + e) = o;
+          if (e == 0) {
+            a.part_ml[prow * 2 + 0] = M;
+            a.part_ml[prow * 2 + 1] = l;
+          }
+        }
+      }
+    }
+  }
+}
+
+// NaN rows of the block's columns (a sequence whose position is out of range)
+template <int D, int NW, bool OBF, class ColOut>
+__device__ __forceinline__ void nan_columns(const DecodeArgs& a, int ncol, ColOut col_out) {
+  for (int idx = threadIdx.x; idx < ncol * D; idx += 64 * NW) {
+    const size_t o = col_out(idx / D) + idx % D;
+    if constexpr (OBF) static_cast<uint16_t*>(a.out)[o] = 0x7fc0;
+    else static_cast<float*>(a.out)[o] = __builtin_nanf("");
+  }
+}
+
+}  // namespace dec
+}  // namespace g4a

@@ -40,6 +40,9 @@ struct DecodeArgs {
   int nchunk;   // chunks per (b, kv head)
   float* part_o;   // [B, q_len, Hq, nchunk, D]
   float* part_ml;  // [B, q_len, Hq, nchunk, 2]
+  // fp8 caches only: value = code value * scale[kv head] (v_scale is k_scale for K=V)
+  const float* k_scale;
+  const float* v_scale;
 };
 
 // Raw key/value rows of a prefill into the decode cache layout.
@@ -51,6 +54,11 @@ struct FillArgs {
   void* v_cache;
   int B, S, Hkv, capacity, window;
   int row_chunks;  // 16-byte chunks per cache row (d * element size / 16)
+  // quantizing fill into fp8 caches: input dtype (0 f32, 1 bf16), head dim,
+  // per-KV-head scales
+  int in_f32, d;
+  const float* k_scale;
+  const float* v_scale;
 };
 
 // bf16 inputs, matrix-core path; D in {256, 512}, G in {1, 2, 4, 8}.
@@ -71,10 +79,17 @@ hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t st);
 hipError_t launch_decode_bf16(const DecodeArgs& a, bool kv_shared, bool out_bf16,
                               hipStream_t st);
 hipError_t launch_decode_f32(const DecodeArgs& a, hipStream_t st);
+// merge of the split partials (the chunks of every (token, query head))
+hipError_t launch_decode_merge(const DecodeArgs& a, bool out_bf16, hipStream_t st);
+// bf16 query over fp8 E4M3 caches; D in {256, 512}, G in {1, 2, 4, 8}
+hipError_t launch_decode_fp8(const DecodeArgs& a, bool kv_shared, bool out_bf16, hipStream_t st);
 hipError_t launch_fill_cache(const FillArgs& a, hipStream_t st);
+hipError_t launch_fill_cache_fp8(const FillArgs& a, hipStream_t st);
 
 // rows of the cache one decode workgroup covers, and chunks per (b, kv head)
 int decode_chunk_rows(int D, int capacity, int window, bool f32);
 int decode_num_chunks(int D, int capacity, int window, bool f32);
+int decode_fp8_chunk_rows(int capacity, int window);
+int decode_fp8_num_chunks(int capacity, int window);
 
 }  // namespace g4a

@@ -120,3 +120,44 @@ def decode_inputs(layer: DecodeLayer, workload, index, dtype, device, lengths=No
             k[b, :, L:] = float("nan")
     pos = (lengths - 1).to(torch.int32).to(device)
     return q, k, v, pos, lengths
+
+
+def e4m3_codes(shape, seed_, device, spread=8.0):
+    """E4M3 codes (uint8) of N(0, spread^2) draws, through torch's float8_e4m3fn
+    cast (|x| stays far below 448 for spread 8, so nothing saturates)."""
+    x = randn(shape, seed_, torch.float32, device) * spread
+    return x.to(torch.float8_e4m3fn).view(torch.uint8)
+
+
+def kv_scales(Hkv, seed_, device, lo=0.08, hi=0.16):
+    """Per-KV-head cache scales, uniform in [lo, hi): code values of spread 8
+    times these are about N(0, 1)."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed_)
+    return (lo + (hi - lo) * torch.rand(Hkv, generator=g, dtype=torch.float32)).to(device)
+
+
+def decode_inputs_fp8(layer: DecodeLayer, workload, index, device, lengths=None, q_len=1):
+    """q [B, q_len, Hq, d] bf16, E4M3 caches [B, Hkv, capacity, d] uint8 (v None
+    for K=V), k_scale, v_scale [Hkv] float32 (v_scale None for K=V), pos [B]
+    int32 (last query's position), lengths [B].  As decode_inputs: ring caches
+    are full; a linear cache holds lengths[b] tokens and NaN codes (0x7F) past
+    them, which the kernels must never read."""
+    B = layer.B
+    if lengths is None:
+        lengths = decode_lengths(B)
+    lengths = lengths.to(torch.int64)
+    q = randn((B, q_len, layer.Hq, layer.d), seed(workload, index, 1), torch.bfloat16, device)
+    shape = (B, layer.Hkv, layer.capacity, layer.d)
+    k = torch.empty(shape, dtype=torch.uint8, device=device)
+    v = None if layer.kind == "global" else torch.empty(shape, dtype=torch.uint8, device=device)
+    for b in range(B):
+        k[b] = e4m3_codes(shape[1:], seed(workload, index, 2) * 100003 + b, device)
+        if v is not None:
+            v[b] = e4m3_codes(shape[1:], seed(workload, index, 3) * 100003 + b, device)
+        if layer.window == 0:
+            k[b, :, int(lengths[b]):] = 0x7F
+    ks = kv_scales(layer.Hkv, seed(workload, index, 4), device)
+    vs = None if v is None else kv_scales(layer.Hkv, seed(workload, index, 5), device)
+    pos = (lengths - 1).to(torch.int32).to(device)
+    return q, k, v, ks, vs, pos, lengths

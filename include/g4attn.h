@@ -202,6 +202,62 @@ int g4attn_decode_multi(const void* q, const void* k_cache, const void* v_cache,
 size_t g4attn_decode_multi_workspace_bytes(int B, int q_len, int Hq, int Hkv, int d, int capacity,
                                            int window);
 
+/*
+ * Low-precision KV cache: one byte per cached element, an OCP FP8 E4M3 code
+ * (1 sign bit, 4 exponent bits with bias 7, 3 mantissa bits, subnormals at
+ * exponent 0, no infinities, 0x7F / 0xFF NaN), the cached value being
+ * code value x scale of its KV head.  The pages count optimized KV caches
+ * among the memory savings of the mobile checkpoints and note that the cache
+ * grows with every token ("Visao geral do modelo Gemma 4", sections
+ * "Treinamento com reconhecimento de quantizacao (QAT)" and "Principais
+ * Consideracoes para o planejamento de memoria"); they give no format, and
+ * E4M3 with a scale per KV head is the reading this library takes.  The cache
+ * is half the bytes of a bf16 one, which halves decode's memory traffic.
+ *
+ * Cache fill into fp8 caches: as g4attn_fill_cache (same slots, same rules),
+ * each element quantized on the way:
+ *     code = E4M3(x / scale[h])
+ * with the quotient rounded once to fp32 (IEEE division), then rounded to the
+ * nearest E4M3 value, ties to the even mantissa; |quotient| >= 448 (infinity
+ * included) saturates to +-448, NaN gives a NaN code.
+ *   k, v        [B, S, Hkv, d]  in_dtype (G4A_F32 or G4A_BF16); v NULL: K=V
+ *   k_scale, v_scale  [Hkv] fp32 device arrays, positive and finite (v_scale
+ *               unused for K=V)
+ *   k_cache, v_cache  [B, Hkv, capacity, d] uint8 codes
+ *   d must be a multiple of 16.
+ * Returns G4A_OK or a negative status.
+ */
+int g4attn_fill_cache_fp8(const void* k, const void* v, const float* k_scale,
+                          const float* v_scale, const int32_t* pos, int B, int S, int Hkv, int d,
+                          void* k_cache, void* v_cache, int capacity, int window, int in_dtype,
+                          void* stream);
+
+/*
+ * Decode of q_len query tokens per sequence (1 <= q_len <= 8; 1 is ordinary
+ * decode) over fp8 caches: exactly g4attn_decode_multi over the dequantized
+ * cache (code value x scale of the KV head).
+ *   q        [B, q_len, Hq, d]  bfloat16
+ *   k_cache, v_cache  [B, Hkv, capacity, d] uint8 E4M3 codes; v_cache NULL
+ *            (or equal to k_cache): K=V, the values are k_cache with k_scale
+ *   k_scale, v_scale  [Hkv] fp32 device arrays, positive and finite
+ *   out      [B, q_len, Hq, d]  out_dtype (G4A_F32 or G4A_BF16)
+ *   pos, window, capacity, theta, p: as for g4attn_decode_multi (a ring needs
+ *   capacity >= window + q_len - 1).  d in {256, 512}; G in {1, 2, 4, 8}.
+ *   workspace: at least g4attn_decode_fp8_workspace_bytes(...) bytes.
+ * Inside, codes are widened exactly to bf16 and multiplied on the matrix
+ * cores with fp32 accumulation; the scales multiply the scores and the
+ * output.  Returns G4A_OK or a negative status.
+ */
+int g4attn_decode_fp8(const void* q, const void* k_cache, const void* v_cache,
+                      const float* k_scale, const float* v_scale, void* out, const int32_t* pos,
+                      int B, int q_len, int Hq, int Hkv, int d, int capacity, int window,
+                      float theta, float p, int out_dtype, void* workspace,
+                      size_t workspace_bytes, void* stream);
+
+/* Workspace bytes g4attn_decode_fp8 needs for these sizes (0 on invalid sizes). */
+size_t g4attn_decode_fp8_workspace_bytes(int B, int q_len, int Hq, int Hkv, int d, int capacity,
+                                         int window);
+
 /* Static text for a status code. */
 const char* g4attn_strerror(int status);
 

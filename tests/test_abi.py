@@ -177,3 +177,66 @@ def test_fill_cache_validation(kw, code):
 def test_fill_cache_empty_is_noop():
     assert fill(S=0, k=None, v=None, pos=None, kc=None, vc=None) == 0
     assert fill(B=0, k=None, v=None, pos=None, kc=None, vc=None) == 0
+
+
+def decf(**kw):
+    args = dict(q=A, k=2 * A, v=3 * A, ks=7 * A, vs=8 * A, out=4 * A, pos=5 * A, B=2, q_len=1,
+                Hq=16, Hkv=2, d=512, capacity=65536, window=0, theta=1e6, p=0.25, o=0, ws=6 * A,
+                ws_bytes=1 << 40, stream=None)
+    args.update(kw)
+    return L.lib().g4attn_decode_fp8(*args.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q_len=0), -1), (dict(q_len=9), -1), (dict(capacity=0), -1), (dict(B=-1), -1),
+    (dict(q=None), -1), (dict(pos=None), -1), (dict(ks=None), -1), (dict(vs=None), -1),
+    (dict(window=512, capacity=512, q_len=2), -1),  # ring < W + q_len - 1
+    (dict(theta=0.0), -1), (dict(p=1.5), -1), (dict(o=7), -1),
+    (dict(d=128), -2), (dict(Hq=24), -2),
+    (dict(ws=None), -4), (dict(ws_bytes=100), -4),
+    (dict(ks=7 * A + 4), -3), (dict(out=4 * A + 2), -3), (dict(k=2 * A + 1), -3),
+])
+def test_decode_fp8_validation(kw, code):
+    assert decf(**kw) == code
+
+
+def test_decode_fp8_k_equals_v_needs_no_value_scale():
+    # v NULL is K=V: a missing v_scale is fine, so the call gets as far as the
+    # workspace check (which fails here on purpose, before any launch)
+    assert decf(v=None, vs=None, ws_bytes=100) == -4
+    assert decf(v=2 * A, vs=None, ws_bytes=100) == -4  # v == k is K=V too
+
+
+def test_decode_fp8_empty_is_noop():
+    assert decf(B=0, q=None, k=None, v=None, ks=None, vs=None, out=None, pos=None, ws=None) == 0
+
+
+def test_decode_fp8_workspace_size():
+    f = L.lib().g4attn_decode_fp8_workspace_bytes
+    assert f(64, 1, 16, 2, 512, 65536, 0) == 64 * 16 * 64 * (512 + 2) * 4  # 1024-row chunks
+    assert f(64, 1, 16, 8, 256, 512, 512) == 64 * 16 * 1 * (256 + 2) * 4  # one chunk per ring
+    assert f(64, 4, 16, 8, 256, 515, 512) == 64 * 4 * 16 * 1 * (256 + 2) * 4
+    assert f(2, 4, 16, 8, 256, 514, 512) == 0  # ring too small for 4 tokens
+    assert f(2, 9, 16, 8, 256, 600, 512) == 0
+
+
+def fill8(**kw):
+    args = dict(k=A, v=2 * A, ks=6 * A, vs=7 * A, pos=3 * A, B=1, S=16, Hkv=8, d=256, kc=4 * A,
+                vc=5 * A, capacity=512, window=512, dtype=1, stream=None)
+    args.update(kw)
+    return L.lib().g4attn_fill_cache_fp8(*args.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(k=None), -1), (dict(pos=None), -1), (dict(kc=None), -1), (dict(vc=None), -1),
+    (dict(ks=None), -1), (dict(vs=None), -1), (dict(B=-1), -1), (dict(Hkv=0), -1),
+    (dict(capacity=0), -1), (dict(window=-1), -1),
+    (dict(dtype=5), -2), (dict(d=24), -2),  # rows must be whole 16-code chunks
+    (dict(k=A + 2), -3), (dict(kc=4 * A + 8), -3), (dict(vs=7 * A + 4), -3),
+])
+def test_fill_cache_fp8_validation(kw, code):
+    assert fill8(**kw) == code
+
+
+def test_fill_cache_fp8_empty_is_noop():
+    assert fill8(S=0, k=None, v=None, ks=None, vs=None, pos=None, kc=None, vc=None) == 0

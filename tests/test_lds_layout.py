@@ -177,3 +177,91 @@ def test_decode_value_operand_transpose_reads(D):
             grp, i = lane // 16, lane % 16
             got = [element(lds, src[16 * grp + i // 4 + 4 * k] + 2 * (i % 4)) for k in range(4)]
             assert got == [(4 * grp + k, 16 * db + i) for k in range(4)], (D, db, lane)
+
+
+# ---- fp8 decode tiles: 32 rows of D one-byte codes, chunk c of row r at c ^ fswz(r) ----
+
+TR8 = 32
+
+
+def fswz(r):
+    return (r & 3) | ((((r >> 3) + 2 * ((r >> 2) & 1)) & 3) << 2)
+
+
+def fp8_tile(D):
+    CPR = D // 16
+    RPI = 64 // CPR
+    lds = {}
+    for n in range(TR8 // RPI):
+        for ln in range(64):
+            row = n * RPI + ln // CPR
+            chunk = (ln % CPR) ^ fswz(row)
+            pos = n * 1024 + 16 * ln
+            assert pos not in lds and 0 <= chunk < CPR
+            lds[pos] = (row, 16 * chunk)
+    assert len(lds) == TR8 * D // 16
+    return lds
+
+
+def code_at(lds, byte):
+    """(key, dim) of the code stored at LDS byte offset `byte`."""
+    key, dim0 = lds[byte - byte % 16]
+    return key, dim0 + byte % 16
+
+
+def kchunk(s, gq):
+    return 8 * (s >> 1) + 2 * gq + (s & 1)
+
+
+@pytest.mark.parametrize("D", [256, 512])
+def test_fp8_decode_score_operand_reads(D):
+    """Half h of the score product: operand row r is key 8*(r//4) + 4h + r%4, so
+    output register j of lane group g is key 8g + 4h + j; k-step s of lane group
+    gq takes dims 8*kchunk(s, gq) .. +7 (the query operand uses the same map),
+    and over all k-steps every dim is taken exactly once."""
+    lds = fp8_tile(D)
+    for g in range(4):
+        for j in range(4):
+            for h in range(2):
+                r = 4 * g + j
+                assert 8 * (r >> 2) + 4 * h + (r & 3) == 8 * g + 4 * h + j
+    for gq in range(4):
+        dims = sorted(8 * kchunk(s, gq) + j for s in range(D // 32) for j in range(8))
+        assert len(set(dims)) == len(dims) == D // 4
+    assert sorted(8 * kchunk(s, gq) + j for s in range(D // 32) for gq in range(4)
+                  for j in range(8)) == list(range(D))
+    for h in range(2):
+        for u2 in range(D // 64):
+            offs = []
+            for lane in range(64):
+                row, gq = lane & 15, lane >> 4
+                kr = 8 * (row >> 2) + 4 * h + (row & 3)
+                off = kr * D + (((4 * u2 + gq) ^ fswz(kr)) << 4)
+                offs.append(off)
+                for e in range(2):
+                    for j in range(8):
+                        assert code_at(lds, off + 8 * e + j) == (kr, 8 * kchunk(2 * u2 + e, gq) + j)
+            for g in range(4):
+                assert len(banks16(offs[16 * g:16 * g + 16])) == 64, (D, h, u2, g)
+
+
+@pytest.mark.parametrize("D", [256, 512])
+def test_fp8_decode_value_operand_transpose_reads(D):
+    """8-bit transpose reads (gfx950 lane map: within 16 lanes, source lane n
+    holds row n // 2, bytes 8*(n % 2) .. +7 of an 8 x 16 byte block, and
+    destination lane i gets column i): lane l holds dim 16*db + l % 16 of keys
+    8*(l // 16) .. +7, the keys its P^T operand holds."""
+    lds = fp8_tile(D)
+    for db in range(D // 16):
+        src = []
+        for lane in range(64):
+            n, gq = lane & 15, lane >> 4
+            kk = 8 * gq + (n >> 1)
+            src.append(kk * D + (n & 1) * 8 + ((db ^ fswz(kk)) << 4))
+        for half in range(2):
+            banks = {(a >> 2) & 63 for a in src[32 * half:32 * half + 32] for a in (a, a + 4)}
+            assert len(banks) == 64, (D, db, half)
+        for lane in range(64):
+            grp, i = lane // 16, lane % 16
+            got = [code_at(lds, src[16 * grp + 2 * k + i // 8] + i % 8) for k in range(8)]
+            assert got == [(8 * grp + k, 16 * db + i) for k in range(8)], (D, db, lane)
