@@ -186,6 +186,8 @@ def main():
     print(f"# timed {args.steps} steps in {wall:.2f}s", file=sys.stderr, flush=True)
     extra = {} if args.no_configs else time_configs(g4, inputs, torch)
     nxt = {} if args.no_configs else time_next(g4, inputs, torch)
+    if not args.no_configs:
+        nxt["fp8"] = time_fp8(g4, inputs, torch)
 
     fl_loc, fl_glo = prefill_flops(loc), prefill_flops(glo)
     (fdl, bdl), (fdg, bdg) = decode_cost(dloc, lengths), decode_cost(dglo, lengths)
@@ -375,6 +377,55 @@ def time_next(g4, inputs, torch, q_len=4, reps=8):
     byts = 2 * k.numel() * 2 + p.numel() * 4
     res["fill_cache_global_s262144"] = {"us": ms * 1e3, "GBps": byts / ms / 1e6,
                                         "frac_hbm": byts / ms / 1e6 / HBM_PEAK_GBS}
+    del k, p, kc
+    return res
+
+
+def time_fp8(g4, inputs, torch, reps=8):
+    """Decode over FP8 E4M3 caches (one byte per element, a scale per KV head)
+    at the decode shapes, and the quantizing fill of the group's global
+    prefill rows.  Rates count every cache row once at one byte per element
+    (the algorithmic bytes of the fp8 cache)."""
+    res = {}
+    loc = inputs.DECODE_LOCAL
+    sets = [inputs.decode_inputs_fp8(loc, 70 + i, 0, "cuda") for i in range(4)]
+    out = torch.empty(sets[0][0].shape, dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(16, g4.decode_fp8_workspace_bytes(loc.B, 1, loc.Hq, loc.Hkv, loc.d,
+                                                            loc.capacity, loc.window)),
+                     dtype=torch.uint8, device="cuda")
+
+    def run_loc(r):
+        q, kc, vc, ks, vs, pos, _ = sets[r % 4]
+        g4.decode_fp8(q, kc, vc, ks, vs, pos, loc.window, loc.theta, loc.p, out=out, workspace=ws)
+
+    ms = _event_time(torch, run_loc, reps)
+    byts = loc.B * loc.Hkv * loc.capacity * loc.d * 2 + sets[0][0].numel() * (2 + 4)
+    res["decode_fp8_local"] = {"us": ms * 1e3, "GBps": byts / ms / 1e6,
+                               "frac_hbm": byts / ms / 1e6 / HBM_PEAK_GBS,
+                               "tok_per_s": loc.B / ms * 1e3}
+    del sets, out, ws
+    glo = inputs.DECODE_GLOBAL
+    q, kc, _, ks, _, pos, lengths = inputs.decode_inputs_fp8(glo, 71, 0, "cuda")
+    out = torch.empty(q.shape, dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(16, g4.decode_fp8_workspace_bytes(glo.B, 1, glo.Hq, glo.Hkv, glo.d,
+                                                            glo.capacity, 0)),
+                     dtype=torch.uint8, device="cuda")
+    ms = _event_time(torch, lambda r: g4.decode_fp8(q, kc, None, ks, None, pos, 0, glo.theta,
+                                                    glo.p, out=out, workspace=ws), reps)
+    byts = int(lengths.sum()) * glo.Hkv * glo.d + q.numel() * (2 + 4)
+    res["decode_fp8_global"] = {"us": ms * 1e3, "GBps": byts / ms / 1e6,
+                                "frac_hbm": byts / ms / 1e6 / HBM_PEAK_GBS,
+                                "tok_per_s": glo.B / ms * 1e3}
+    del q, kc, out, ws
+    gl = inputs.global_(1, inputs.GROUP_S)
+    k = inputs.randn((gl.B, gl.S, gl.Hkv, gl.d), 6201, torch.bfloat16, "cuda")
+    p = inputs.positions(gl.B, gl.S, "cuda")
+    ks = inputs.kv_scales(gl.Hkv, 6202, "cuda", 0.01, 0.02)
+    kc = torch.empty((gl.B, gl.Hkv, gl.S, gl.d), dtype=torch.uint8, device="cuda")
+    ms = _event_time(torch, lambda r: g4.fill_cache_fp8(k, None, p, kc, None, 0, ks), reps)
+    byts = k.numel() * (2 + 1) + p.numel() * 4
+    res["fill_cache_fp8_global_s262144"] = {"us": ms * 1e3, "GBps": byts / ms / 1e6,
+                                            "frac_hbm": byts / ms / 1e6 / HBM_PEAK_GBS}
     del k, p, kc
     return res
 
