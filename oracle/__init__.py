@@ -11,6 +11,7 @@ Array conventions (row-major, contiguous):
   decode_multi q [B,L,Hq,d], caches as decode, pos [B] (last query's position)
   fill_cache k/v [B,S,Hkv,d], pos [B,S] -> caches [B,Hkv,C,d]
   fp8 caches  uint8 E4M3 codes [B,Hkv,C,d] with float32 scales [Hkv]
+  vision_prefill q [B,S,Hq,d], k/v [B,S,Hkv,d], pos2 [B,S,2] (w, h), lengths [B]
 Inputs are float32, or bf16 given as their uint16 bit patterns; outputs fp64.
 """
 import ctypes
@@ -42,6 +43,8 @@ def load(path):
     lib.g4o_rope.restype = None
     lib.g4o_nrot.argtypes = [I, D]
     lib.g4o_nrot.restype = I
+    lib.g4o_vision_prefill.argtypes = [P, P, P, I, P, P, I, I, I, I, I, D, P, L, P]
+    lib.g4o_vision_prefill.restype = I
     lib.g4o_e4m3_value.argtypes = [I]
     lib.g4o_e4m3_value.restype = D
     lib.g4o_e4m3_encode.argtypes = [ctypes.c_float]
@@ -259,3 +262,36 @@ def decode_fp8(q, k_codes, v_codes, k_scale, v_scale, pos, window, theta, p, lib
 def bf16_bits_to_f64(bits):
     """Exact fp64 values of bf16 bit patterns."""
     return (np.asarray(bits, np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def vision_prefill(q, k, v, pos2, theta, lengths=None, rows=None, lib=None):
+    """Bidirectional attention with 2D RoPE over the patches of each image
+    (pos2 [B,S,2] = (w, h) per patch; lengths [B] valid patches, None = S).
+
+    rows: None for every row (out [B,S,Hq,d]) or flattened ids b*S+i
+    (out [len(rows),Hq,d]).  Rows of padding patches are zero.
+    """
+    q, dt = _in(q)
+    k, dk = _in(k)
+    v, dv = _in(v)
+    if not (dt == dk == dv):
+        raise TypeError("q, k, v must share a dtype")
+    B, S, Hq, d = q.shape
+    Hkv = k.shape[2]
+    assert k.shape == (B, S, Hkv, d) and v.shape == k.shape
+    pos2 = np.ascontiguousarray(pos2, dtype=np.int32)
+    assert pos2.shape == (B, S, 2)
+    ln = None if lengths is None else np.ascontiguousarray(lengths, dtype=np.int32)
+    assert ln is None or ln.shape == (B,)
+    if rows is None:
+        out = np.empty((B, S, Hq, d), np.float64)
+        rp, nr = None, 0
+    else:
+        rows = np.ascontiguousarray(rows, dtype=np.int64)
+        out = np.empty((rows.size, Hq, d), np.float64)
+        rp, nr = _ptr(rows), rows.size
+    rc = _lib(lib).g4o_vision_prefill(_ptr(q), _ptr(k), _ptr(v), dt, _ptr(pos2), _ptr(ln), B, S,
+                                      Hq, Hkv, d, float(theta), rp, nr, _ptr(out))
+    if rc != 0:
+        raise ValueError(f"g4o_vision_prefill failed ({rc})")
+    return out

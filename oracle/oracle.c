@@ -540,3 +540,89 @@ int g4o_quantize_e4m3(const void* x, int dtype, const float* scale, int64_t rows
       }
   return G4O_OK;
 }
+
+/*
+ * Vision-encoder attention: 2D RoPE and no causal mask.
+ *
+ * The vision encoder turns an image into a sequence of 16x16-pixel patches
+ * and encodes each patch's position with 2D RoPE, which splits the embedding
+ * in two parts and encodes the horizontal (w) and the vertical (h) position
+ * separately ("Guia visual do Gemma 4", sections "Encoder de visao" and
+ * "Suporte a proporcao variavel").  Readings taken where the page is silent:
+ *  - the head dim d is split into halves [0, d/2) and [d/2, d); half c is an
+ *    ordinary RoPE of a head of dim d/2 (pairs (2t, 2t+1) of the half, angle
+ *    pos_c * theta^(-2t/(d/2)), counter-clockwise) driven by position
+ *    component c, where component 0 is w and component 1 is h, the order the
+ *    page names them;
+ *  - every patch of an image attends to every patch of the image
+ *    (bidirectional, as in a ViT: no causal mask, no window);
+ *  - images in one batch may hold fewer than S patches: lengths[b] patches
+ *    are valid, the keys past them are not attended to, and the output rows of
+ *    the padding positions are zero.
+ *   q [B,S,Hq,d], k, v [B,S,Hkv,d]; pos2 [B,S,2] int32 (w, h); lengths [B]
+ *   int32 or NULL (all S); rows / nrows as for g4o_prefill.
+ */
+int g4o_vision_prefill(const void* q, const void* k, const void* v, int dtype,
+                       const int32_t* pos2, const int32_t* lengths, int B, int S, int Hq, int Hkv,
+                       int d, double theta, const int64_t* rows, int64_t nrows, double* out) {
+  int rc = g4o_check(B, S, Hq, Hkv, d, 0, theta, 1.0);
+  if (rc) return rc;
+  if ((d % 4) || !q || !k || !v || !pos2 || !out || (dtype != 0 && dtype != 1)) return G4O_EINVAL;
+  const int G = Hq / Hkv, half = d / 2;
+  const double scale = 1.0 / sqrt((double)d);
+  const int64_t n_out = rows ? nrows : (int64_t)B * S;
+  int err = 0;
+#pragma omp parallel
+  {
+    double* qr = (double*)malloc(sizeof(double) * d);
+    double* kr = (double*)malloc(sizeof(double) * d);
+    double* sc = (double*)malloc(sizeof(double) * (size_t)(S > 0 ? S : 1));
+    if (!qr || !kr || !sc) {
+#pragma omp atomic write
+      err = 1;
+    } else {
+#pragma omp for schedule(dynamic, 1)
+      for (int64_t task = 0; task < n_out * Hq; ++task) {
+        const int64_t ri = task / Hq;
+        const int h = (int)(task % Hq), g = h / G;
+        const int64_t id = rows ? rows[ri] : ri;
+        const int b = (int)(id / S), i = (int)(id % S);
+        double* o = out + ((size_t)ri * Hq + h) * (size_t)d;
+        int n = lengths ? lengths[b] : S;
+        if (n < 0) n = 0;
+        if (n > S) n = S;
+        if (i >= n) {  /* padding patch */
+          for (int e = 0; e < d; ++e) o[e] = 0.0;
+          continue;
+        }
+        const size_t qoff = (((size_t)b * S + i) * Hq + h) * (size_t)d;
+        const size_t pq = ((size_t)b * S + i) * 2;
+        for (int e = 0; e < d; ++e) qr[e] = g4o_in(q, dtype, qoff + e);
+        g4o_rope(qr, half, half / 2, theta, (double)pos2[pq]);
+        g4o_rope(qr + half, half, half / 2, theta, (double)pos2[pq + 1]);
+        for (int j = 0; j < n; ++j) {
+          const size_t koff = (((size_t)b * S + j) * Hkv + g) * (size_t)d;
+          const size_t pk = ((size_t)b * S + j) * 2;
+          for (int e = 0; e < d; ++e) kr[e] = g4o_in(k, dtype, koff + e);
+          g4o_rope(kr, half, half / 2, theta, (double)pos2[pk]);
+          g4o_rope(kr + half, half, half / 2, theta, (double)pos2[pk + 1]);
+          double s = 0.0;
+          for (int e = 0; e < d; ++e) s += qr[e] * kr[e];
+          sc[j] = s * scale;
+        }
+        double m = -INFINITY;
+        for (int j = 0; j < n; ++j) if (sc[j] > m) m = sc[j];
+        double l = 0.0;
+        for (int j = 0; j < n; ++j) { sc[j] = exp(sc[j] - m); l += sc[j]; }
+        for (int e = 0; e < d; ++e) o[e] = 0.0;
+        for (int j = 0; j < n; ++j) {
+          const size_t voff = (((size_t)b * S + j) * Hkv + g) * (size_t)d;
+          for (int e = 0; e < d; ++e) o[e] += sc[j] * g4o_in(v, dtype, voff + e);
+        }
+        for (int e = 0; e < d; ++e) o[e] /= l;
+      }
+    }
+    free(qr); free(kr); free(sc);
+  }
+  return err ? G4O_ENOMEM : G4O_OK;
+}

@@ -47,3 +47,37 @@ def attention(q, k, v, pos, window, theta, n_rot):
     w = np.exp(sc)
     w = w / w.sum(axis=-1, keepdims=True)
     return np.einsum("bhij,bjhd->bihd", w, vv)
+
+
+def vision_attention(q, k, v, pos2, theta, lengths=None):
+    """Bidirectional attention with 2D RoPE: half c of the head dims is an
+    ordinary RoPE of dim d/2 driven by position component c; keys past
+    lengths[b] are masked and those rows are zero.  pos2 [B,S,2]."""
+    B, S, Hq, d = q.shape
+    Hkv = k.shape[2]
+    G = Hq // Hkv
+    half = d // 2
+
+    def rot2(x):
+        y = np.empty_like(x)
+        y[..., :half] = rotate(x[..., :half], pos2[..., 0], theta, half // 2)
+        y[..., half:] = rotate(x[..., half:], pos2[..., 1], theta, half // 2)
+        return y
+
+    n = np.full(B, S) if lengths is None else np.clip(np.asarray(lengths), 0, S)
+    qr = rot2(np.nan_to_num(q))
+    kr = np.repeat(rot2(np.nan_to_num(k)), G, axis=2)
+    vv = np.repeat(np.nan_to_num(v), G, axis=2)
+    sc = np.einsum("bihd,bjhd->bhij", qr, kr) / np.sqrt(d)
+    valid = np.arange(S)[None, :] < n[:, None]  # [B, S] keys
+    sc = np.where(valid[:, None, None, :], sc, -np.inf)
+    out = np.zeros((B, S, Hq, d))
+    for b in range(B):
+        if n[b] == 0:
+            continue
+        s = sc[b, :, :n[b]]
+        s = s - s.max(axis=-1, keepdims=True)
+        w = np.exp(s)
+        w = w / w.sum(axis=-1, keepdims=True)
+        out[b, :n[b]] = np.einsum("hij,jhd->ihd", w[:, :n[b]], vv[b])
+    return out
