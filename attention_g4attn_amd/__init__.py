@@ -115,6 +115,26 @@ def global_prefill(q, kv, pos, window=0, theta=1e6, p=0.25, out=None, out_dtype=
     return out
 
 
+def vision_prefill(q, k, v, pos2, theta=1e4, lengths=None, out=None, out_dtype=None,
+                   workspace=None):
+    """Vision-encoder attention (g4attn_vision_prefill): every patch of an
+    image sees every valid patch of the image, with 2D RoPE driven by
+    pos2 [B, S, 2] = (w, h).  lengths [B] int32 (None: all S valid); rows of
+    padding patches are zero.  bf16 q, k, v with d = 256."""
+    _dev(q, k, v, pos2, lengths, out, workspace)
+    B, S, Hq, d = q.shape
+    Hkv = k.shape[2]
+    out = _out(q.shape, out, out_dtype, q.device)
+    workspace = _workspace(prefill_workspace_bytes(B, S, Hkv, d, 1.0, _code(q)), workspace,
+                           q.device)
+    rc = _g4lib().g4attn_vision_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(pos2),
+                                        _ptr(lengths), B, S, Hq, Hkv, d, float(theta), _code(q),
+                                        _code(out), _ptr(workspace), _nbytes(workspace),
+                                        _stream())
+    _check(rc, "g4attn_vision_prefill")
+    return out
+
+
 def decode_workspace_bytes(B, Hq, Hkv, d, capacity, window):
     return int(_g4lib().g4attn_decode_workspace_bytes(B, Hq, Hkv, d, capacity, window))
 

@@ -15,6 +15,7 @@ SIGNATURES = {
     "g4attn_prefill_workspace_bytes": ([I, I, I, I, F, I], Z),
     "g4attn_local_prefill": ([P, P, P, P, P, I, I, I, I, I, I, F, F, I, I, P, Z, P], I),
     "g4attn_global_prefill": ([P, P, P, P, I, I, I, I, I, I, F, F, I, I, P, Z, P], I),
+    "g4attn_vision_prefill": ([P, P, P, P, P, P, I, I, I, I, I, F, I, I, P, Z, P], I),
     "g4attn_decode": ([P, P, P, P, P, I, I, I, I, I, I, F, F, I, I, P, Z, P], I),
     "g4attn_decode_workspace_bytes": ([I, I, I, I, I, I], Z),
     "g4attn_decode_multi": ([P, P, P, P, P, I, I, I, I, I, I, I, F, F, I, I, P, Z, P], I),

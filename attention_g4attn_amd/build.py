@@ -15,7 +15,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libg4attn.so")
 BUILD = os.path.join(HERE, "_build")
-SOURCES = ["api.cpp", "prefill_kv512.hip", "prefill_d256.hip", "prefill_sep512.hip",
+SOURCES = ["api.cpp", "prefill_kv512.hip", "prefill_d256.hip", "prefill_sep512.hip", "prefill_vis.hip",
            "decode_bf16.hip", "decode_fp8.hip", "attn_f32.hip", "cache_fill.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

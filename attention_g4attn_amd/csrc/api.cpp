@@ -118,6 +118,46 @@ G4A_API int g4attn_global_prefill(const void* q, const void* kv, void* out, cons
                  workspace, workspace_bytes, stream, true);
 }
 
+G4A_API int g4attn_vision_prefill(const void* q, const void* k, const void* v, void* out,
+                                  const int32_t* pos2, const int32_t* lengths, int B, int S,
+                                  int Hq, int Hkv, int d, float theta, int in_dtype,
+                                  int out_dtype, void* workspace, size_t workspace_bytes,
+                                  void* stream) {
+  if (B < 0 || S < 0) return G4A_EINVAL;
+  int rc = check_common(Hq, Hkv, d, 0, theta, 1.f, in_dtype, out_dtype);
+  if (rc) return rc;
+  if (in_dtype != G4A_BF16 || d != 256) return G4A_EUNSUPPORTED;
+  if (B == 0 || S == 0) return G4A_OK;
+  if (!q || !k || !v || !out || !pos2) return G4A_EINVAL;
+  if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(out) || misaligned(pos2) ||
+      (lengths && misaligned(lengths)))
+    return G4A_EALIGN;
+  if ((double)B * S * Hq * d > 9.0e18 || (double)B * S * Hkv > 2.0e9) return G4A_EINVAL;
+  g4a::PrefillArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.out = out;
+  a.pos = pos2;
+  a.lengths = lengths;
+  a.B = B;
+  a.S = S;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.D = d;
+  a.window = 0;
+  a.n_rot = d / 2;  // every pair of both halves turns
+  a.log2_theta = log2((double)theta);
+  a.scale = (float)(1.0 / sqrt((double)d));
+  a.scale_log2e = (float)(1.4426950408889634 / sqrt((double)d));
+  const size_t need = prefill_ws_bytes(B, S, Hkv, d, a.n_rot, in_dtype);
+  if (!workspace || workspace_bytes < need) return G4A_EWORKSPACE;
+  if (misaligned(workspace)) return G4A_EALIGN;
+  a.ws = workspace;
+  return finish(g4a::launch_vision_prefill(a, out_dtype == G4A_BF16,
+                                           static_cast<hipStream_t>(stream)));
+}
+
 namespace {
 
 // Ring rule: plain decode keeps capacity == window; several query tokens need

@@ -19,6 +19,9 @@ struct PrefillArgs {
   float scale_log2e;  // log2(e) / sqrt(D)
   float scale;        // 1 / sqrt(D)
   int nq, nheads;     // filled in by the launcher
+  // vision attention only: pos is [B, S, 2] (w, h) and lengths [B] the valid
+  // patches of each image (null: all S)
+  const int32_t* lengths;
 };
 
 // Decode of q_len query tokens per sequence: q, out [B, q_len, Hq, D]; pos[b]
@@ -72,6 +75,8 @@ hipError_t launch_prefill_kv512(const PrefillArgs& a, bool out_bf16, hipStream_t
 hipError_t launch_prefill_d256(const PrefillArgs& a, bool kv_shared, bool out_bf16,
                                hipStream_t st);
 hipError_t launch_prefill_sep512(const PrefillArgs& a, bool out_bf16, hipStream_t st);
+// vision-encoder attention (2D RoPE, no causal mask): bf16, D = 256, separate K/V
+hipError_t launch_vision_prefill(const PrefillArgs& a, bool out_bf16, hipStream_t st);
 // f32 inputs, fp32 vector path; D in {64, 128, 256, 512}, G in {1, 2, 4, 8}
 hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t st);
 

@@ -36,6 +36,11 @@
 //   - A wave skips tiles none of its rows can see; only edge tiles are
 //     masked.  Grid order: KV heads fastest, then query tiles from the longest
 //     causal row down, so each XCD streams one KV head's tiles in step.
+//   - VIS instances compute the vision encoder's attention instead: 2D RoPE
+//     (half c of the head dims is a RoPE of dim d/2 driven by component c of
+//     the patch position (w, h)) and no causal mask, every patch of an image
+//     seeing the image's first lengths[b] patches ("Guia visual do Gemma 4",
+//     sections "Encoder de visao" and "Suporte a proporcao variavel").
 #pragma once
 #include <type_traits>
 
@@ -145,10 +150,21 @@ __device__ __forceinline__ T& lds_at(unsigned char* base, int off) {
   return *reinterpret_cast<T*>(base + off);
 }
 
+// Revolutions per unit of position of pair t: theta^(-2t/D) / (2 pi); for
+// the 2D rotation of the vision encoder, pair t of half t / (D/4) at
+// frequency index t % (D/4) of a RoPE of dim D/2.
+template <bool VIS>
+__device__ __forceinline__ double pair_rev(int t, int D, double log2_theta) {
+  if constexpr (VIS) return rope_rev_per_pos(t % (D / 4), D / 2, log2_theta);
+  else return rope_rev_per_pos(t, D, log2_theta);
+}
+
 // Rotated key slab, one pass over the keys: ws[row][0 .. SW) = the first SW
 // dims of k[row] with pair t < n_rot turned by pos * theta^(-2t/D), rounded to
 // bf16; row = (b*S + j)*Hkv + hkv.  One 16-byte chunk (4 pairs) per thread.
-template <int SW>
+// VIS: pos is [B*S, 2] and the pairs of the chunk (all in one half) turn by
+// the component of their half.
+template <int SW, bool VIS = false>
 __global__ void __launch_bounds__(256) rope_keys_kernel(const uint16_t* __restrict__ k,
                                                        uint16_t* __restrict__ ws,
                                                        const int32_t* __restrict__ pos,
@@ -161,12 +177,12 @@ __global__ void __launch_bounds__(256) rope_keys_kernel(const uint16_t* __restri
     const int c = (int)(i % CPR);
     u32x4 x = *reinterpret_cast<const u32x4*>(k + row * D + 8 * c);
     if (4 * c < n_rot) {
-      const int p = pos[row / Hkv];
+      const int p = VIS ? pos[(row / Hkv) * 2 + (4 * c >= D / 4)] : pos[row / Hkv];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int t = 4 * c + e;
         float cs, sn;
-        rope_cs_accurate(p, rope_rev_per_pos(t, D, log2_theta), cs, sn);
+        rope_cs_accurate(p, pair_rev<VIS>(t, D, log2_theta), cs, sn);
         const float x0 = bf_lo(x[e]), x1 = bf_hi(x[e]);
         const uint32_t r = pack_bf16(x0 * cs - x1 * sn, x0 * sn + x1 * cs);
         x[e] = t < n_rot ? r : x[e];
@@ -180,15 +196,20 @@ __global__ void __launch_bounds__(256) rope_keys_kernel(const uint16_t* __restri
 // (base-2 scaled) known in advance, so no rescaling is needed.  Lane e owns
 // dims e*(D/64) .. +D/64-1; every key's score is a wave-wide reduction.
 // Keys are read raw and rotated here.
-template <int D, bool OBF>
+// VIS: keys 0 .. nv-1 (no causal mask), positions per half from pos [B*S, 2].
+template <int D, bool OBF, bool VIS = false>
 __device__ __noinline__ void exact_row(const uint16_t* qp, const uint16_t* kp, const uint16_t* vp,
                                        void* outp, const int32_t* posp, int S, int Hq, int Hkv,
                                        int W, int n_rot, float scale_log2e, int b, int hkv, int t,
-                                       int h, float m, const double* gtab) {
+                                       int h, float m, const double* gtab, int nv = 0) {
   constexpr int E = D / 64;  // dims per lane, even
   const int lane = threadIdx.x & 63;
   const uint16_t* qr = qp + (((size_t)b * S + t) * Hq + h) * D;
-  const int qpos = posp[(size_t)b * S + t];
+  // position of pair d0/2 of token j
+  auto ppos = [&](int j, int d0) {
+    if constexpr (VIS) return posp[((size_t)b * S + j) * 2 + (d0 >= D / 2)];
+    else return posp[(size_t)b * S + j];
+  };
   float qv[E];
 #pragma unroll
   for (int e = 0; e < E; e += 2) {
@@ -196,7 +217,7 @@ __device__ __noinline__ void exact_row(const uint16_t* qp, const uint16_t* kp, c
     float x0 = bf_lo(qr[d0]), x1 = bf_lo(qr[d0 + 1]);
     if (d0 / 2 < n_rot) {
       float c, s;
-      rope_cs_accurate(qpos, gtab[d0 / 2], c, s);
+      rope_cs_accurate(ppos(t, d0), gtab[d0 / 2], c, s);
       const float y0 = x0 * c - x1 * s, y1 = x0 * s + x1 * c;
       x0 = y0;
       x1 = y1;
@@ -207,12 +228,12 @@ __device__ __noinline__ void exact_row(const uint16_t* qp, const uint16_t* kp, c
   float o[E], l = 0.f;
 #pragma unroll
   for (int e = 0; e < E; ++e) o[e] = 0.f;
-  const int lo = W > 0 ? max(0, t - W + 1) : 0;
-  for (int j = lo; j <= t; ++j) {
+  const int lo = VIS ? 0 : (W > 0 ? max(0, t - W + 1) : 0);
+  const int hi = VIS ? nv - 1 : t;
+  for (int j = lo; j <= hi; ++j) {
     const size_t row = ((size_t)b * S + j) * Hkv + hkv;
     const uint16_t* kr = kp + row * D;
     const uint16_t* vr = vp + row * D;
-    const int kpos = posp[(size_t)b * S + j];
     float part = 0.f;
 #pragma unroll
     for (int e = 0; e < E; e += 2) {
@@ -220,7 +241,7 @@ __device__ __noinline__ void exact_row(const uint16_t* qp, const uint16_t* kp, c
       float x0 = bf_lo(kr[d0]), x1 = bf_lo(kr[d0 + 1]);
       if (d0 / 2 < n_rot) {
         float c, s;
-        rope_cs_accurate(kpos, gtab[d0 / 2], c, s);
+        rope_cs_accurate(ppos(j, d0), gtab[d0 / 2], c, s);
         const float y0 = x0 * c - x1 * s, y1 = x0 * s + x1 * c;
         x0 = y0;
         x1 = y1;
@@ -251,7 +272,7 @@ __device__ __noinline__ void exact_row(const uint16_t* qp, const uint16_t* kp, c
 // products of tile kt instead of all at once before them.  Every wave must then
 // compute every tile that holds a visible key for any wave of the workgroup,
 // which holds without a window when a workgroup's tokens fit in one tile.
-template <int D, int G, bool KVS, bool OBF, int SW, int NST, int MB, bool SPREAD>
+template <int D, int G, bool KVS, bool OBF, int SW, int NST, int MB, bool SPREAD, bool VIS>
 __global__ void __launch_bounds__(NW * 64, 1) prefill_kernel(PrefillArgs a) {
   constexpr int RW = 32 * MB;          // rows per wave
   constexpr int M = NW * RW;           // rows per workgroup
@@ -265,6 +286,7 @@ __global__ void __launch_bounds__(NW * 64, 1) prefill_kernel(PrefillArgs a) {
   static_assert(L::STAGE % (1024 * NW) == 0, "stage = whole direct loads per wave");
   static_assert(NST == 2 || NST == 3, "ring");
   static_assert(!SPREAD || (NST == 3 && TQ <= BN), "spread loads need the 3-deep ring and TQ <= BN");
+  static_assert(!VIS || (!SPREAD && SW == D && D % 64 == 0), "vision: full slab, halves of whole chunks");
   // With two query blocks per wave the score and output accumulators leave
   // few registers: the lane parts of LDS offsets are then recomputed per tile
   // from an opaque copy of the lane id instead of staying live across the
@@ -294,8 +316,11 @@ __global__ void __launch_bounds__(NW * 64, 1) prefill_kernel(PrefillArgs a) {
   const int t0 = qt * TQ;
   const int t_end = min(t0 + TQ, S);
 
-  for (int t = tid; t < D / 2; t += NW * 64) gtab[t] = rope_rev_per_pos(t, D, a.log2_theta);
+  for (int t = tid; t < D / 2; t += NW * 64) gtab[t] = pair_rev<VIS>(t, D, a.log2_theta);
   __syncthreads();
+  // vision: the image's valid patches (keys past them are not attended to)
+  int nv = S;
+  if constexpr (VIS) nv = a.lengths ? min(max(a.lengths[b], 0), S) : S;
 
   // ---- query rows of this lane (one per block), rotated, as B operands ----
   int tq[MB], hq[MB];
@@ -308,7 +333,9 @@ __global__ void __launch_bounds__(NW * 64, 1) prefill_kernel(PrefillArgs a) {
     hq[mb] = hkv * G + row % G;
     row_ok[mb] = tq[mb] < S;
     const int tqc = row_ok[mb] ? tq[mb] : S - 1;
-    const int qpos = a.pos[(size_t)b * S + tqc];
+    // VIS: component 0 (w) for the first half of the dims, 1 (h) for the second
+    const int qpos = VIS ? a.pos[((size_t)b * S + tqc) * 2] : a.pos[(size_t)b * S + tqc];
+    const int qpos1 = VIS ? a.pos[((size_t)b * S + tqc) * 2 + 1] : qpos;
     const uint16_t* qrow =
         static_cast<const uint16_t*>(a.q) + (((size_t)b * S + tqc) * a.Hq + hq[mb]) * D;
 #pragma unroll
@@ -317,16 +344,18 @@ __global__ void __launch_bounds__(NW * 64, 1) prefill_kernel(PrefillArgs a) {
       qf[mb][s] = row_ok[mb] ? x : u32x4{0, 0, 0, 0};
     }
 #pragma unroll
-    for (int s = 0; s < NSS; ++s)
-      if (8 * s < n_rot) qf[mb][s] = rotate_chunk_bf16(qf[mb][s], 2 * s + hl, qpos, n_rot, gtab);
+    for (int s = 0; s < NSS; ++s)  // chunk 2s + hl lies in the second half iff s >= D/32
+      if (8 * s < n_rot)
+        qf[mb][s] = rotate_chunk_bf16(qf[mb][s], 2 * s + hl, (VIS && s >= D / 32) ? qpos1 : qpos,
+                                      n_rot, gtab);
   }
 
   // token span of this wave's rows
   const int tw0 = t0 + (RW * w) / G;
   const int tw1 = min(t0 + (RW * w + RW - 1) / G, S - 1);
-  const bool wave_ok = tw0 < S;
-  const int klo = W > 0 ? max(0, t0 - W + 1) : 0;
-  const int kt0 = klo / BN, kt1 = (t_end - 1) / BN;
+  const bool wave_ok = tw0 < (VIS ? nv : S);  // vision: waves of padding rows only skip
+  const int klo = (!VIS && W > 0) ? max(0, t0 - W + 1) : 0;
+  const int kt0 = klo / BN, kt1 = VIS ? (nv - 1) / BN : (t_end - 1) / BN;
 
   // ---- direct HBM -> LDS loads of one tile ----
   // Per tile a buffer resource covers the rows kv0 .. kv0+rows-1 of this KV
@@ -460,6 +489,18 @@ __global__ void __launch_bounds__(NW * 64, 1) prefill_kernel(PrefillArgs a) {
   // ---- causal / band mask of tile kt (edge tiles only) ----
   auto mask = [&](int kt, f32x16 (&sacc)[MB]) {
     const int kv0 = kt * BN;
+    if constexpr (VIS) {  // keys past the image's patches only
+      if (kv0 + BN > nv) {
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int j = kv0 + 8 * (r >> 2) + 4 * hl + (r & 3);
+            sacc[mb][r] = j < nv ? sacc[mb][r] : -INFINITY;
+          }
+      }
+      return;
+    }
     const bool need_mask = (kv0 + BN - 1 > tw0) || (W > 0 && kv0 <= tw1 - W);
     if (need_mask) {  // wave-uniform
 #pragma unroll
@@ -577,8 +618,20 @@ __global__ void __launch_bounds__(NW * 64, 1) prefill_kernel(PrefillArgs a) {
   // token, before its window, or padding)
   auto visible = [&](int kt) {
     const int kv0 = kt * BN;
+    if constexpr (VIS) return wave_ok && kv0 < nv;
     return (SPREAD || wave_ok) && kv0 <= tw1 && !(W > 0 && kv0 + BN - 1 <= tw0 - W);
   };
+  // vision: an image with no valid patch has only zero rows (and no tile to load)
+  if (VIS && nv == 0) {
+    for (int idx = tid; idx < M * D / 4; idx += NW * 64) {
+      const int r = idx / (D / 4), tk = t0 + r / G;
+      if (tk >= S) continue;
+      const size_t o = (((size_t)b * S + tk) * a.Hq + hkv * G + r % G) * D + 4 * (idx % (D / 4));
+      if constexpr (OBF) *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.out) + o) = u32x2{0, 0};
+      else *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + o) = f32x4{};
+    }
+    return;
+  }
 
   // ---- KV loop, unrolled by the ring depth so every stage is a fixed object ----
   // The tile count is padded up to a multiple of the ring depth; padding tiles
@@ -631,12 +684,12 @@ __global__ void __launch_bounds__(NW * 64, 1) prefill_kernel(PrefillArgs a) {
     }
   }
 
-  // ---- epilogue: O / l ----
+  // ---- epilogue: O / l (vision: padding rows are zero) ----
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
     const float lt = l_run[mb] + __shfl_xor(l_run[mb], 32);
     if (!row_ok[mb] || ((ovf >> mb) & 1)) continue;
-    const float inv = 1.f / lt;
+    const float inv = (VIS && tq[mb] >= nv) ? 0.f : 1.f / lt;
     const size_t obase = (((size_t)b * S + tq[mb]) * a.Hq + hq[mb]) * D;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
@@ -668,16 +721,18 @@ __global__ void __launch_bounds__(NW * 64, 1) prefill_kernel(PrefillArgs a) {
         rows &= rows - 1;
         const int t = __shfl(tq[mb], src_lane), h = __shfl(hq[mb], src_lane);
         const float mref = __shfl(m_seen[mb], src_lane);
-        exact_row<D, OBF>(static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
-                          static_cast<const uint16_t*>(a.v), a.out, a.pos, S, a.Hq, a.Hkv, W,
-                          n_rot, cs, b, hkv, t, h, mref, gtab);
+        exact_row<D, OBF, VIS>(static_cast<const uint16_t*>(a.q),
+                               static_cast<const uint16_t*>(a.k),
+                               static_cast<const uint16_t*>(a.v), a.out, a.pos, S, a.Hq, a.Hkv,
+                               W, n_rot, cs, b, hkv, t, h, mref, gtab, nv);
       }
     }
   }
 }
 
 // Rotated key slab for slab width SW, then the attention kernel, on stream st.
-template <int D, int G, bool KVS, bool OBF, int SW, int NST, int MB, bool SPREAD = false>
+template <int D, int G, bool KVS, bool OBF, int SW, int NST, int MB, bool SPREAD = false,
+          bool VIS = false>
 hipError_t launch(const PrefillArgs& a, hipStream_t st) {
   constexpr int TQ = NW * 32 * MB / G;
   PrefillArgs x = a;
@@ -688,12 +743,12 @@ hipError_t launch(const PrefillArgs& a, hipStream_t st) {
   if (nblk > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   const long long nchunks = (long long)a.B * a.S * a.Hkv * (SW / 8);
   const long long rblk = (nchunks + 255) / 256;
-  hipLaunchKernelGGL((rope_keys_kernel<SW>), dim3((unsigned)(rblk < 65536 ? rblk : 65536)),
+  hipLaunchKernelGGL((rope_keys_kernel<SW, VIS>), dim3((unsigned)(rblk < 65536 ? rblk : 65536)),
                      dim3(256), 0, st, static_cast<const uint16_t*>(a.k),
                      static_cast<uint16_t*>(a.ws), a.pos, nchunks, a.Hkv, D, a.n_rot,
                      a.log2_theta);
   if (SPREAD && a.window != 0) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((prefill_kernel<D, G, KVS, OBF, SW, NST, MB, SPREAD>), dim3((unsigned)nblk),
+  hipLaunchKernelGGL((prefill_kernel<D, G, KVS, OBF, SW, NST, MB, SPREAD, VIS>), dim3((unsigned)nblk),
                      dim3(NW * 64), 0, st, x);
   return hipGetLastError();
 }

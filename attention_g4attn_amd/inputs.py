@@ -161,3 +161,53 @@ def decode_inputs_fp8(layer: DecodeLayer, workload, index, device, lengths=None,
     vs = None if v is None else kv_scales(layer.Hkv, seed(workload, index, 5), device)
     pos = (lengths - 1).to(torch.int32).to(device)
     return q, k, v, ks, vs, pos, lengths
+
+
+# Vision encoder: images as grids of 16x16-pixel patches, at most 9 x budget
+# patches for a soft-token budget of 70 .. 1120 ("Guia visual do Gemma 4",
+# sections "Encoder de visao" and "Suporte a resolucao variavel").  The pages
+# give no head geometry for the encoder: 8 heads of dim 256 (MHA).
+@dataclass(frozen=True)
+class VisionLayer:
+    grids: tuple  # (w, h) patch grid of each image; S = the largest w*h
+    Hq: int = 8
+    Hkv: int = 8
+    d: int = 256
+    theta: float = LOCAL_THETA
+
+    @property
+    def B(self):
+        return len(self.grids)
+
+    @property
+    def S(self):
+        return max(w * h for w, h in self.grids)
+
+
+VISION_280 = VisionLayer(((60, 42), (42, 60), (56, 45), (48, 52)))  # budget 280: <= 2520 patches
+VISION_1120 = VisionLayer(((120, 84),))                              # budget 1120: 10080 patches
+
+
+def vision_positions(layer: VisionLayer, device):
+    """pos2 [B, S, 2] int32 = (w, h) of each patch in raster order (rows of
+    the grid one after the other), zeros past an image's patches; lengths [B]."""
+    B, S = layer.B, layer.S
+    pos = torch.zeros((B, S, 2), dtype=torch.int32)
+    lengths = torch.empty(B, dtype=torch.int32)
+    for b, (w, h) in enumerate(layer.grids):
+        n = w * h
+        i = torch.arange(n, dtype=torch.int32)
+        pos[b, :n, 0] = i % w
+        pos[b, :n, 1] = i // w
+        lengths[b] = n
+    return pos.to(device), lengths.to(device)
+
+
+def vision_inputs(layer: VisionLayer, workload, dtype, device):
+    """q [B,S,Hq,d], k, v [B,S,Hkv,d], pos2 [B,S,2], lengths [B]."""
+    B, S = layer.B, layer.S
+    q = randn((B, S, layer.Hq, layer.d), seed(workload, 0, 1), dtype, device)
+    k = randn((B, S, layer.Hkv, layer.d), seed(workload, 0, 2), dtype, device)
+    v = randn((B, S, layer.Hkv, layer.d), seed(workload, 0, 3), dtype, device)
+    pos2, lengths = vision_positions(layer, device)
+    return q, k, v, pos2, lengths

@@ -114,6 +114,32 @@ int g4attn_global_prefill(const void* q, const void* kv, void* out, const int32_
                           void* stream);
 
 /*
+ * Vision-encoder attention: every patch of an image attends to every patch
+ * of the image (no causal mask), with 2D RoPE.  The encoder turns an image
+ * into 16x16-pixel patches; 2D RoPE splits the embedding in two parts that
+ * encode the horizontal (w) and vertical (h) positions separately ("Guia
+ * visual do Gemma 4", sections "Encoder de visao" and "Suporte a proporcao
+ * variavel").  Here half c of the head dims ([0, d/2) for c = 0, [d/2, d) for
+ * c = 1) is an ordinary RoPE of a head of dim d/2, pair t = dims (2t, 2t+1)
+ * of the half turning by pos2[..., c] * theta^(-2t/(d/2)); component 0 is w,
+ * component 1 is h.
+ *   q    [B, S, Hq, d]  bf16          k, v [B, S, Hkv, d]  bf16
+ *   out  [B, S, Hq, d]  out_dtype     pos2 [B, S, 2] int32 (w, h) per patch
+ *   lengths [B] int32, or NULL (every image has S patches): image b has
+ *        lengths[b] valid patches (clamped to [0, S]); patches past them are
+ *        not attended to and their output rows are zero.
+ *   theta: rotary base of each half.
+ *   d = 256, G in {1, 2, 4, 8}, in_dtype G4A_BF16 (others: G4A_EUNSUPPORTED).
+ *   workspace: g4attn_prefill_workspace_bytes(B, S, Hkv, d, 1.0, G4A_BF16)
+ *        bytes (the rotated keys).
+ * Returns G4A_OK or a negative status; out is written in full.
+ */
+int g4attn_vision_prefill(const void* q, const void* k, const void* v, void* out,
+                          const int32_t* pos2, const int32_t* lengths, int B, int S, int Hq,
+                          int Hkv, int d, float theta, int in_dtype, int out_dtype,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Decode: one query token per sequence against a cache of raw (unrotated)
  * keys and values; the rotation of every cached key is applied on the fly at
  * the position that key holds.

@@ -240,3 +240,27 @@ def test_fill_cache_fp8_validation(kw, code):
 
 def test_fill_cache_fp8_empty_is_noop():
     assert fill8(S=0, k=None, v=None, ks=None, vs=None, pos=None, kc=None, vc=None) == 0
+
+
+def vis(**kw):
+    args = dict(q=A, k=2 * A, v=3 * A, out=4 * A, pos=5 * A, ln=6 * A, B=2, S=100, Hq=8, Hkv=8,
+                d=256, theta=1e4, i=1, o=0, ws=7 * A, ws_bytes=1 << 40, stream=None)
+    args.update(kw)
+    return L.lib().g4attn_vision_prefill(*args.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), -1), (dict(v=None), -1), (dict(pos=None), -1), (dict(out=None), -1),
+    (dict(B=-1), -1), (dict(Hq=12), -1), (dict(theta=0.0), -1), (dict(o=5), -1),
+    (dict(d=512), -2), (dict(d=128), -2), (dict(i=0, o=0), -2), (dict(Hq=24, Hkv=2), -2),
+    (dict(ws=None), -4), (dict(ws_bytes=1000), -4),
+    (dict(ln=6 * A + 4), -3), (dict(pos=5 * A + 8), -3),
+])
+def test_vision_prefill_validation(kw, code):
+    assert vis(**kw) == code
+
+
+def test_vision_prefill_lengths_may_be_null_and_empty_is_noop():
+    assert vis(ln=None, ws_bytes=1000) == -4  # passes the other checks
+    assert vis(S=0, q=None, k=None, v=None, out=None, pos=None, ln=None, ws=None) == 0
+    assert vis(B=0, q=None, k=None, v=None, out=None, pos=None, ln=None, ws=None) == 0
