@@ -188,6 +188,7 @@ def main():
     nxt = {} if args.no_configs else time_next(g4, inputs, torch)
     if not args.no_configs:
         nxt["fp8"] = time_fp8(g4, inputs, torch)
+        nxt["vision"] = time_vision(g4, inputs, torch)
 
     fl_loc, fl_glo = prefill_flops(loc), prefill_flops(glo)
     (fdl, bdl), (fdg, bdg) = decode_cost(dloc, lengths), decode_cost(dglo, lengths)
@@ -427,6 +428,27 @@ def time_fp8(g4, inputs, torch, reps=8):
     res["fill_cache_fp8_global_s262144"] = {"us": ms * 1e3, "GBps": byts / ms / 1e6,
                                             "frac_hbm": byts / ms / 1e6 / HBM_PEAK_GBS}
     del k, p, kc
+    return res
+
+
+def time_vision(g4, inputs, torch, reps=5):
+    """Vision-encoder attention (2D RoPE, no causal mask) at the budget-280
+    batch (4 images up to 2520 patches) and one budget-1120 image (10080
+    patches).  FLOPs count 4*d per (valid query, valid key) pair per head."""
+    res = {}
+    for name, layer in (("budget280_b4", inputs.VISION_280), ("budget1120_b1", inputs.VISION_1120)):
+        q, k, v, pos2, lengths = inputs.vision_inputs(layer, 9, torch.bfloat16, "cuda")
+        out = torch.empty(q.shape, dtype=torch.float32, device="cuda")
+        ws = torch.empty(g4.prefill_workspace_bytes(layer.B, layer.S, layer.Hkv, layer.d, 1.0),
+                         dtype=torch.uint8, device="cuda")
+        ms = _event_time(torch, lambda r: g4.vision_prefill(q, k, v, pos2, layer.theta,
+                                                            lengths=lengths, out=out,
+                                                            workspace=ws), reps)
+        flops = sum((w * h) ** 2 for w, h in layer.grids) * layer.Hq * 4 * layer.d
+        res[name] = {"ms": ms, "tflops": flops / ms / 1e9,
+                     "frac_mfma": flops / ms / 1e9 / MFMA_BF16_PEAK_TFLOPS,
+                     "patches": [w * h for w, h in layer.grids]}
+        del q, k, v, pos2, lengths, out, ws
     return res
 
 
