@@ -19,7 +19,8 @@ import statistics
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 KERNEL_SOURCES = ["attention_g4attn_amd/csrc/prefill.hpp", "attention_g4attn_amd/csrc/common.hpp",
                   "attention_g4attn_amd/csrc/prefill_kv512.hip"]
-DECODE_SOURCES = ["attention_g4attn_amd/csrc/decode_bf16.hip", "attention_g4attn_amd/csrc/common.hpp"]
+DECODE_SOURCES = ["attention_g4attn_amd/csrc/decode_bf16.hip", "attention_g4attn_amd/csrc/decode_common.hpp",
+                  "attention_g4attn_amd/csrc/common.hpp"]
 
 
 def source_hash(files=KERNEL_SOURCES):

@@ -227,7 +227,7 @@ def main():
         roof = {"bound": "mfma", "achieved": ach, "peak": MFMA_BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": ach / MFMA_BF16_PEAK_TFLOPS,
                 "traffic": measured_traffic() if S == inputs.GROUP_S else None,
-                "kernel": "g4a::pf::prefill_kernel<512, 8, true, false, 128, 3, 1, true>",
+                "kernel": "g4a::pf::prefill_kernel<512, 8, true, false, 128, 3, 1, true, false>",
                 "flops_per_launch": fl_glo, "ms_per_launch": t}
     roof_dec = None
     if run_decode:
