@@ -69,6 +69,38 @@ __device__ __forceinline__ u32x4 widen8(uint32_t w0, uint32_t w1) {
   return r;
 }
 
+// Pairs 4c .. 4c+3 of the two keys a lane holds in a score product, from 8
+// codes each (bytes of a0 then a1, b0 then b1): widened to fp32 (exact), pair
+// t < n_rot turned (ALL: every pair), packed to bf16 (round to nearest even).
+// Key a sits at position pos, key b at pos + delta, where dtab[t] = (cos,
+// sin) of pair t's angle for delta: key b's angles follow from key a's by
+// angle addition, with no second reduction or sine.
+template <bool ALL>
+__device__ __forceinline__ void widen_rotate8x2(uint32_t a0, uint32_t a1, uint32_t b0, uint32_t b1,
+                                                int c, int pos, int n_rot, const double* gtab,
+                                                const f32x2* dtab, u32x4& ya, u32x4& yb) {
+  const f32x2 xa[4] = {__builtin_amdgcn_cvt_pk_f32_fp8(a0, false),
+                       __builtin_amdgcn_cvt_pk_f32_fp8(a0, true),
+                       __builtin_amdgcn_cvt_pk_f32_fp8(a1, false),
+                       __builtin_amdgcn_cvt_pk_f32_fp8(a1, true)};
+  const f32x2 xb[4] = {__builtin_amdgcn_cvt_pk_f32_fp8(b0, false),
+                       __builtin_amdgcn_cvt_pk_f32_fp8(b0, true),
+                       __builtin_amdgcn_cvt_pk_f32_fp8(b1, false),
+                       __builtin_amdgcn_cvt_pk_f32_fp8(b1, true)};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int t = 4 * c + i;
+    float cs, sn;
+    rope_cs_fast(pos, gtab[t], cs, sn);
+    const f32x2 d = dtab[t];
+    const float cs1 = cs * d[0] - sn * d[1], sn1 = sn * d[0] + cs * d[1];
+    const uint32_t ra = pack_bf16(xa[i][0] * cs - xa[i][1] * sn, xa[i][0] * sn + xa[i][1] * cs);
+    const uint32_t rb = pack_bf16(xb[i][0] * cs1 - xb[i][1] * sn1, xb[i][0] * sn1 + xb[i][1] * cs1);
+    ya[i] = (ALL || t < n_rot) ? ra : pack_bf16(xa[i][0], xa[i][1]);
+    yb[i] = (ALL || t < n_rot) ? rb : pack_bf16(xb[i][0], xb[i][1]);
+  }
+}
+
 // 8-bit transpose read: within each 16-lane group, the lanes' 8-byte segments
 // form an 8 x 16 byte matrix (lane n holds row n/2, bytes 8*(n%2) .. +7), and
 // lane n receives column n (byte k from row k).
@@ -81,8 +113,9 @@ __device__ __forceinline__ u32x2 lds_read_tr8(const unsigned char* p) {
 // 2u + 1 share the 16 dims 64u + 16gq .. +15, low half first
 __device__ __forceinline__ int kchunk(int s, int gq) { return 8 * (s >> 1) + 2 * gq + (s & 1); }
 
-// RK = score k-steps that may hold turning pairs (4 when n_rot <= 64).
-template <int D, int G, bool KVS, int RK, bool OBF>
+// RK = score k-steps that may hold turning pairs (4 when n_rot <= 64); ALL:
+// every pair of those k-steps turns (n_rot = 64, or n_rot = D/2).
+template <int D, int G, bool KVS, int RK, bool ALL, bool OBF>
 __global__ void __launch_bounds__(64 * NW8) __attribute__((amdgpu_waves_per_eu(2, 2)))
 decode_fp8_kernel(DecodeArgs a) {
   constexpr int NW = NW8;
@@ -95,6 +128,9 @@ decode_fp8_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char tk[NW * KB];            // K (or K=V) tiles
   __shared__ __attribute__((aligned(16))) unsigned char tv[KVS ? 16 : NW * KB];  // V tiles
   __shared__ double gtab[D / 2];
+  // (cos, sin) of pair t's angle for a position step of 4, and of 4 - C (a
+  // ring's wrap between a lane's two keys)
+  __shared__ f32x2 dtab4[D / 2], dtab4c[D / 2];
   __shared__ float mls[NW][16][2];
   __shared__ int tnext;  // next unclaimed tile of the chunk
 
@@ -160,7 +196,15 @@ decode_fp8_kernel(DecodeArgs a) {
     }
   };
 
-  for (int t = threadIdx.x; t < D / 2; t += 64 * NW) gtab[t] = rope_rev_per_pos(t, D, a.log2_theta);
+  for (int t = threadIdx.x; t < D / 2; t += 64 * NW) {
+    const double g = rope_rev_per_pos(t, D, a.log2_theta);
+    gtab[t] = g;
+    float c4, s4, cw, sw;
+    rope_cs_fast(4, g, c4, s4);
+    rope_cs_fast(4 - C, g, cw, sw);
+    dtab4[t] = f32x2{c4, s4};
+    dtab4c[t] = f32x2{cw, sw};
+  }
   if (threadIdx.x == 0) tnext = NW;
   __syncthreads();
   auto claim = [&]() -> int {
@@ -195,11 +239,14 @@ decode_fp8_kernel(DecodeArgs a) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int kr = 8 * (row >> 2) + 4 * h + (row & 3);  // tile row of operand row `row`
-      const int r = min(rr0 + kr, r1 - 1);               // rows past the end are masked
-      tpos[h] = W > 0 ? P - (P - r) % C : r;
+      // rows past the end are masked (and read as zeros): a linear cache
+      // keeps their row as the position, a ring clamps them to the last row
+      tpos[h] = W > 0 ? P - (P - min(rr0 + kr, r1 - 1)) % C : rr0 + kr;
       base[h] = kr * D;
       sw[h] = fswz(kr);
     }
+    // key h = 1 sits 4 positions after key h = 0, or 4 - C across a ring's wrap
+    const f32x2* dtab = (W > 0 && tpos[1] - tpos[0] == 4 - C) ? dtab4c : dtab4;
     f32x4 acc[2] = {};
 #pragma unroll
     for (int u2 = 0; u2 < NS / 2; ++u2) {
@@ -208,12 +255,17 @@ decode_fp8_kernel(DecodeArgs a) {
       for (int h = 0; h < 2; ++h) raw[h] = lds_at<u32x4>(kt, base[h] + (((4 * u2 + gq) ^ sw[h]) << 4));
 #pragma unroll
       for (int e = 0; e < 2; ++e) {  // k-step 2*u2 + e: codes 8e .. 8e+7 of the read
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          u32x4 kf = widen8(raw[h][2 * e], raw[h][2 * e + 1]);
-          if (2 * u2 + e < RK) kf = rotate_chunk_bf16(kf, kchunk(2 * u2 + e, gq), tpos[h], n_rot, gtab);
-          acc[h] = mfma16x16x32(kf, qf[2 * u2 + e], acc[h]);
+        u32x4 k0, k1;
+        if (2 * u2 + e < RK) {
+          widen_rotate8x2<ALL>(raw[0][2 * e], raw[0][2 * e + 1], raw[1][2 * e],
+                               raw[1][2 * e + 1], kchunk(2 * u2 + e, gq), tpos[0], n_rot, gtab,
+                               dtab, k0, k1);
+        } else {
+          k0 = widen8(raw[0][2 * e], raw[0][2 * e + 1]);
+          k1 = widen8(raw[1][2 * e], raw[1][2 * e + 1]);
         }
+        acc[0] = mfma16x16x32(k0, qf[2 * u2 + e], acc[0]);
+        acc[1] = mfma16x16x32(k1, qf[2 * u2 + e], acc[1]);
       }
     }
     s0 = acc[0];
@@ -325,12 +377,15 @@ template <int D, int G, bool KVS, bool OBF>
 hipError_t launch_fp8(const DecodeArgs& a, hipStream_t st) {
   const long long n = (long long)a.B * a.Hkv * a.ncb * a.nchunk;
   if (n > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  if (a.n_rot <= 64)
-    hipLaunchKernelGGL((decode_fp8_kernel<D, G, KVS, 4, OBF>), dim3((unsigned)n), dim3(64 * NW8),
-                       0, st, a);
+  const dim3 grid((unsigned)n), block(64 * NW8);
+  if (a.n_rot == 64)
+    hipLaunchKernelGGL((decode_fp8_kernel<D, G, KVS, 4, true, OBF>), grid, block, 0, st, a);
+  else if (a.n_rot < 64)
+    hipLaunchKernelGGL((decode_fp8_kernel<D, G, KVS, 4, false, OBF>), grid, block, 0, st, a);
+  else if (a.n_rot == D / 2)
+    hipLaunchKernelGGL((decode_fp8_kernel<D, G, KVS, D / 32, true, OBF>), grid, block, 0, st, a);
   else
-    hipLaunchKernelGGL((decode_fp8_kernel<D, G, KVS, D / 32, OBF>), dim3((unsigned)n),
-                       dim3(64 * NW8), 0, st, a);
+    hipLaunchKernelGGL((decode_fp8_kernel<D, G, KVS, D / 32, false, OBF>), grid, block, 0, st, a);
   return hipGetLastError();
 }
 
