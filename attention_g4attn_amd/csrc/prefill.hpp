@@ -145,6 +145,17 @@ struct Lds {
 template <int N>
 using IC = std::integral_constant<int, N>;
 
+// Workgroups per CU the instance is built for.  The d = 256 instance with one
+// 32-row block per wave and a 2-stage ring fits two: 64 KiB of LDS, and at
+// most 256 registers per wave once the per-lane LDS offsets are recomputed
+// per tile, so each SIMD runs two waves and one wave's softmax overlaps the
+// other's products.  The others hold 256 + 256 registers per wave (the
+// output accumulators of 32*MB rows of d dims and the query operands).
+template <int D, int MB, int NST>
+constexpr int wg_per_cu() {
+  return (D == 256 && MB == 1 && NST == 2) ? 2 : 1;
+}
+
 template <class T>
 __device__ __forceinline__ T& lds_at(unsigned char* base, int off) {
   return *reinterpret_cast<T*>(base + off);
@@ -273,7 +284,7 @@ __device__ __noinline__ void exact_row(const uint16_t* qp, const uint16_t* kp, c
 // compute every tile that holds a visible key for any wave of the workgroup,
 // which holds without a window when a workgroup's tokens fit in one tile.
 template <int D, int G, bool KVS, bool OBF, int SW, int NST, int MB, bool SPREAD, bool VIS>
-__global__ void __launch_bounds__(NW * 64, 1) prefill_kernel(PrefillArgs a) {
+__global__ void __launch_bounds__(NW * 64, (wg_per_cu<D, MB, NST>())) prefill_kernel(PrefillArgs a) {
   constexpr int RW = 32 * MB;          // rows per wave
   constexpr int M = NW * RW;           // rows per workgroup
   constexpr int TQ = M / G;            // tokens per workgroup
@@ -287,11 +298,11 @@ __global__ void __launch_bounds__(NW * 64, 1) prefill_kernel(PrefillArgs a) {
   static_assert(NST == 2 || NST == 3, "ring");
   static_assert(!SPREAD || (NST == 3 && TQ <= BN), "spread loads need the 3-deep ring and TQ <= BN");
   static_assert(!VIS || (!SPREAD && SW == D && D % 64 == 0), "vision: full slab, halves of whole chunks");
-  // With two query blocks per wave the score and output accumulators leave
-  // few registers: the lane parts of LDS offsets are then recomputed per tile
-  // from an opaque copy of the lane id instead of staying live across the
-  // loop. With one block they fit and stay live.
-  constexpr bool RECOMP = MB == 2;
+  // With two query blocks per wave, or at two workgroups per CU, the score
+  // and output accumulators leave few registers: the lane parts of LDS
+  // offsets are then recomputed per tile from an opaque copy of the lane id
+  // instead of staying live across the loop.  Otherwise they fit and stay live.
+  constexpr bool RECOMP = MB == 2 || wg_per_cu<D, MB, NST>() == 2;
   __shared__ __attribute__((aligned(16))) unsigned char st0[L::STAGE];
   __shared__ __attribute__((aligned(16))) unsigned char st1[L::STAGE];
   __shared__ __attribute__((aligned(16))) unsigned char st2[NST == 3 ? L::STAGE : 16];

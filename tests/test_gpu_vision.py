@@ -4,8 +4,7 @@ the fp64 oracle (GPU).
 - Small and medium shapes, every row compared: G = 1, 2, 8; sequence lengths
   that leave ragged key tiles and partial workgroups; padded images (lengths
   below S, down to an image with no patch); random and raster grid positions;
-  fp32 and bf16 outputs.  Both workgroup heights the launcher picks between
-  (128 rows for small grids, 256 rows for a grid of whole rounds).
+  fp32 and bf16 outputs; a batch of eight images (sampled rows).
 - A score far above the row's first tile takes the exact recompute path.
 - Full size: budget-280 batch (4 images up to 2520 patches, one padded) and
   one budget-1120 image (10080 patches), sampled rows of every image, the
@@ -67,10 +66,9 @@ def test_vision_prefill_parity(case):
             assert (out[b, n:] == 0).all()
 
 
-def test_vision_prefill_256_row_workgroups():
-    """A grid that fills whole rounds of 256-row workgroups (8 images of up
-    to 1024 patches, 8 heads): the launcher keeps the two-block tiling.
-    Sampled rows of every image, one image padded."""
+def test_vision_prefill_batch_of_eight_images():
+    """8 images of up to 1024 patches, 8 heads (a grid of several whole
+    rounds of workgroups); sampled rows of every image, one image padded."""
     layer = inputs.VisionLayer(((32, 32),) * 7 + ((30, 31),), Hq=8, Hkv=8)
     q, k, v, pos2, lengths = inputs.vision_inputs(layer, 92, torch.bfloat16, DEV)
     out = run(q, k, v, pos2, lengths)
@@ -82,7 +80,7 @@ def test_vision_prefill_256_row_workgroups():
     ids = np.array(ids, np.int64)
     ref = ref_rows(q, k, v, pos2, lengths, rows=ids)
     got = out.view(layer.B * S, layer.Hq, layer.d)[torch.as_tensor(ids, device=DEV)]
-    assert_parity(got, ref, torch.bfloat16, "vision 256-row workgroups")
+    assert_parity(got, ref, torch.bfloat16, "vision batch of eight")
 
 
 def test_vision_prefill_bf16_output_and_raster_grid():
