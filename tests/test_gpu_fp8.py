@@ -240,3 +240,17 @@ def test_fill_fp8_group_global_prefill_s262144_sampled_rows():
     want = oracle.quantize_e4m3(to_oracle(k[0, torch.as_tensor(rows, device=DEV)]), np8(ks))
     got = kc[0][:, torch.as_tensor(rows, device=DEV)].permute(1, 0, 2).contiguous()
     assert np.array_equal(np8(got), want)
+
+
+def test_decode_fp8_ring_at_large_positions():
+    """Ring decode at positions near 2^24 (the angle reduction and the
+    angle-addition tables at large arguments), 3 query tokens, G = 2."""
+    layer = inputs.DecodeLayer("local", 2, 16, 8, 256, 64 + 2, 64, 1e4, 1.0)
+    q, kc, vc, ks, vs, _, _ = inputs.decode_inputs_fp8(layer, 73, 0, DEV,
+                                                       torch.tensor([66, 66]), 3)
+    pos = torch.tensor([(1 << 24) - 5, (1 << 24) + 12345], dtype=torch.int32, device=DEV)
+    out = g4.decode_fp8(q, kc, vc, ks, vs, pos, layer.window, layer.theta, layer.p)
+    torch.cuda.synchronize()
+    ref = oracle_fp8(q, kc, vc, ks, vs, pos, layer.window, layer.theta, layer.p)
+    assert torch.isfinite(out).all()
+    assert_parity(out, ref, torch.bfloat16, "fp8 ring at large positions")

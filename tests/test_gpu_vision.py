@@ -131,3 +131,19 @@ def test_vision_full_size_sampled_rows(layer):
     got = out.view(layer.B * S, layer.Hq, layer.d)[torch.as_tensor(ids, device=DEV)]
     mx, mean = assert_parity(got, ref, torch.bfloat16, f"vision {layer}")
     print(f"  rows {len(ids)}: max {mx:.2e} mean {mean:.2e}", flush=True)
+
+
+@pytest.mark.parametrize("S,ln", [(1, None), (33, [1, 33]), (32, [32, 31])])
+def test_vision_tiny_images(S, ln):
+    """One patch, and images that end on or just past a 32-key tile edge."""
+    B = 1 if ln is None else len(ln)
+    g = torch.Generator(device="cpu")
+    g.manual_seed(7 + S)
+    pos2 = torch.randint(0, 50, (B, S, 2), generator=g, dtype=torch.int32).to(DEV)
+    q = inputs.randn((B, S, 8, 256), 971 + S, torch.bfloat16, DEV)
+    k = inputs.randn((B, S, 4, 256), 972 + S, torch.bfloat16, DEV)
+    v = inputs.randn((B, S, 4, 256), 973 + S, torch.bfloat16, DEV)
+    lengths = None if ln is None else torch.tensor(ln, dtype=torch.int32, device=DEV)
+    out = run(q, k, v, pos2, lengths)
+    ref = ref_rows(q, k, v, pos2, lengths)
+    assert_parity(out, ref, torch.bfloat16, f"vision tiny S={S}")
