@@ -55,6 +55,29 @@ size_t prefill_ws_bytes(int B, int S, int Hkv, int d, int n_rot, int in_dtype) {
   return (size_t)B * S * Hkv * g4a::prefill_slab_dims(d, n_rot) * 2;
 }
 
+// Fields of a prefill launch shared by the causal and the vision calls.
+g4a::PrefillArgs prefill_args(const void* q, const void* k, const void* v, void* out,
+                              const int32_t* pos, int B, int S, int Hq, int Hkv, int d, int window,
+                              float theta, int n_rot) {
+  g4a::PrefillArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.out = out;
+  a.pos = pos;
+  a.B = B;
+  a.S = S;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.D = d;
+  a.window = window;
+  a.n_rot = n_rot;
+  a.log2_theta = log2((double)theta);
+  a.scale = (float)(1.0 / sqrt((double)d));
+  a.scale_log2e = (float)(1.4426950408889634 / sqrt((double)d));
+  return a;
+}
+
 int prefill(const void* q, const void* k, const void* v, void* out, const int32_t* pos, int B,
             int S, int Hq, int Hkv, int d, int window, float theta, float p, int in_dtype,
             int out_dtype, void* workspace, size_t workspace_bytes, void* stream,
@@ -68,22 +91,8 @@ int prefill(const void* q, const void* k, const void* v, void* out, const int32_
     return G4A_EALIGN;
   // element counts must stay addressable; the grid must fit in 2^31 workgroups
   if ((double)B * S * Hq * d > 9.0e18 || (double)B * S * Hkv > 2.0e9) return G4A_EINVAL;
-  g4a::PrefillArgs a{};
-  a.q = q;
-  a.k = k;
-  a.v = v;
-  a.out = out;
-  a.pos = pos;
-  a.B = B;
-  a.S = S;
-  a.Hq = Hq;
-  a.Hkv = Hkv;
-  a.D = d;
-  a.window = window;
-  a.n_rot = rotated_pairs(d, p);
-  a.log2_theta = log2((double)theta);
-  a.scale = (float)(1.0 / sqrt((double)d));
-  a.scale_log2e = (float)(1.4426950408889634 / sqrt((double)d));
+  g4a::PrefillArgs a =
+      prefill_args(q, k, v, out, pos, B, S, Hq, Hkv, d, window, theta, rotated_pairs(d, p));
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (in_dtype == G4A_F32) return finish(g4a::launch_prefill_f32(a, st));
   if (!g4a::prefill_supported(d)) return G4A_EUNSUPPORTED;
@@ -133,23 +142,9 @@ G4A_API int g4attn_vision_prefill(const void* q, const void* k, const void* v, v
       (lengths && misaligned(lengths)))
     return G4A_EALIGN;
   if ((double)B * S * Hq * d > 9.0e18 || (double)B * S * Hkv > 2.0e9) return G4A_EINVAL;
-  g4a::PrefillArgs a{};
-  a.q = q;
-  a.k = k;
-  a.v = v;
-  a.out = out;
-  a.pos = pos2;
+  // every pair of both halves turns
+  g4a::PrefillArgs a = prefill_args(q, k, v, out, pos2, B, S, Hq, Hkv, d, 0, theta, d / 2);
   a.lengths = lengths;
-  a.B = B;
-  a.S = S;
-  a.Hq = Hq;
-  a.Hkv = Hkv;
-  a.D = d;
-  a.window = 0;
-  a.n_rot = d / 2;  // every pair of both halves turns
-  a.log2_theta = log2((double)theta);
-  a.scale = (float)(1.0 / sqrt((double)d));
-  a.scale_log2e = (float)(1.4426950408889634 / sqrt((double)d));
   const size_t need = prefill_ws_bytes(B, S, Hkv, d, a.n_rot, in_dtype);
   if (!workspace || workspace_bytes < need) return G4A_EWORKSPACE;
   if (misaligned(workspace)) return G4A_EALIGN;
@@ -165,6 +160,32 @@ namespace {
 bool ring_ok(int capacity, int window, int q_len, bool multi) {
   if (window == 0) return true;
   return multi ? capacity >= window + q_len - 1 : capacity == window;
+}
+
+// Fields of a decode launch shared by every cache type; chunking, workspace
+// and scales are set by the caller.
+g4a::DecodeArgs decode_args(const void* q, const void* k_cache, const void* v_cache, void* out,
+                            const int32_t* pos, int B, int q_len, int Hq, int Hkv, int d,
+                            int capacity, int window, float theta, float p) {
+  g4a::DecodeArgs a{};
+  a.q = q;
+  a.k = k_cache;
+  a.v = v_cache ? v_cache : k_cache;
+  a.out = out;
+  a.pos = pos;
+  a.B = B;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.D = d;
+  a.capacity = capacity;
+  a.window = window;
+  a.n_rot = rotated_pairs(d, p);
+  a.q_len = q_len;
+  a.ncb = ((Hq / Hkv) * q_len + 15) / 16;
+  a.log2_theta = log2((double)theta);
+  a.scale = (float)(1.0 / sqrt((double)d));
+  a.scale_log2e = (float)(1.4426950408889634 / sqrt((double)d));
+  return a;
 }
 
 size_t decode_ws_bytes(int B, int q_len, int Hq, int Hkv, int d, int capacity, int window,
@@ -193,24 +214,8 @@ int decode(const void* q, const void* k_cache, const void* v_cache, void* out,
     return G4A_EALIGN;
   if ((double)B * Hkv * capacity * d > 9.0e18) return G4A_EINVAL;
   const bool f32 = in_dtype == G4A_F32;
-  g4a::DecodeArgs a{};
-  a.q = q;
-  a.k = k_cache;
-  a.v = v_cache ? v_cache : k_cache;
-  a.out = out;
-  a.pos = pos;
-  a.B = B;
-  a.Hq = Hq;
-  a.Hkv = Hkv;
-  a.D = d;
-  a.capacity = capacity;
-  a.window = window;
-  a.n_rot = rotated_pairs(d, p);
-  a.q_len = q_len;
-  a.ncb = ((Hq / Hkv) * q_len + 15) / 16;
-  a.log2_theta = log2((double)theta);
-  a.scale = (float)(1.0 / sqrt((double)d));
-  a.scale_log2e = (float)(1.4426950408889634 / sqrt((double)d));
+  g4a::DecodeArgs a = decode_args(q, k_cache, v_cache, out, pos, B, q_len, Hq, Hkv, d, capacity,
+                                  window, theta, p);
   a.chunk = g4a::decode_chunk_rows(d, capacity, window, f32);
   a.nchunk = g4a::decode_num_chunks(d, capacity, window, f32);
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -254,6 +259,30 @@ G4A_API int g4attn_decode_multi(const void* q, const void* k_cache, const void* 
                 in_dtype, out_dtype, workspace, workspace_bytes, stream, true);
 }
 
+namespace {
+
+// Fields of a cache fill shared by the byte copy and the quantizing fill; a
+// false return means the grid would not fit (G4A_EINVAL).
+bool fill_args(g4a::FillArgs& a, const void* k, const void* v, const int32_t* pos, int B, int S,
+               int Hkv, void* k_cache, void* v_cache, int capacity, int window, int row_chunks) {
+  a = g4a::FillArgs{};
+  a.k = k;
+  a.v = v;
+  a.pos = pos;
+  a.k_cache = k_cache;
+  a.v_cache = v ? v_cache : nullptr;
+  a.B = B;
+  a.S = S;
+  a.Hkv = Hkv;
+  a.capacity = capacity;
+  a.window = window;
+  a.row_chunks = row_chunks;
+  const int nw = window > 0 ? (S < capacity ? S : capacity) : S;  // tokens a ring keeps
+  return (double)B * nw * Hkv * row_chunks <= 2.0e9;
+}
+
+}  // namespace
+
 G4A_API int g4attn_fill_cache(const void* k, const void* v, const int32_t* pos, int B, int S,
                               int Hkv, int d, void* k_cache, void* v_cache, int capacity,
                               int window, int dtype, void* stream) {
@@ -266,20 +295,10 @@ G4A_API int g4attn_fill_cache(const void* k, const void* v, const int32_t* pos, 
   if (misaligned(k) || (v && misaligned(v)) || misaligned(pos) || misaligned(k_cache) ||
       (v && misaligned(v_cache)))
     return G4A_EALIGN;
-  g4a::FillArgs a{};
-  a.k = k;
-  a.v = v;
-  a.pos = pos;
-  a.k_cache = k_cache;
-  a.v_cache = v ? v_cache : nullptr;
-  a.B = B;
-  a.S = S;
-  a.Hkv = Hkv;
-  a.capacity = capacity;
-  a.window = window;
-  a.row_chunks = (int)((long long)d * esize / 16);
-  const int nw = window > 0 ? (S < capacity ? S : capacity) : S;
-  if ((double)B * nw * Hkv * a.row_chunks > 2.0e9) return G4A_EINVAL;
+  g4a::FillArgs a;
+  if (!fill_args(a, k, v, pos, B, S, Hkv, k_cache, v_cache, capacity, window,
+                 (int)((long long)d * esize / 16)))
+    return G4A_EINVAL;
   return finish(g4a::launch_fill_cache(a, static_cast<hipStream_t>(stream)));
 }
 
@@ -319,24 +338,8 @@ G4A_API int g4attn_decode_fp8(const void* q, const void* k_cache, const void* v_
       (!kv_shared && misaligned(v_scale)))
     return G4A_EALIGN;
   if ((double)B * Hkv * capacity * d > 9.0e18) return G4A_EINVAL;
-  g4a::DecodeArgs a{};
-  a.q = q;
-  a.k = k_cache;
-  a.v = kv_shared ? k_cache : v_cache;
-  a.out = out;
-  a.pos = pos;
-  a.B = B;
-  a.Hq = Hq;
-  a.Hkv = Hkv;
-  a.D = d;
-  a.capacity = capacity;
-  a.window = window;
-  a.n_rot = rotated_pairs(d, p);
-  a.q_len = q_len;
-  a.ncb = ((Hq / Hkv) * q_len + 15) / 16;
-  a.log2_theta = log2((double)theta);
-  a.scale = (float)(1.0 / sqrt((double)d));
-  a.scale_log2e = (float)(1.4426950408889634 / sqrt((double)d));
+  g4a::DecodeArgs a = decode_args(q, k_cache, kv_shared ? nullptr : v_cache, out, pos, B, q_len,
+                                  Hq, Hkv, d, capacity, window, theta, p);
   a.chunk = g4a::decode_fp8_chunk_rows(capacity, window);
   a.nchunk = g4a::decode_fp8_num_chunks(capacity, window);
   a.k_scale = k_scale;
@@ -363,24 +366,13 @@ G4A_API int g4attn_fill_cache_fp8(const void* k, const void* v, const float* k_s
   if (misaligned(k) || (v && misaligned(v)) || misaligned(pos) || misaligned(k_cache) ||
       misaligned(k_scale) || (v && (misaligned(v_cache) || misaligned(v_scale))))
     return G4A_EALIGN;
-  g4a::FillArgs a{};
-  a.k = k;
-  a.v = v;
-  a.pos = pos;
-  a.k_cache = k_cache;
-  a.v_cache = v ? v_cache : nullptr;
-  a.B = B;
-  a.S = S;
-  a.Hkv = Hkv;
-  a.capacity = capacity;
-  a.window = window;
-  a.row_chunks = d / 16;
+  g4a::FillArgs a;
+  if (!fill_args(a, k, v, pos, B, S, Hkv, k_cache, v_cache, capacity, window, d / 16))
+    return G4A_EINVAL;
   a.in_f32 = in_dtype == G4A_F32;
   a.d = d;
   a.k_scale = k_scale;
   a.v_scale = v ? v_scale : nullptr;
-  const int nw = window > 0 ? (S < capacity ? S : capacity) : S;
-  if ((double)B * nw * Hkv * a.row_chunks > 2.0e9) return G4A_EINVAL;
   return finish(g4a::launch_fill_cache_fp8(a, static_cast<hipStream_t>(stream)));
 }
 
