@@ -33,7 +33,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle baseline sample")
-    ap.add_argument("--only", choices=["all", "local", "global", "decode"], default="all",
+    ap.add_argument("--only", choices=["all", "local", "global", "decode", "fp8"], default="all",
                     help="restrict the step to one kernel kind (profiling runs)")
     ap.add_argument("--seq", type=int, default=None, help="override the prefill length")
     ap.add_argument("--no-configs", action="store_true",
@@ -184,9 +184,12 @@ def main():
         if D_glo is not None:
             per_kind["global_decode"].append(next(it))
     print(f"# timed {args.steps} steps in {wall:.2f}s", file=sys.stderr, flush=True)
-    extra = {} if args.no_configs else time_configs(g4, inputs, torch)
-    nxt = {} if args.no_configs else time_next(g4, inputs, torch)
-    if not args.no_configs:
+    only_fp8 = args.only == "fp8"  # the fp8-cache timings alone (for counter runs)
+    extra = {} if args.no_configs or only_fp8 else time_configs(g4, inputs, torch)
+    nxt = {} if args.no_configs or only_fp8 else time_next(g4, inputs, torch)
+    if only_fp8:
+        nxt["fp8"] = time_fp8(g4, inputs, torch)
+    elif not args.no_configs:
         nxt["fp8"] = time_fp8(g4, inputs, torch)
         nxt["vision"] = time_vision(g4, inputs, torch)
 
@@ -217,7 +220,7 @@ def main():
                                      "tok_per_s": dglo.B / tg * 1e3}
         kind_rep["group_decode_tok_per_s"] = dloc.B / (5 * tl + tg) * 1e3
 
-    if not args.no_configs:
+    if not args.no_configs and not only_fp8:
         nxt["schedules"] = time_schedules(g4, inputs, torch, kind_rep)
 
     roof = None
