@@ -8,6 +8,9 @@ against the fp64 oracle (GPU).
   several cache chunks (merge kernel), fp32 inputs and bf16 outputs.
 - Closed loop: prefill, fill the cache with the prompt and then the new
   tokens, decode the new tokens at once: equals the oracle's prefill rows.
+- Full size, at the benchmark's shapes: 4-token decode of batch 64 over the
+  515-slot rings and the 64K K=V cache (12 sampled sequences compared), and
+  the fill of the 256K-token K=V prefill (sampled rows, bit for bit).
 Tolerances as for the other parity tests (bf16: max 1e-2, mean 1e-3; f32 1e-4).
 """
 import numpy as np
@@ -162,3 +165,53 @@ def test_prefill_fill_cache_decode_closed_loop(kind):
                          layer.window, layer.theta, layer.p, rows=rows)
     ref = ref.reshape(layer.B, L, layer.Hq, layer.d)
     assert_parity(out, ref, torch.bfloat16, f"closed loop {kind}")
+
+
+@pytest.mark.parametrize("kind", ["local-ring515", "global-kv-linear65536"])
+def test_decode_multi_full_size_sampled_sequences(kind):
+    """4 query tokens per sequence at the benchmark's shapes (batch 64); every
+    output of 12 sampled sequences compared (the GPU computes all 64)."""
+    L = 4
+    if kind.startswith("local"):
+        base = inputs.DECODE_LOCAL
+        layer = inputs.DecodeLayer(base.kind, base.B, base.Hq, base.Hkv, base.d,
+                                   base.window + L - 1, base.window, base.theta, base.p)
+    else:
+        layer = inputs.DECODE_GLOBAL
+    lengths = inputs.decode_lengths(layer.B)
+    _, kc, vc, pos, _ = inputs.decode_inputs(layer, 62, 0, torch.bfloat16, DEV, lengths)
+    q = inputs.randn((layer.B, L, layer.Hq, layer.d), 6201, torch.bfloat16, DEV)
+    print(f"decode_multi full size {kind}", flush=True)
+    out = g4.decode_multi(q, kc, vc, pos, layer.window, layer.theta, layer.p)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all()
+    seqs = sorted({0, layer.B - 1} | set(np.random.default_rng(63).choice(layer.B, 10, replace=False)
+                                          .tolist()))
+    for b in seqs:
+        P = int(pos[b])
+        rows = layer.capacity if layer.window > 0 else P + 1  # the rows a linear cache holds
+        ref = oracle.decode_multi(to_oracle(q[b:b + 1]), to_oracle(kc[b:b + 1, :, :rows]),
+                                  None if vc is None else to_oracle(vc[b:b + 1, :, :rows]),
+                                  pos[b:b + 1].cpu().numpy(), layer.window, layer.theta, layer.p)
+        assert_parity(out[b:b + 1], ref, torch.bfloat16, f"{kind} b={b}")
+
+
+def test_fill_cache_group_global_prefill_s262144_sampled_rows():
+    """The fill the benchmark times: the 256K-token K=V rows into a linear
+    cache; sampled rows compared bit for bit with the oracle's fill."""
+    gl = inputs.global_(1, inputs.GROUP_S)
+    k = inputs.randn((gl.B, gl.S, gl.Hkv, gl.d), 6201, torch.bfloat16, DEV)
+    p = inputs.positions(gl.B, gl.S, DEV)
+    kc = torch.empty((gl.B, gl.Hkv, gl.S, gl.d), dtype=torch.bfloat16, device=DEV)
+    print("fill_cache full size", flush=True)
+    g4.fill_cache(k, None, p, kc, None, 0)
+    torch.cuda.synchronize()
+    rows = np.array(sorted({0, 1, 4095, 4096, gl.S // 2, gl.S - 1}
+                           | set(np.random.default_rng(64).choice(gl.S, 26, replace=False)
+                                 .tolist())), np.int64)
+    sub_k = k[:, torch.as_tensor(rows, device=DEV)].contiguous()       # [1, n, Hkv, d]
+    sub_p = torch.arange(rows.size, dtype=torch.int32)[None].numpy()   # slot i for row i
+    want, _ = oracle.fill_cache(to_oracle(sub_k), None, sub_p,
+                                np.zeros((1, gl.Hkv, rows.size, gl.d), np.uint16), None, 0)
+    got = kc[:, :, torch.as_tensor(rows, device=DEV)].contiguous()
+    assert np.array_equal(to_oracle(got), want)
