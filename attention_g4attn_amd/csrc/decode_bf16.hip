@@ -95,6 +95,7 @@ decode_split_kernel(DecodeArgs a) {
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l16 = lane & 15, g4 = lane >> 4;
   const Unit u = unit_of_block(a);  // XCD-aware grid order
+  if (u.b < 0) return;
   const int cb = u.cb, ch = u.ch, b = u.b, hkv = u.hkv;
   const int P = a.pos[b];
   const int W = a.window, C = a.capacity, QL = a.q_len;

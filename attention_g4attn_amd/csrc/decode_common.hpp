@@ -38,24 +38,84 @@ __device__ __forceinline__ T& lds_at(unsigned char* base, int off) {
 }
 
 // Work unit of a split workgroup: column block cb (16 (query token, head)
-// columns), chunk ch of the cache rows, sequence b, KV head hkv.
+// columns), chunk ch of the cache rows, sequence b, KV head hkv.  b < 0: the
+// workgroup has no unit and returns at once.
 struct Unit {
   int cb, ch, b, hkv;
 };
 
-// Units (b, kv head, chunk) go in groups of 8; the column blocks of the units
-// of a group take grid indices 8 apart (r apart in a last, smaller group of r
-// units).  Workgroups are dealt to the 8 XCDs in grid order, so every column
-// block of a chunk runs on the same XCD at about the same time and its later
-// reads of the chunk hit that XCD's L2.
+// Chunks of sequence b that hold a row its queries may see.  A sequence whose
+// position is out of range has none: the merge kernel writes its NaN rows.
+__device__ __forceinline__ int active_chunks(const DecodeArgs& a, int P) {
+  if (P < 0 || (a.window == 0 && P >= a.capacity)) return 0;
+  const int last = a.window > 0 ? min(P, a.capacity - 1) : P;
+  return min(last / a.chunk + 1, a.nchunk);
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ int wave_scan_incl(int v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int t = __shfl_up(v, d);
+    v += lane >= d ? t : 0;
+  }
+  return v;
+}
+
+// Grid index -> unit.  Units are the (sequence, KV head, chunk) triples with
+// a visible row, chunk fastest, numbered densely: the grid is sized for every
+// chunk of the capacity, and the blocks past the active units (sequences
+// shorter than the capacity leave many) all sit at the end of the grid and
+// return at once.  With the empty blocks interleaved among the working ones
+// (a fixed block per chunk of the capacity), shader-clock probes of a batch-64
+// K=V decode found working waves in only about 61% of the wave slots over the
+// launch, against 90% with the dense numbering, and the lower XCDs received
+// more units than the upper ones.
+// Units go in groups of 8; the column blocks of the units of a group take
+// grid indices 8 apart (r apart in a last, smaller group of r units).
+// Workgroups are dealt to the 8 XCDs in grid order, so every column block of
+// a chunk runs on the same XCD at about the same time and its later reads of
+// the chunk hit that XCD's L2; and each XCD receives the same number of units.
+// One chunk per sequence (rings): every (sequence, KV head) is a unit, so the
+// workgroup of a sequence with a bad position writes its NaN rows itself.
 __device__ __forceinline__ Unit unit_of_block(const DecodeArgs& a) {
-  const int nunit = a.B * a.Hkv * a.nchunk;
+  const int lane = threadIdx.x & 63;
+  int nunit;
+  if (a.nchunk == 1) {
+    nunit = a.B * a.Hkv;
+  } else {
+    int total = 0;
+    for (int b0 = 0; b0 < a.B; b0 += 64) {
+      const int b = b0 + lane;
+      total += __shfl(wave_scan_incl(b < a.B ? active_chunks(a, a.pos[b]) : 0), 63);
+    }
+    nunit = __builtin_amdgcn_readfirstlane(total) * a.Hkv;
+  }
   const int grp = blockIdx.x / (8 * a.ncb);
   const int gsz = min(8, nunit - 8 * grp);  // units in this group
+  if (gsz <= 0) return Unit{0, 0, -1, 0};
   const int within = blockIdx.x - grp * 8 * a.ncb;
+  if (within >= gsz * a.ncb) return Unit{0, 0, -1, 0};  // past the last unit's blocks
   const int unit = 8 * grp + within % gsz;
-  const int bh = unit / a.nchunk;
-  return Unit{within / gsz, unit % a.nchunk, bh / a.Hkv, bh % a.Hkv};
+  const int cb = within / gsz;
+  if (a.nchunk == 1) return Unit{cb, 0, unit / a.Hkv, unit % a.Hkv};
+  // the sequence whose units [acc + excl, acc + incl) hold `unit`
+  int acc = 0;
+  for (int b0 = 0; b0 < a.B; b0 += 64) {
+    const int b = b0 + lane;
+    const int n = b < a.B ? active_chunks(a, a.pos[b]) : 0;
+    const int incl = wave_scan_incl(n * a.Hkv);
+    const unsigned long long hit = __ballot(acc + incl > unit);
+    if (hit) {
+      const int l = __builtin_ctzll(hit);
+      const int nb = __builtin_amdgcn_readfirstlane(__shfl(n, l));
+      const int rem = unit - acc - __builtin_amdgcn_readfirstlane(__shfl(incl, l)) + nb * a.Hkv;
+      return Unit{cb, rem % nb, b0 + l, rem / nb};
+    }
+    acc += __builtin_amdgcn_readfirstlane(__shfl(incl, 63));
+  }
+  return Unit{0, 0, -1, 0};
 }
 
 // End of a chunk.  oacc holds O^T of this wave (lane (g4, l16): dims

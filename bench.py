@@ -135,6 +135,11 @@ def main():
     stream = torch.cuda.current_stream()
     kinds = ["local_prefill", "global_prefill", "local_decode", "global_decode"]
 
+    # Each run of launches of one kind (the 5 local prefills, the global
+    # prefill, the 5 local decodes, the global decode) is bracketed by one
+    # event pair on the launch stream, and its time divided by the launches
+    # in it.  An event pair around every single launch adds the event
+    # packets' own cost to each: about 5 us on a 55 us decode launch.
     def step(record):
         ev = []
         def mark():
@@ -142,18 +147,22 @@ def main():
                 e = torch.cuda.Event(enable_timing=True)
                 e.record(stream)
                 ev.append(e)
-        for (q, k, v, pos), out in zip(L_in, L_out):
+        if L_in:
             mark()
-            g4.local_prefill(q, k, v, pos, loc.window, loc.theta, loc.p, out=out, workspace=pws_l)
+            for (q, k, v, pos), out in zip(L_in, L_out):
+                g4.local_prefill(q, k, v, pos, loc.window, loc.theta, loc.p, out=out,
+                                 workspace=pws_l)
             mark()
         if G_in is not None:
             q, kv, _, pos = G_in
             mark()
             g4.global_prefill(q, kv, pos, 0, glo.theta, glo.p, out=G_out, workspace=pws_g)
             mark()
-        for (q, kc, vc, pos, _), out in zip(D_loc, D_out_l):
+        if D_loc:
             mark()
-            g4.decode(q, kc, vc, pos, dloc.window, dloc.theta, dloc.p, out=out, workspace=ws_l)
+            for (q, kc, vc, pos, _), out in zip(D_loc, D_out_l):
+                g4.decode(q, kc, vc, pos, dloc.window, dloc.theta, dloc.p, out=out,
+                          workspace=ws_l)
             mark()
         if D_glo is not None:
             q, kc, _, pos, _ = D_glo
@@ -173,16 +182,15 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     for ev in all_ev:
-        pairs = [ev[i].elapsed_time(ev[i + 1]) for i in range(0, len(ev), 2)]
-        it = iter(pairs)
-        for _ in L_in:
-            per_kind["local_prefill"].append(next(it))
+        pairs = iter([ev[i].elapsed_time(ev[i + 1]) for i in range(0, len(ev), 2)])
+        if L_in:
+            per_kind["local_prefill"].append(next(pairs) / len(L_in))
         if G_in is not None:
-            per_kind["global_prefill"].append(next(it))
-        for _ in D_loc:
-            per_kind["local_decode"].append(next(it))
+            per_kind["global_prefill"].append(next(pairs))
+        if D_loc:
+            per_kind["local_decode"].append(next(pairs) / len(D_loc))
         if D_glo is not None:
-            per_kind["global_decode"].append(next(it))
+            per_kind["global_decode"].append(next(pairs))
     print(f"# timed {args.steps} steps in {wall:.2f}s", file=sys.stderr, flush=True)
     only_fp8 = args.only == "fp8"  # the fp8-cache timings alone (for counter runs)
     extra = {} if args.no_configs or only_fp8 else time_configs(g4, inputs, torch)

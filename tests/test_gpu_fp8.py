@@ -176,6 +176,27 @@ def test_decode_fp8_positions_out_of_range_nan(window):
     assert_parity(out[1], ref[1], torch.bfloat16, "sequence 1")
 
 
+def test_decode_fp8_many_sequences_mixed_lengths():
+    """70 sequences over a 3-chunk linear K=V cache, lengths from 1 to the
+    capacity and out-of-range positions (the grid maps workgroups only onto
+    chunks with visible rows)."""
+    layer = inputs.DecodeLayer("global", 70, 8, 1, 512, 2200, 0, 1e6, 0.25)
+    g = torch.Generator()
+    g.manual_seed(6)
+    lengths = torch.randint(1, layer.capacity + 1, (layer.B,), generator=g)
+    lengths[:3] = torch.tensor([1, 1024, layer.capacity])
+    q, kc, _, ks, _, pos, _ = inputs.decode_inputs_fp8(layer, 74, 0, DEV, lengths)
+    bad = [3, 63, 64, 69]
+    pos[bad] = torch.tensor([-1, layer.capacity, -9, layer.capacity + 1],
+                            dtype=torch.int32, device=DEV)
+    out = g4.decode_fp8(q, kc, None, ks, None, pos, 0, layer.theta, layer.p)
+    torch.cuda.synchronize()
+    good = [b for b in range(layer.B) if b not in bad]
+    assert torch.isnan(out[bad]).all()
+    ref = oracle_fp8(q[good], kc[good], None, ks, None, pos[good], 0, layer.theta, layer.p)
+    assert_parity(out[good], ref, torch.bfloat16, "70 sequences")
+
+
 @pytest.mark.parametrize("kind", ["local", "global"])
 def test_prefill_rows_fill_fp8_decode_closed_loop(kind):
     """Prefill rows quantized into the cache as a prompt and then new tokens;

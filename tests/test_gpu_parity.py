@@ -222,6 +222,29 @@ def test_decode_bad_positions_nan():
     assert torch.isnan(out[0]).all() and torch.isnan(out[1]).all() and torch.isfinite(out[2]).all()
 
 
+def test_decode_many_sequences_mixed_lengths():
+    """130 sequences (the grid's unit numbering scans them 64 at a time) over a
+    3-chunk linear cache: lengths from 1 to the capacity, and positions past
+    the cache or negative.  Workgroups map densely onto the chunks that hold
+    visible rows; every good row must match and every bad one be NaN."""
+    layer = inputs.DecodeLayer("global", 130, 8, 1, 512, 2500, 0, 1e6, 0.25)
+    g = torch.Generator()
+    g.manual_seed(5)
+    lengths = torch.randint(1, layer.capacity + 1, (layer.B,), generator=g)
+    lengths[:4] = torch.tensor([1, 1024, 1025, layer.capacity])
+    q, kc, _, pos, _ = inputs.decode_inputs(layer, 93, 0, torch.bfloat16, DEV, lengths)
+    bad = [5, 64, 65, 129]
+    pos[bad] = torch.tensor([-1, layer.capacity, -7, layer.capacity + 4000],
+                            dtype=torch.int32, device=DEV)
+    out = g4.decode(q, kc, None, pos, 0, layer.theta, layer.p)
+    torch.cuda.synchronize()
+    good = [b for b in range(layer.B) if b not in bad]
+    assert torch.isnan(out[bad]).all()
+    ref = oracle.decode(to_oracle(q[good]), to_oracle(kc[good]), None,
+                        pos[good].cpu().numpy(), 0, layer.theta, layer.p)
+    assert_parity(out[good], ref, torch.bfloat16, "130 sequences")
+
+
 def test_decode_equals_last_prefill_row():
     S = 517
     layer = inputs.Layer("global", 1, S, 16, 2, 512, 0, 1e6, 0.25)
