@@ -4,11 +4,18 @@
   python -m attention_g4attn_amd.profsum traffic --fetch <counter_collection.csv>
       --write <counter_collection.csv> --kernel <name prefix> --copy-bytes N
       --cmd-fetch "<command>" --cmd-write "<command>" --out <file>
+  python -m attention_g4attn_amd.profsum mfma <counter_collection.csv> --kernel <name prefix>
+      --cmd "<command>" --out <file>
 
 `traffic` scales FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of the kernel by
 what the same counters read for the plain device copy of --copy-bytes bytes in
 the same run (rocclr's copyBuffer kernel), and records the sha256 of the kernel
 sources so a reader can tell whether the figure still describes the code.
+
+`mfma` turns SQ_VALU_MFMA_BUSY_CYCLES (matrix-core busy cycles summed over
+the 1024 SIMDs) and SQ_INSTS_VALU_MFMA_MOPS_BF16 (bf16 matrix work in units of
+512 FLOPs) of one kernel into its matrix-core busy fraction over the
+dispatch's duration at the 2.4 GHz peak clock, and its executed FLOPs.
 """
 import argparse
 import csv
@@ -87,6 +94,43 @@ def traffic(args):
     open(args.out, "w").write("\n".join(lines) + "\n")
 
 
+SIMDS = 1024          # 256 CUs x 4 SIMDs
+PEAK_CLOCK_HZ = 2.4e9
+
+
+def mfma(args):
+    busy, mops, dur = [], [], []
+    per = {}
+    for r in csv.DictReader(open(args.csv)):
+        if not r["Kernel_Name"].startswith(args.kernel):
+            continue
+        d = per.setdefault(r["Dispatch_Id"], {})
+        d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+        d["_ns"] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+    for d in per.values():
+        busy.append(d["SQ_VALU_MFMA_BUSY_CYCLES"])
+        mops.append(d["SQ_INSTS_VALU_MFMA_MOPS_BF16"])
+        dur.append(d["_ns"] * 1e-9)
+    if not per:
+        raise SystemExit("kernel dispatches missing from the counter file")
+    b, m, t = statistics.mean(busy), statistics.mean(mops), statistics.mean(dur)
+    lines = [
+        "# Matrix-core activity of one launch, from rocprofv3 counters",
+        f"kernel: {args.kernel}",
+        f"command: {args.cmd}",
+        f"dispatches: {len(per)}",
+        f"sq_valu_mfma_busy_cycles_per_dispatch: {b:.6e}",
+        f"sq_insts_valu_mfma_mops_bf16_per_dispatch: {m:.6e}",
+        f"dispatch_seconds: {t:.6f}",
+        f"mfma_flops_per_dispatch: {m * 512:.6e}",
+        f"mfma_busy_fraction_at_2.4GHz: {b / SIMDS / (t * PEAK_CLOCK_HZ):.4f}",
+        f"mfma_tflops: {m * 512 / t / 1e12:.1f}",
+        f"source_sha256: {source_hash(args.sources)}",
+        "sources: " + ", ".join(args.sources),
+    ]
+    open(args.out, "w").write("\n".join(lines) + "\n")
+
+
 def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="what", required=True)
@@ -104,8 +148,15 @@ def main():
     t.add_argument("--out", required=True)
     t.add_argument("--sources", nargs="+", default=KERNEL_SOURCES,
                    help="files whose sha256 identifies the kernel version")
+    m = sub.add_parser("mfma")
+    m.add_argument("csv")
+    m.add_argument("--kernel", required=True)
+    m.add_argument("--cmd", required=True)
+    m.add_argument("--out", required=True)
+    m.add_argument("--sources", nargs="+", default=KERNEL_SOURCES,
+                   help="files whose sha256 identifies the kernel version")
     a = ap.parse_args()
-    stats(a) if a.what == "stats" else traffic(a)
+    {"stats": stats, "traffic": traffic, "mfma": mfma}[a.what](a)
 
 
 if __name__ == "__main__":

@@ -46,22 +46,24 @@ def parse():
 PROFILES = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles")
 TRAFFIC_SUMMARY = os.path.join(PROFILES, "prefill_global_kv512_s262144_hbm_traffic.txt")
 DECODE_TRAFFIC_SUMMARY = os.path.join(PROFILES, "decode_global_kv512_b64_hbm_traffic.txt")
-def measured_traffic(path=TRAFFIC_SUMMARY):
-    """HBM bytes per launch of a kernel, from a committed rocprofv3 counter
-    summary, or None when the kernel sources it names changed since."""
+MFMA_SUMMARY = os.path.join(PROFILES, "prefill_global_kv512_s262144_mfma_busy.txt")
+
+
+def measured_traffic(path=TRAFFIC_SUMMARY, key="hbm_bytes_per_launch"):
+    """One figure (HBM bytes per launch by default) of a committed rocprofv3
+    counter summary, or None when the kernel sources it names changed since."""
     try:
         text = open(path).read()
     except OSError:
         return None
     vals = dict(line.split(":", 1) for line in text.splitlines()
-                if ":" in line and line.split(":", 1)[0] in ("source_sha256", "hbm_bytes_per_launch",
-                                                            "sources"))
+                if ":" in line and line.split(":", 1)[0] in ("source_sha256", key, "sources"))
     from attention_g4attn_amd.profsum import source_hash
     sources = [f.strip() for f in vals.get("sources", "").split(",") if f.strip()]
     if not sources or vals.get("source_sha256", "").strip() != source_hash(sources):
         return None
     try:
-        return float(vals["hbm_bytes_per_launch"])
+        return float(vals[key])
     except (KeyError, ValueError):
         return None
 
@@ -238,6 +240,9 @@ def main():
         roof = {"bound": "mfma", "achieved": ach, "peak": MFMA_BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": ach / MFMA_BF16_PEAK_TFLOPS,
                 "traffic": measured_traffic() if S == inputs.GROUP_S else None,
+                # matrix-core busy fraction of the same launch from its counters
+                "mfma_busy": (measured_traffic(MFMA_SUMMARY, "mfma_busy_fraction_at_2.4GHz")
+                              if S == inputs.GROUP_S else None),
                 "kernel": "g4a::pf::prefill_kernel<512, 8, true, false, 128, 3, 1, true, false>",
                 "flops_per_launch": fl_glo, "ms_per_launch": t}
     roof_dec = None
