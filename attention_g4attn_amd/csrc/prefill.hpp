@@ -182,10 +182,18 @@ __global__ void __launch_bounds__(256) rope_keys_kernel(const uint16_t* __restri
                                                        long long nchunks, int Hkv, int D, int n_rot,
                                                        double log2_theta) {
   constexpr int CPR = SW / 8;  // chunks per slab row
+  static_assert(256 % CPR == 0, "the grid stride keeps each thread on one chunk column");
+  // A thread's chunk column c is the same in every iteration (the stride is a
+  // multiple of CPR), so the frequencies of its 4 pairs are computed once:
+  // recomputing them per chunk (an fp64 exponential each) made the pass
+  // compute-bound.
+  const int c = (int)(threadIdx.x % CPR);
+  double g[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) g[e] = pair_rev<VIS>(4 * c + e, D, log2_theta);
   for (long long i = blockIdx.x * 256ll + threadIdx.x; i < nchunks;
        i += (long long)gridDim.x * 256) {
     const long long row = i / CPR;
-    const int c = (int)(i % CPR);
     u32x4 x = *reinterpret_cast<const u32x4*>(k + row * D + 8 * c);
     if (4 * c < n_rot) {
       const int p = VIS ? pos[(row / Hkv) * 2 + (4 * c >= D / 4)] : pos[row / Hkv];
@@ -193,7 +201,7 @@ __global__ void __launch_bounds__(256) rope_keys_kernel(const uint16_t* __restri
       for (int e = 0; e < 4; ++e) {
         const int t = 4 * c + e;
         float cs, sn;
-        rope_cs_accurate(p, pair_rev<VIS>(t, D, log2_theta), cs, sn);
+        rope_cs_accurate(p, g[e], cs, sn);
         const float x0 = bf_lo(x[e]), x1 = bf_hi(x[e]);
         const uint32_t r = pack_bf16(x0 * cs - x1 * sn, x0 * sn + x1 * cs);
         x[e] = t < n_rot ? r : x[e];
