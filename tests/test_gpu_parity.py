@@ -106,8 +106,11 @@ def test_large_positions_offset():
     assert_parity(out, oracle_prefill(layer, q, k, v, pos, W), torch.bfloat16, "offset local")
 
 
-def test_bf16_output():
-    layer = SMALL[0]
+@pytest.mark.parametrize("layer", [SMALL[0], SMALL[2], SMALL[5]],
+                         ids=["global-d512", "local-d256", "kv-d256"])
+def test_bf16_output(layer):
+    """bf16 output: the d = 512 epilogue stores from the accumulators, the
+    d = 256 one stages whole rows through LDS first (ragged S included)."""
     out, (q, k, v, pos, W) = run_prefill(layer, torch.bfloat16, out_dtype=torch.bfloat16)
     assert out.dtype == torch.bfloat16
     ref = oracle_prefill(layer, q, k, v, pos, W)
