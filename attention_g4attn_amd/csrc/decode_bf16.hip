@@ -124,6 +124,7 @@ decode_split_kernel(DecodeArgs a) {
   // that stream faster take more tiles and all finish together.  A wave's
   // tiles increase, so its loads are issued in tile order.
   const int nt = (r1 - r0 + TR - 1) / TR;
+  const bool stream_loads = a.ncb == 1;  // cache rows read once: non-temporal
   const int n_rot = a.n_rot;
   unsigned char* kt = tk + (KREG ? 0 : w * KB);
   unsigned char* vt0 = tv + (KVS ? 0 : w * KB);
@@ -155,7 +156,7 @@ decode_split_kernel(DecodeArgs a) {
     for (int n = 0; n < TR / RPI; ++n) {
       const int row = n * RPI + ln / CPR;
       const uint32_t voff = (uint32_t)row * (2 * D) + ((uint32_t)((ln % CPR) ^ dswz(row)) << 4);
-      lds_dma16(rs, voff, dst + n * 1024);
+      lds_dma16(rs, voff, dst + n * 1024, stream_loads);
     }
   };
   // The angle table is shared by the waves of a workgroup.  With several
@@ -185,7 +186,9 @@ decode_split_kernel(DecodeArgs a) {
     const uint32_t base = (uint32_t)(ln & 15) * (2 * D) + (uint32_t)(ln >> 4) * 16;
 #pragma unroll
     for (int s = 0; s < NS; ++s)
-      kr[s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, base + 64 * s, 0, 0));
+      kr[s] = __builtin_bit_cast(
+          u32x4, stream_loads ? __builtin_amdgcn_raw_buffer_load_b128(rs, base + 64 * s, 0, CPOL_NT)
+                    : __builtin_amdgcn_raw_buffer_load_b128(rs, base + 64 * s, 0, 0));
   };
   u32x4 kr0[KREG ? NS : 1], kr1[KREG ? NS : 1], kr2[KREG ? NS : 1];
   if (tA < nt) {

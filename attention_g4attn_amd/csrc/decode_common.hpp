@@ -18,12 +18,23 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
   return __builtin_amdgcn_make_buffer_rsrc(u, (short)0, (int)n, 0x00020000);
 }
 
+// Cache policy of the cache-row loads.  With one column block per chunk every
+// cache row is read once per launch, so it is loaded non-temporal: keeping it
+// in L2 helps nothing, and the batch-64 decodes ran at 55.4-57.0 us (local)
+// and 792-807 us (global) with the default policy against 52.4-52.5 and
+// 708-769 us non-temporal (same box).  With several column blocks (several
+// query tokens of G = 8 heads) the later blocks of a chunk read it again from
+// L2, and non-temporal loads made the 4-token global decode slower (1448 ->
+// 1643 us), so those keep the default policy.
+constexpr int CPOL_NT = 2;
+
 // 16 bytes at voff of the resource into LDS at ldst + 16 * lane (reads past
-// the resource's size return zeros)
+// the resource's size return zeros); nt: non-temporal (wave-uniform)
 __device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rs, uint32_t voff,
-                                          unsigned char* ldst) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(ldst),
-                                           16, voff, 0, 0, 0);
+                                          unsigned char* ldst, bool nt) {
+  auto* l = (__attribute__((address_space(3))) void*)(ldst);
+  if (nt) __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, l, 16, voff, 0, 0, CPOL_NT);
+  else __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, l, 16, voff, 0, 0, 0);
 }
 
 template <int N>

@@ -180,6 +180,7 @@ decode_fp8_kernel(DecodeArgs a) {
   const uint8_t* kbase = static_cast<const uint8_t*>(a.k) + hoff;
   const uint8_t* vbase = static_cast<const uint8_t*>(a.v) + hoff;
 
+  const bool stream_loads = a.ncb == 1;  // cache rows read once: non-temporal
   // 32 rows of tile i of one tensor into an LDS tile; rows past r1 read as zeros
   auto issue = [&](const uint8_t* base, int i, unsigned char* dst) {
     const int rr0 = r0 + i * TR8;
@@ -193,7 +194,7 @@ decode_fp8_kernel(DecodeArgs a) {
     for (int n = 0; n < NLD; ++n) {
       const int row = n * RPI + ln / CPR;
       const uint32_t voff = (uint32_t)row * D + ((uint32_t)((ln % CPR) ^ fswz(row)) << 4);
-      lds_dma16(rs, voff, dst + n * 1024);
+      lds_dma16(rs, voff, dst + n * 1024, stream_loads);
     }
   };
 
