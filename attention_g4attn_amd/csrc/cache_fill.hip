@@ -30,8 +30,12 @@ __global__ void __launch_bounds__(256) fill_cache_kernel(FillArgs a, int first, 
     const int slot = a.window > 0 ? P % a.capacity : P;
     const size_t src = (((size_t)b * a.S + i) * a.Hkv + g) * a.row_chunks + c;
     const size_t dst = (((size_t)b * a.Hkv + g) * a.capacity + slot) * a.row_chunks + c;
-    static_cast<u32x4*>(a.k_cache)[dst] = static_cast<const u32x4*>(a.k)[src];
-    if (a.v) static_cast<u32x4*>(a.v_cache)[dst] = static_cast<const u32x4*>(a.v)[src];
+    // streaming copy: each chunk is read and written once (non-temporal)
+    __builtin_nontemporal_store(__builtin_nontemporal_load(static_cast<const u32x4*>(a.k) + src),
+                                static_cast<u32x4*>(a.k_cache) + dst);
+    if (a.v)
+      __builtin_nontemporal_store(__builtin_nontemporal_load(static_cast<const u32x4*>(a.v) + src),
+                                  static_cast<u32x4*>(a.v_cache) + dst);
   }
 }
 
@@ -55,10 +59,10 @@ __device__ __forceinline__ u32x4 quantize16(const void* src, size_t e, float s) 
   if constexpr (F32) {
     const f32x4* p = reinterpret_cast<const f32x4*>(static_cast<const float*>(src) + e);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) out[j] = quantize4(p[j], s);
+    for (int j = 0; j < 4; ++j) out[j] = quantize4(__builtin_nontemporal_load(p + j), s);
   } else {
     const u32x4* p = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(src) + e);
-    const u32x4 w0 = p[0], w1 = p[1];
+    const u32x4 w0 = __builtin_nontemporal_load(p), w1 = __builtin_nontemporal_load(p + 1);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const uint32_t lo = j < 2 ? w0[2 * j] : w1[2 * j - 4];
@@ -88,8 +92,11 @@ __global__ void __launch_bounds__(256) fill_cache_fp8_kernel(FillArgs a, int fir
     const int slot = a.window > 0 ? P % a.capacity : P;
     const size_t src = ((((size_t)b * a.S + i) * a.Hkv + g) * a.row_chunks + c) * 16;  // element
     const size_t dst = (((size_t)b * a.Hkv + g) * a.capacity + slot) * a.row_chunks + c;
-    static_cast<u32x4*>(a.k_cache)[dst] = quantize16<F32>(a.k, src, a.k_scale[g]);
-    if (a.v) static_cast<u32x4*>(a.v_cache)[dst] = quantize16<F32>(a.v, src, a.v_scale[g]);
+    __builtin_nontemporal_store(quantize16<F32>(a.k, src, a.k_scale[g]),
+                                static_cast<u32x4*>(a.k_cache) + dst);
+    if (a.v)
+      __builtin_nontemporal_store(quantize16<F32>(a.v, src, a.v_scale[g]),
+                                  static_cast<u32x4*>(a.v_cache) + dst);
   }
 }
 
