@@ -417,7 +417,9 @@ __global__ void __launch_bounds__(NW * 64, (wg_per_cu<D, MB, NST>())) prefill_ke
     if constexpr (RECOMP) asm volatile("" : "+v"(ln), "+s"(wl), "+s"(rb));
     const int r0 = (wl * LPW + n) * RPI;  // first row of this load, wave-uniform
     const int r = r0 + ln / CPR;
-    const uint32_t voff = (uint32_t)r * rb + ((uint32_t)((ln % CPR) ^ swz(r)) << 4);
+    // r < BN and rb <= Hkv * D * 2 < 2^24: a 24-bit multiply (full rate; the
+    // 32-bit product was emitted as a 64-bit multiply-add, once per load)
+    const uint32_t voff = __umul24((uint32_t)r, rb) + ((uint32_t)((ln % CPR) ^ swz(r)) << 4);
     lds_dma16(rs, voff, 0, dst + r0 * RB);
   };
   // loads per wave per tile: slab, raw keys (when the slab does not hold
