@@ -629,11 +629,22 @@ __global__ void __launch_bounds__(NW * 64, (wg_per_cu<D, MB, NST>())) prefill_ke
   };
 
   // one whole tile
+  // With two workgroups per CU, a wave issuing matrix products runs at wave
+  // priority 1 and drops to 0 for the mask and the first softmax half, so the
+  // SIMD's other wave yields issue slots to the products while it is in its
+  // own softmax (window-1024 layer at S = 32768: 0.84 -> 0.82 ms, same box).
+  constexpr bool PRIO = wg_per_cu<D, MB, NST>() == 2;
   auto compute = [&](int kt, auto stage, auto&& side) {
     f32x16 sacc[MB];
+    if constexpr (PRIO) __builtin_amdgcn_s_setprio(1);
     scores(stage, sacc, side);
+    if constexpr (PRIO) __builtin_amdgcn_s_setprio(0);
     mask(kt, sacc);
-    values(stage, [&](u32x4 (&pf)[MB][2], auto k2c) { softmax(sacc, pf, k2c); });
+    values(stage, [&](u32x4 (&pf)[MB][2], auto k2c) {
+      softmax(sacc, pf, k2c);
+      if constexpr (PRIO && decltype(k2c)::value == 0) __builtin_amdgcn_s_setprio(1);
+    });
+    if constexpr (PRIO) __builtin_amdgcn_s_setprio(0);
   };
   // a wave skips tiles where none of its rows sees a key (past its last
   // token, before its window, or padding)
