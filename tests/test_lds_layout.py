@@ -265,3 +265,39 @@ def test_fp8_decode_value_operand_transpose_reads(D):
             grp, i = lane // 16, lane % 16
             got = [code_at(lds, src[16 * grp + 2 * k + i // 8] + i % 8) for k in range(8)]
             assert got == [(8 * grp + k, 16 * db + i) for k in range(8)], (D, db, lane)
+
+
+# ---- staged output rows of the d = 256 prefill epilogue ----
+# A wave writes 16 rows of fp32 output into LDS (lane (l32, hl) writes the
+# 16-byte chunks c = 8*db + 2*g4 + hl of its row l32 - 16p, at chunk c ^ r),
+# then reads each row back whole (lane l reads chunk l of row r, at l ^ r).
+
+@pytest.mark.parametrize("p", [0, 1])
+def test_staged_output_rows(p):
+    D = 256
+    CPR = D * 4 // 16  # 16-byte chunks per fp32 row
+    written = {}
+    for db in range(D // 32):
+        for g4 in range(4):
+            banks = []
+            for lane in range(64):
+                l32, hl = lane & 31, lane >> 5
+                r = l32 - 16 * p
+                if not 0 <= r < 16:
+                    continue
+                c = 8 * db + 2 * g4 + hl
+                pos = r * CPR + (c ^ r)
+                assert pos not in written
+                written[pos] = (r, c)
+                banks.append((lane // 16, ((c ^ r) % 16)))
+            # the 16 lanes served together (one hl, 16 rows) hit 16 distinct bank quads
+            for grp in set(g for g, _ in banks):
+                quads = [q for g, q in banks if g == grp]
+                assert len(quads) == len(set(quads)) == 16
+    assert len(written) == 16 * CPR
+    for r in range(16):
+        got = [written[r * CPR + (lane ^ r)] for lane in range(64)]
+        assert got == [(r, lane) for lane in range(64)]  # row r, chunks in order
+        # a 16-byte read is served 16 lanes at a time: 16 distinct bank quads
+        for g in range(4):
+            assert len({(lane ^ r) % 16 for lane in range(16 * g, 16 * g + 16)}) == 16

@@ -52,3 +52,91 @@ def test_every_tile_load_stays_inside_k(shape):
             assert kv0 * rb + extent <= S * rb
             if kt > kt1:  # padding tile: every key is past the last token
                 assert kt * BN > t_end - 1
+
+
+# ---- decode grid numbering (unit_of_block in decode_common.hpp) ----
+# Blocks map densely onto the (sequence, KV head, chunk) units that hold a
+# visible row: the active chunks of sequence b are those up to its last
+# visible row, none for an out-of-range position (the merge kernel writes its
+# NaN rows), and with one chunk per sequence every (b, KV head) is a unit.
+# The replay follows the kernel's scan 64 sequences at a time and checks that
+# each active unit gets exactly one block per column block and no block gets
+# anything else.
+
+def active_chunks(P, window, capacity, chunk, nchunk):
+    if P < 0 or (window == 0 and P >= capacity):
+        return 0
+    last = min(P, capacity - 1) if window > 0 else P
+    return min(last // chunk + 1, nchunk)
+
+
+def unit_of_block(blk, pos, Hkv, chunk, nchunk, window, capacity, ncb):
+    B = len(pos)
+    if nchunk == 1:
+        nunit = B * Hkv
+    else:
+        nunit = Hkv * sum(active_chunks(p, window, capacity, chunk, nchunk) for p in pos)
+    grp = blk // (8 * ncb)
+    gsz = min(8, nunit - 8 * grp)
+    if gsz <= 0:
+        return None
+    within = blk - grp * 8 * ncb
+    if within >= gsz * ncb:
+        return None
+    unit, cb = 8 * grp + within % gsz, within // gsz
+    if nchunk == 1:
+        return cb, 0, unit // Hkv, unit % Hkv
+    acc = 0
+    for b0 in range(0, B, 64):
+        n = [active_chunks(pos[b], window, capacity, chunk, nchunk) if b < B else 0
+             for b in range(b0, b0 + 64)]
+        incl, run = [], 0
+        for x in n:
+            run += x * Hkv
+            incl.append(run)
+        hits = [l for l in range(64) if acc + incl[l] > unit]
+        if hits:
+            l = hits[0]
+            rem = unit - acc - incl[l] + n[l] * Hkv
+            return cb, rem % n[l], b0 + l, rem // n[l]
+        acc += incl[63]
+    raise AssertionError("unit past every sequence")
+
+
+DECODE_GRIDS = [  # B, Hkv, capacity, window, chunk, ncb, positions (seeded)
+    (64, 2, 65536, 0, 1024, 1, "lengths"),
+    (130, 1, 2500, 0, 1024, 1, "mixed"),
+    (70, 1, 2200, 0, 1024, 4, "mixed"),
+    (3, 2, 3000, 0, 1024, 3, [5000, -1, 2999]),
+    (64, 8, 512, 512, 512, 1, "mixed"),
+    (5, 2, 4096, 0, 1024, 1, [-1, -1, -1, -1, -1]),
+    (200, 2, 4096, 0, 1024, 2, "edges"),
+]
+
+
+@pytest.mark.parametrize("grid", DECODE_GRIDS, ids=[f"B{g[0]}-C{g[2]}-ncb{g[5]}" for g in DECODE_GRIDS])
+def test_decode_units_dense_and_complete(grid):
+    import random
+    B, Hkv, C, W, chunk, ncb, kind = grid
+    rnd = random.Random(B * 7 + C)
+    if kind == "lengths":
+        pos = [rnd.randint(4096, 65536) - 1 for _ in range(B)]
+    elif kind == "mixed":
+        pos = [rnd.randint(-3, C + 50) for _ in range(B)]
+    elif kind == "edges":
+        pos = [rnd.choice([-1, 0, chunk - 1, chunk, C - 1, C]) for _ in range(B)]
+    else:
+        pos = kind
+    nchunk = (C + chunk - 1) // chunk if W == 0 else 1
+    seen = set()
+    for blk in range(B * Hkv * ncb * nchunk):  # the launch's grid
+        u = unit_of_block(blk, pos, Hkv, chunk, nchunk, W, C, ncb)
+        if u is None:
+            continue
+        assert u not in seen, u
+        seen.add(u)
+    want = set()
+    for b, P in enumerate(pos):
+        n = 1 if nchunk == 1 else active_chunks(P, W, C, chunk, nchunk)
+        want |= {(cb, c, b, h) for cb in range(ncb) for c in range(n) for h in range(Hkv)}
+    assert seen == want
