@@ -117,6 +117,29 @@ def test_decode_multi_bf16_output():
     assert np.all(np.abs(got - ref) <= 1e-2 + 2.0 ** -8 * np.abs(ref))
 
 
+def test_decode_multi_many_sequences_two_column_blocks():
+    """70 sequences (two 64-sequence scans of the grid numbering), 3 tokens of
+    G = 8 heads (two column blocks), a 3-chunk K=V cache, lengths from 3 to the
+    capacity and two positions past it (NaN rows)."""
+    layer = inputs.DecodeLayer("global", 70, 16, 2, 512, 2100, 0, 1e6, 0.25)
+    g = torch.Generator()
+    g.manual_seed(11)
+    lengths = torch.randint(3, layer.capacity + 1, (layer.B,), generator=g)
+    lengths[:3] = torch.tensor([3, 1024, layer.capacity])
+    kc, _ = _cache_pair(layer, torch.bfloat16, 960)
+    q = inputs.randn((layer.B, 3, layer.Hq, layer.d), 962, torch.bfloat16, DEV)
+    pos = (lengths - 1).to(torch.int32).to(DEV)
+    bad = [64, 69]
+    pos[bad] = layer.capacity + 3
+    out = g4.decode_multi(q, kc, None, pos, 0, layer.theta, layer.p)
+    torch.cuda.synchronize()
+    assert torch.isnan(out[bad]).all()
+    good = [b for b in range(layer.B) if b not in bad]
+    ref = oracle.decode_multi(to_oracle(q[good]), to_oracle(kc[good]), None,
+                              pos[good].cpu().numpy(), 0, layer.theta, layer.p)
+    assert_parity(out[good], ref, torch.bfloat16, "70 sequences, 3 tokens")
+
+
 @pytest.mark.parametrize("window", [0, 32])
 def test_decode_multi_negative_token_positions_nan(window):
     """pos = 1 with 4 tokens: tokens 0 and 1 sit at -2 and -1 and give NaN rows."""
