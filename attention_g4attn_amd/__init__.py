@@ -50,6 +50,52 @@ def _dev(*ts):
             raise ValueError("tensors must be contiguous")
 
 
+# Metadata checks, run before the placement checks and the C call: the C ABI
+# sees only pointers and sizes, so a tensor of the wrong dtype or shape would
+# be read or written past its end there.
+
+def _shape(t, shape, name):
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _dtype(t, dtypes, name):
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name}: dtype {t.dtype}, expected one of {list(dtypes)}")
+
+
+def _ndim(t, n, name):
+    if t.dim() != n:
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {n} dims")
+
+
+def _like(t, ref, shape, name):
+    """t has ref's dtype and the given shape (t may be None)."""
+    if t is None:
+        return
+    _dtype(t, (ref.dtype,), name)
+    _shape(t, shape, name)
+
+
+def _positions(pos, shape, name="pos"):
+    _dtype(pos, (_torch().int32,), name)
+    _shape(pos, shape, name)
+
+
+def _input(q, n, name="q"):
+    torch = _torch()
+    _dtype(q, (torch.float32, torch.bfloat16), name)
+    _ndim(q, n, name)
+
+
+def _out_ok(out, shape):
+    if out is None:
+        return
+    torch = _torch()
+    _dtype(out, (torch.float32, torch.bfloat16), "out")
+    _shape(out, shape, "out")
+
+
 def _ptr(t):
     return t.data_ptr() if t is not None else None
 
@@ -88,9 +134,15 @@ def _nbytes(t):
 def local_prefill(q, k, v, pos, window, theta=1e4, p=1.0, out=None, out_dtype=None,
                   workspace=None):
     """Causal sliding-window attention, separate K and V (g4attn_local_prefill)."""
-    _dev(q, k, v, pos, out, workspace)
+    _input(q, 4)
     B, S, Hq, d = q.shape
+    _ndim(k, 4, "k")
     Hkv = k.shape[2]
+    _like(k, q, (B, S, Hkv, d), "k")
+    _like(v, q, (B, S, Hkv, d), "v")
+    _positions(pos, (B, S))
+    _out_ok(out, (B, S, Hq, d))
+    _dev(q, k, v, pos, out, workspace)
     out = _out((B, S, Hq, d), out, out_dtype, q.device)
     ws = _workspace(prefill_workspace_bytes(B, S, Hkv, d, p, _code(q)), workspace, q.device)
     rc = _g4lib().g4attn_local_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(pos), B, S, Hq,
@@ -103,9 +155,14 @@ def local_prefill(q, k, v, pos, window, theta=1e4, p=1.0, out=None, out_dtype=No
 def global_prefill(q, kv, pos, window=0, theta=1e6, p=0.25, out=None, out_dtype=None,
                    workspace=None):
     """Causal attention with keys identical to values (g4attn_global_prefill)."""
-    _dev(q, kv, pos, out, workspace)
+    _input(q, 4)
     B, S, Hq, d = q.shape
+    _ndim(kv, 4, "kv")
     Hkv = kv.shape[2]
+    _like(kv, q, (B, S, Hkv, d), "kv")
+    _positions(pos, (B, S))
+    _out_ok(out, (B, S, Hq, d))
+    _dev(q, kv, pos, out, workspace)
     out = _out((B, S, Hq, d), out, out_dtype, q.device)
     ws = _workspace(prefill_workspace_bytes(B, S, Hkv, d, p, _code(q)), workspace, q.device)
     rc = _g4lib().g4attn_global_prefill(_ptr(q), _ptr(kv), _ptr(out), _ptr(pos), B, S, Hq, Hkv, d,
@@ -121,9 +178,17 @@ def vision_prefill(q, k, v, pos2, theta=1e4, lengths=None, out=None, out_dtype=N
     image sees every valid patch of the image, with 2D RoPE driven by
     pos2 [B, S, 2] = (w, h).  lengths [B] int32 (None: all S valid); rows of
     padding patches are zero.  bf16 q, k, v with d = 256."""
-    _dev(q, k, v, pos2, lengths, out, workspace)
+    _input(q, 4)
     B, S, Hq, d = q.shape
+    _ndim(k, 4, "k")
     Hkv = k.shape[2]
+    _like(k, q, (B, S, Hkv, d), "k")
+    _like(v, q, (B, S, Hkv, d), "v")
+    _positions(pos2, (B, S, 2), "pos2")
+    if lengths is not None:
+        _positions(lengths, (B,), "lengths")
+    _out_ok(out, (B, S, Hq, d))
+    _dev(q, k, v, pos2, lengths, out, workspace)
     out = _out(q.shape, out, out_dtype, q.device)
     workspace = _workspace(prefill_workspace_bytes(B, S, Hkv, d, 1.0, _code(q)), workspace,
                            q.device)
@@ -145,10 +210,15 @@ def decode(q, k_cache, v_cache, pos, window, theta, p, out=None, workspace=None,
 
     v_cache None means K=V; window > 0 is a ring cache of `window` slots.
     """
-    torch = _torch()
-    _dev(q, k_cache, v_cache, pos, out, workspace)
+    _input(q, 3)
     B, Hq, d = q.shape
+    _ndim(k_cache, 4, "k_cache")
     _, Hkv, C, _ = k_cache.shape
+    _like(k_cache, q, (B, Hkv, C, d), "k_cache")
+    _like(v_cache, q, (B, Hkv, C, d), "v_cache")
+    _positions(pos, (B,))
+    _out_ok(out, (B, Hq, d))
+    _dev(q, k_cache, v_cache, pos, out, workspace)
     out = _out((B, Hq, d), out, out_dtype, q.device)
     workspace = _workspace(decode_workspace_bytes(B, Hq, Hkv, d, C, window), workspace,
                            q.device)
@@ -172,10 +242,15 @@ def decode_multi(q, k_cache, v_cache, pos, window, theta, p, out=None, workspace
     q is [B, q_len, Hq, d]; pos [B] is the position of the last token; a ring
     (window > 0) needs capacity >= window + q_len - 1.
     """
-    torch = _torch()
-    _dev(q, k_cache, v_cache, pos, out, workspace)
+    _input(q, 4)
     B, L, Hq, d = q.shape
+    _ndim(k_cache, 4, "k_cache")
     _, Hkv, C, _ = k_cache.shape
+    _like(k_cache, q, (B, Hkv, C, d), "k_cache")
+    _like(v_cache, q, (B, Hkv, C, d), "v_cache")
+    _positions(pos, (B,))
+    _out_ok(out, (B, L, Hq, d))
+    _dev(q, k_cache, v_cache, pos, out, workspace)
     out = _out((B, L, Hq, d), out, out_dtype, q.device)
     workspace = _workspace(decode_multi_workspace_bytes(B, L, Hq, Hkv, d, C, window), workspace,
                            q.device)
@@ -192,25 +267,43 @@ def fill_cache(k, v, pos, k_cache, v_cache, window):
 
     v None means K=V (only k_cache is written); window > 0 is a ring.
     """
-    _dev(k, v, pos, k_cache, v_cache)
+    _input(k, 4, "k")
     B, S, Hkv, d = k.shape
+    _like(v, k, (B, S, Hkv, d), "v")
+    _positions(pos, (B, S))
+    _ndim(k_cache, 4, "k_cache")
     C = k_cache.shape[2]
+    _like(k_cache, k, (B, Hkv, C, d), "k_cache")
+    if v is not None:
+        if v_cache is None:
+            raise ValueError("v_cache is required when v is given")
+        _like(v_cache, k, (B, Hkv, C, d), "v_cache")
+    _dev(k, v, pos, k_cache, v_cache)
     rc = _g4lib().g4attn_fill_cache(_ptr(k), _ptr(v), _ptr(pos), B, S, Hkv, d, _ptr(k_cache),
                                   _ptr(v_cache), C, int(window), _code(k), _stream())
     _check(rc, "g4attn_fill_cache")
     return k_cache, v_cache
 
 
-def _fp8_cache(t):
-    if t is not None and t.element_size() != 1:
-        raise TypeError(f"fp8 caches hold one byte per element (uint8 or float8_e4m3fn), got {t.dtype}")
+def _fp8_cache(t, shape=None, name="cache"):
+    if t is None:
+        return
+    torch = _torch()
+    if t.dtype not in (torch.uint8, torch.float8_e4m3fn):
+        raise TypeError(f"{name}: fp8 caches hold one E4M3 code per element (uint8 or "
+                        f"float8_e4m3fn), got {t.dtype}")
+    if shape is not None:
+        _shape(t, shape, name)
 
 
-def _scales(*ts):
+def _scales(Hkv, *ts):
     torch = _torch()
     for t in ts:
-        if t is not None and t.dtype != torch.float32:
+        if t is None:
+            continue
+        if t.dtype != torch.float32:
             raise TypeError(f"scales must be float32, got {t.dtype}")
+        _shape(t, (Hkv,), "scale")
 
 
 def fill_cache_fp8(k, v, pos, k_cache, v_cache, window, k_scale, v_scale=None):
@@ -219,12 +312,21 @@ def fill_cache_fp8(k, v, pos, k_cache, v_cache, window, k_scale, v_scale=None):
 
     v None means K=V (only k_cache is written, v_scale unused).
     """
-    _dev(k, v, pos, k_cache, v_cache, k_scale, v_scale)
-    _fp8_cache(k_cache)
-    _fp8_cache(v_cache)
-    _scales(k_scale, v_scale)
+    _input(k, 4, "k")
     B, S, Hkv, d = k.shape
+    _like(v, k, (B, S, Hkv, d), "v")
+    _positions(pos, (B, S))
+    _ndim(k_cache, 4, "k_cache")
     C = k_cache.shape[2]
+    _fp8_cache(k_cache, (B, Hkv, C, d), "k_cache")
+    if v is not None:
+        if v_cache is None or v_scale is None:
+            raise ValueError("v_cache and v_scale are required when v is given")
+        _fp8_cache(v_cache, (B, Hkv, C, d), "v_cache")
+    if k_scale is None:
+        raise ValueError("k_scale is required")
+    _scales(Hkv, k_scale, v_scale if v is not None else None)
+    _dev(k, v, pos, k_cache, v_cache, k_scale, v_scale)
     rc = _g4lib().g4attn_fill_cache_fp8(_ptr(k), _ptr(v), _ptr(k_scale), _ptr(v_scale), _ptr(pos),
                                         B, S, Hkv, d, _ptr(k_cache), _ptr(v_cache), C,
                                         int(window), _code(k), _stream())
@@ -244,14 +346,21 @@ def decode_fp8(q, k_cache, v_cache, k_scale, v_scale, pos, window, theta, p, out
     per element (uint8 or float8_e4m3fn); k_scale, v_scale are float32 [Hkv];
     v_cache None means K=V (values are k_cache with k_scale).
     """
-    _dev(q, k_cache, v_cache, k_scale, v_scale, pos, out, workspace)
-    _fp8_cache(k_cache)
-    _fp8_cache(v_cache)
-    _scales(k_scale, v_scale)
-    if _code(q) != BF16:
+    if q.dtype != _torch().bfloat16:
         raise TypeError("decode_fp8 takes a bfloat16 query")
+    _ndim(q, 4, "q")
     B, L, Hq, d = q.shape
+    _ndim(k_cache, 4, "k_cache")
     _, Hkv, C, _ = k_cache.shape
+    _fp8_cache(k_cache, (B, Hkv, C, d), "k_cache")
+    _fp8_cache(v_cache, (B, Hkv, C, d), "v_cache")
+    kv_shared = v_cache is None or v_cache is k_cache
+    if k_scale is None or (not kv_shared and v_scale is None):
+        raise ValueError("k_scale (and v_scale for a separate v_cache) are required")
+    _scales(Hkv, k_scale, None if kv_shared else v_scale)
+    _positions(pos, (B,))
+    _out_ok(out, (B, L, Hq, d))
+    _dev(q, k_cache, v_cache, k_scale, v_scale, pos, out, workspace)
     out = _out((B, L, Hq, d), out, out_dtype, q.device)
     workspace = _workspace(decode_fp8_workspace_bytes(B, L, Hq, Hkv, d, C, window), workspace,
                            q.device)

@@ -43,6 +43,11 @@ int check_common(int Hq, int Hkv, int d, int window, float theta, float p, int i
   return G4A_OK;
 }
 
+// The bf16 prefill kernels address a key row inside a tile as row * (Hkv * d
+// * 2 bytes) with a 24-bit multiply, so one token's keys of all KV heads must
+// span fewer than 2^24 bytes (Hkv < 16384 at d = 512, < 32768 at d = 256).
+bool prefill_rows_addressable(int Hkv, int d) { return (long long)Hkv * d * 2 < (1LL << 24); }
+
 int finish(hipError_t e) {
   if (e == hipSuccess) return G4A_OK;
   g_last_hip_error = (int)e;
@@ -95,7 +100,7 @@ int prefill(const void* q, const void* k, const void* v, void* out, const int32_
       prefill_args(q, k, v, out, pos, B, S, Hq, Hkv, d, window, theta, rotated_pairs(d, p));
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (in_dtype == G4A_F32) return finish(g4a::launch_prefill_f32(a, st));
-  if (!g4a::prefill_supported(d)) return G4A_EUNSUPPORTED;
+  if (!g4a::prefill_supported(d) || !prefill_rows_addressable(Hkv, d)) return G4A_EUNSUPPORTED;
   const size_t need = prefill_ws_bytes(B, S, Hkv, d, a.n_rot, in_dtype);
   if (!workspace || workspace_bytes < need) return G4A_EWORKSPACE;
   if (misaligned(workspace)) return G4A_EALIGN;
@@ -135,7 +140,8 @@ G4A_API int g4attn_vision_prefill(const void* q, const void* k, const void* v, v
   if (B < 0 || S < 0) return G4A_EINVAL;
   int rc = check_common(Hq, Hkv, d, 0, theta, 1.f, in_dtype, out_dtype);
   if (rc) return rc;
-  if (in_dtype != G4A_BF16 || d != 256) return G4A_EUNSUPPORTED;
+  if (in_dtype != G4A_BF16 || d != 256 || !prefill_rows_addressable(Hkv, d))
+    return G4A_EUNSUPPORTED;
   if (B == 0 || S == 0) return G4A_OK;
   if (!q || !k || !v || !out || !pos2) return G4A_EINVAL;
   if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(out) || misaligned(pos2) ||

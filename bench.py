@@ -231,7 +231,7 @@ def main():
         kind_rep["group_decode_tok_per_s"] = dloc.B / (5 * tl + tg) * 1e3
 
     if not args.no_configs and not only_fp8:
-        nxt["schedules"] = time_schedules(g4, inputs, torch, kind_rep)
+        nxt["schedules"] = time_schedules(g4, inputs, torch)
 
     roof = None
     if run_global:
@@ -256,7 +256,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline and run_global and run_local:
-        cpu = cpu_baseline(args, loc, glo, L_in[0], G_in, L_out[0], G_out)
+        cpu = cpu_baseline(args, loc, glo, L_in[0], G_in, L_out[0], G_out, 5 * fl_loc + fl_glo)
 
     rec = {
         "metric": "attention TFLOP/s (prefill) + decode tok/s, as % of MFMA / HBM roofline",
@@ -483,14 +483,19 @@ SCHEDULES = {
 }
 
 
-def time_schedules(g4, inputs, torch, kinds, reps=2):
-    """Prefill and one decode step of every layer of each schedule, from
-    per-layer timings: the layers of a kind at one context cost the same."""
-    res, cache = {}, {}
+def time_schedules(g4, inputs, torch, reps=2, dec_reps=4):
+    """Prefill and one batch-64 decode step of every layer of each schedule.
+    Every layer kind is timed at the schedule's own geometry: the local prefill
+    at its window and context, the global prefill at the context, the local
+    decode over full rings of `window` slots, and the global decode over
+    linear K=V caches of the context's length with cache lengths uniform in
+    [4096, context].  Layers of one kind at one geometry cost the same, so a
+    stack's time is the per-layer time times its layer count."""
+    res, pre_cache, dec_cache = {}, {}, {}
 
     def prefill_ms(layer):
         key = (layer.kind, layer.S, layer.window)
-        if key not in cache:
+        if key not in pre_cache:
             q, k, v, pos = inputs.prefill_inputs(layer, 80, 0, torch.bfloat16, "cuda")
             out = torch.empty(q.shape, dtype=torch.float32, device="cuda")
             ws = torch.empty(max(16, g4.prefill_workspace_bytes(layer.B, layer.S, layer.Hkv,
@@ -502,9 +507,34 @@ def time_schedules(g4, inputs, torch, kinds, reps=2):
             else:
                 f = lambda r: g4.local_prefill(q, k, v, pos, layer.window, layer.theta, layer.p,
                                                out=out, workspace=ws)
-            cache[key] = _event_time(torch, f, reps)
+            pre_cache[key] = _event_time(torch, f, reps)
             del q, k, v, pos, out, ws
-        return cache[key]
+        return pre_cache[key]
+
+    def decode_us(layer, lengths):
+        """(us per call, algorithmic bytes) of one batch-64 decode launch; ring
+        layers rotate over two cache copies (distinct layers' caches)."""
+        key = (layer.kind, layer.capacity, layer.window)
+        if key not in dec_cache:
+            ncopy = 2 if layer.window > 0 else 1
+            sets = [inputs.decode_inputs(layer, 82 + i, 0, torch.bfloat16, "cuda", lengths)
+                    for i in range(ncopy)]
+            out = torch.empty(sets[0][0].shape, dtype=torch.float32, device="cuda")
+            ws = torch.empty(max(16, g4.decode_workspace_bytes(layer.B, layer.Hq, layer.Hkv,
+                                                               layer.d, layer.capacity,
+                                                               layer.window)),
+                             dtype=torch.uint8, device="cuda")
+
+            def f(r):
+                q, kc, vc, pos, _ = sets[r % ncopy]
+                g4.decode(q, kc, vc, pos, layer.window, layer.theta, layer.p, out=out,
+                          workspace=ws)
+            ms = _event_time(torch, f, dec_reps)
+            _, byts = decode_cost(layer, lengths)
+            dec_cache[key] = (ms * 1e3, byts)
+            del sets, out, ws
+            torch.cuda.empty_cache()
+        return dec_cache[key]
 
     for name, sc in SCHEDULES.items():
         n_glob = sc["layers"] // (sc["ratio"] + 1)
@@ -516,22 +546,43 @@ def time_schedules(g4, inputs, torch, kinds, reps=2):
         entry = {"layers": sc["layers"], "local_layers": n_loc, "global_layers": n_glob,
                  "window": sc["window"], "context": sc["S"], "prefill_ms": t_pre,
                  "prefill_tflops": fl / t_pre / 1e9}
-        # decode: local layers are 512-slot rings at window 512 (measured in
-        # the step); a 1024-slot ring reads twice the bytes at the same rate
-        if "local_decode" in kinds and "global_decode" in kinds:
-            tl = kinds["local_decode"]["us"] * sc["window"] / 512
-            tg = kinds["global_decode"]["us"]
-            step = n_loc * tl + n_glob * tg
-            entry.update({"decode_step_us": step, "decode_tok_per_s": 64 / step * 1e6,
-                          "decode_note": "batch 64; local time scaled by window / 512"})
+        b = inputs.DECODE_LOCAL.B
+        dl = inputs.DecodeLayer("local", b, 16, 8, 256, sc["window"], sc["window"],
+                                inputs.LOCAL_THETA, 1.0)
+        dg = inputs.DecodeLayer("global", b, 16, 2, 512, sc["S"], 0, inputs.GLOBAL_THETA, 0.25)
+        lengths = inputs.decode_lengths(b, 4009, 4096, sc["S"])
+        tl, bl = decode_us(dl, lengths)
+        tg, bg = decode_us(dg, lengths)
+        step = n_loc * tl + n_glob * tg
+        entry.update({"decode_step_us": step, "decode_tok_per_s": b / step * 1e6,
+                      "decode_local_us": tl, "decode_local_frac_hbm": bl / tl / 1e3 / HBM_PEAK_GBS,
+                      "decode_global_us": tg,
+                      "decode_global_frac_hbm": bg / tg / 1e3 / HBM_PEAK_GBS,
+                      "decode_global_mean_len": float(lengths.double().mean()),
+                      "decode_note": f"batch {b}; local ring of {sc['window']} slots, global "
+                                     f"K=V cache of {sc['S']} rows, lengths U[4096, {sc['S']}]; "
+                                     f"each kind timed at this geometry"})
         res[name] = entry
     return res
 
 
-def cpu_baseline(args, loc, glo, L0, G0, Lout, Gout):
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_baseline(args, loc, glo, L0, G0, Lout, Gout, step_prefill_flops):
     """The fp64 oracle, untuned, on a bounded sample of rows of the same
-    workload (first local layer and the global layer); also reports the
-    parity of those rows against the GPU outputs of the run."""
+    workload (first local layer and the global layer), on every host thread
+    and then on one; also reports the parity of those rows against the GPU
+    outputs of the run.  The rates are measured over the row sample; the time
+    of the whole prefill group is extrapolated from them by the ratio of
+    algorithmic FLOPs."""
     import numpy as np
     import torch
 
@@ -539,7 +590,7 @@ def cpu_baseline(args, loc, glo, L0, G0, Lout, Gout):
     from tests.helpers import to_oracle
 
     S = loc.S
-    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    threads = oracle.threads()
     qg, kvg, _, posg = G0
     ql, kl, vl, posl = L0
     t0 = time.time()
@@ -572,14 +623,36 @@ def cpu_baseline(args, loc, glo, L0, G0, Lout, Gout):
             break
         n_g = max(n_g + 1, min(4096, int(n_g * args.cpu_seconds / max(t, 1e-3))))
     f = flops(rows_g, rows_l)
+    print(f"# oracle sample on {threads} threads: {t:.1f}s", file=sys.stderr, flush=True)
     got_g = Gout.view(S, glo.Hq, glo.d)[torch.as_tensor(rows_g, device=Gout.device)]
     got_l = Lout.view(S, loc.Hq, loc.d)[torch.as_tensor(rows_l, device=Lout.device)]
     eg = np.abs(got_g.double().cpu().numpy() - og)
     el = np.abs(got_l.double().cpu().numpy() - ol)
-    return {"value": f / t / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "seconds": t,
-            "sample": f"{len(rows_g)} query rows (all 16 heads) of the global layer and "
-                      f"{len(rows_l)} rows of the first local layer, S={S}; fp64, OpenMP",
+    # one thread: a smaller sample of the same kinds of rows, about a third of
+    # the CPU seconds
+    oracle.set_threads(1)
+    try:
+        n1 = max(1, int(len(rows_g) * args.cpu_seconds / 3 / max(t * threads, 1e-3)))
+        r1g = rng.choice(S, n1, replace=False)
+        r1l = rng.choice(S, 8 * n1, replace=False)
+        t1, _, _ = run(r1g, r1l)
+        f1 = flops(r1g, r1l)
+    finally:
+        oracle.set_threads(threads)
+    print(f"# oracle sample on 1 thread: {t1:.1f}s", file=sys.stderr, flush=True)
+    rate, rate1 = f / t, f1 / t1
+    return {"value": rate / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "cpu_model": cpu_model(), "host_cpus": os.cpu_count(), "seconds": t,
+            "sample": f"row sample: {len(rows_g)} query rows (all 16 heads) of the global layer "
+                      f"and {len(rows_l)} rows of the first local layer, S={S}; fp64, OpenMP on "
+                      f"{threads} threads; the rate is the sample's algorithmic FLOPs over its "
+                      f"time",
+            "one_thread": {"value": rate1 / 1e12, "unit": "TFLOP/s", "seconds": t1,
+                           "sample": f"{len(r1g)} global rows and {len(r1l)} local rows"},
+            "extrapolated_group_prefill_s": step_prefill_flops / rate,
+            "extrapolated_group_prefill_s_one_thread": step_prefill_flops / rate1,
+            "extrapolation": "whole prefill of the 5:1 group (5 local + 1 global layer) at the "
+                             "sample's rate, scaled by algorithmic FLOPs; not measured",
             "parity_sample": {"global_max_abs": float(eg.max()), "global_mean_abs": float(eg.mean()),
                               "local_max_abs": float(el.max()), "local_mean_abs": float(el.mean())}}
 

@@ -44,7 +44,9 @@
  *     fp32 accumulation; f32 inputs are computed in fp32 throughout.
  *   - Supported shapes: d in {256, 512} for bf16 inputs, d in {64, 128, 256,
  *     512} for f32 inputs; G = Hq / Hkv in {1, 2, 4, 8}; other combinations
- *     return G4A_EUNSUPPORTED.
+ *     return G4A_EUNSUPPORTED.  The bf16 prefill calls (causal and vision)
+ *     also need Hkv * d * 2 < 2^24 (one token's keys of all KV heads under
+ *     16 MiB: Hkv < 16384 at d = 512) and return G4A_EUNSUPPORTED otherwise.
  */
 #ifndef G4ATTN_H
 #define G4ATTN_H
@@ -81,6 +83,14 @@ extern "C" {
 size_t g4attn_prefill_workspace_bytes(int B, int S, int Hkv, int d, float p, int in_dtype);
 
 /*
+ * Both causal prefill calls take the arguments the pages' statement of the
+ * problem names (q, k/v or kv, positions, window, group size via Hq/Hkv, head
+ * dim, theta, p) plus a workspace, sized by g4attn_prefill_workspace_bytes.
+ * The workspace is an extension of that statement: keys are rotated once
+ * each, by one pass into the workspace, instead of in every key tile load of
+ * every query tile that reads them (about S/32 times per key for a global
+ * layer), which measured faster and frees the attention kernel's registers.
+ *
  * Sliding-window (local) causal prefill with separate keys and values.
  *   q    [B, S, Hq,  d]  in_dtype        k, v [B, S, Hkv, d]  in_dtype
  *   out  [B, S, Hq,  d]  out_dtype       pos  [B, S] int32 token positions
@@ -115,14 +125,12 @@ int g4attn_global_prefill(const void* q, const void* kv, void* out, const int32_
 
 /*
  * Vision-encoder attention: every patch of an image attends to every patch
- * of the image (no causal mask), with 2D RoPE.  The encoder turns an image
- * into 16x16-pixel patches; 2D RoPE splits the embedding in two parts that
- * encode the horizontal (w) and vertical (h) positions separately ("Guia
- * visual do Gemma 4", sections "Encoder de visao" and "Suporte a proporcao
- * variavel").  Here half c of the head dims ([0, d/2) for c = 0, [d/2, d) for
- * c = 1) is an ordinary RoPE of a head of dim d/2, pair t = dims (2t, 2t+1)
- * of the half turning by pos2[..., c] * theta^(-2t/(d/2)); component 0 is w,
- * component 1 is h.
+ * of the image (no causal mask), with 2D RoPE ("Guia visual do Gemma 4",
+ * sections "Encoder de visao" and "Suporte a proporcao variavel").  Half c of
+ * the head dims ([0, d/2) for c = 0, [d/2, d) for c = 1) is an ordinary RoPE
+ * of a head of dim d/2, pair t = dims (2t, 2t+1) of the half turning by
+ * pos2[..., c] * theta^(-2t/(d/2)); component 0 is the patch's column w,
+ * component 1 its row h.
  *   q    [B, S, Hq, d]  bf16          k, v [B, S, Hkv, d]  bf16
  *   out  [B, S, Hq, d]  out_dtype     pos2 [B, S, 2] int32 (w, h) per patch
  *   lengths [B] int32, or NULL (every image has S patches): image b has

@@ -51,6 +51,10 @@ def load(path):
     lib.g4o_e4m3_encode.restype = I
     lib.g4o_quantize_e4m3.argtypes = [P, I, P, L, I, I, P]
     lib.g4o_quantize_e4m3.restype = I
+    lib.g4o_threads.argtypes = []
+    lib.g4o_threads.restype = I
+    lib.g4o_set_threads.argtypes = [I]
+    lib.g4o_set_threads.restype = None
     return lib
 
 
@@ -82,6 +86,16 @@ def _in(a, f64=False):
 
 def _ptr(a):
     return a.ctypes.data_as(ctypes.c_void_p) if a is not None else None
+
+
+def threads(lib=None):
+    """Threads the oracle's OpenMP loops use."""
+    return int(_lib(lib).g4o_threads())
+
+
+def set_threads(n, lib=None):
+    """Use n threads in the oracle's OpenMP loops from now on."""
+    _lib(lib).g4o_set_threads(int(n))
 
 
 def nrot(d, p, lib=None):

@@ -544,11 +544,10 @@ int g4o_quantize_e4m3(const void* x, int dtype, const float* scale, int64_t rows
 /*
  * Vision-encoder attention: 2D RoPE and no causal mask.
  *
- * The vision encoder turns an image into a sequence of 16x16-pixel patches
- * and encodes each patch's position with 2D RoPE, which splits the embedding
- * in two parts and encodes the horizontal (w) and the vertical (h) position
- * separately ("Guia visual do Gemma 4", sections "Encoder de visao" and
- * "Suporte a proporcao variavel").  Readings taken where the page is silent:
+ * Each patch carries a two-component grid position (w, h); head dims
+ * [0, d/2) rotate by component w and [d/2, d) by component h ("Guia visual do
+ * Gemma 4", sections "Encoder de visao" and "Suporte a proporcao variavel").
+ * Readings taken where the page is silent:
  *  - the head dim d is split into halves [0, d/2) and [d/2, d); half c is an
  *    ordinary RoPE of a head of dim d/2 (pairs (2t, 2t+1) of the half, angle
  *    pos_c * theta^(-2t/(d/2)), counter-clockwise) driven by position
@@ -625,4 +624,17 @@ int g4o_vision_prefill(const void* q, const void* k, const void* v, int dtype,
     free(qr); free(kr); free(sc);
   }
   return err ? G4O_ENOMEM : G4O_OK;
+}
+
+/*
+ * Threads of the OpenMP loops above: the count in use, and a setter so that a
+ * caller can time the oracle on one thread as well as on all of them.  No
+ * arithmetic.
+ */
+#include <omp.h>
+
+int g4o_threads(void) { return omp_get_max_threads(); }
+
+void g4o_set_threads(int n) {
+  if (n > 0) omp_set_num_threads(n);
 }

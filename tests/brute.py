@@ -31,21 +31,26 @@ def mask_matrix(S, window):
     return m
 
 
-def attention(q, k, v, pos, window, theta, n_rot):
-    """q [B,S,Hq,d], k/v [B,S,Hkv,d] float64; returns [B,S,Hq,d]."""
+def probabilities(q, k, pos, window, theta, n_rot):
+    """Dense softmax weights [B, Hq, S(query), S(key)], 0 where masked."""
     B, S, Hq, d = q.shape
     Hkv = k.shape[2]
     G = Hq // Hkv
     qr = rotate(q, pos, theta, n_rot)
-    kr = rotate(k, pos, theta, n_rot)
-    kr = np.repeat(kr, G, axis=2)
-    vv = np.repeat(v, G, axis=2)
+    kr = np.repeat(rotate(k, pos, theta, n_rot), G, axis=2)
     sc = np.einsum("bihd,bjhd->bhij", qr, kr) / np.sqrt(d)
     m = mask_matrix(S, window)
     sc = np.where(m[None, None], sc, -np.inf)
     sc = sc - sc.max(axis=-1, keepdims=True)
     w = np.exp(sc)
-    w = w / w.sum(axis=-1, keepdims=True)
+    return w / w.sum(axis=-1, keepdims=True)
+
+
+def attention(q, k, v, pos, window, theta, n_rot):
+    """q [B,S,Hq,d], k/v [B,S,Hkv,d] float64; returns [B,S,Hq,d]."""
+    G = q.shape[2] // k.shape[2]
+    w = probabilities(q, k, pos, window, theta, n_rot)
+    vv = np.repeat(v, G, axis=2)
     return np.einsum("bhij,bjhd->bihd", w, vv)
 
 

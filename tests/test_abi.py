@@ -264,3 +264,14 @@ def test_vision_prefill_lengths_may_be_null_and_empty_is_noop():
     assert vis(ln=None, ws_bytes=1000) == -4  # passes the other checks
     assert vis(S=0, q=None, k=None, v=None, out=None, pos=None, ln=None, ws=None) == 0
     assert vis(B=0, q=None, k=None, v=None, out=None, pos=None, ln=None, ws=None) == 0
+
+
+def test_prefill_rejects_key_rows_past_the_24_bit_row_offset():
+    """The bf16 prefill kernels compute a key row's offset inside a tile with a
+    24-bit multiply, so Hkv * d * 2 must stay below 2^24 bytes."""
+    big = 1 << 14  # Hkv * 512 * 2 = 2^24 at d = 512; 2^23 at d = 256 still fits
+    assert glob(Hq=big * 8, Hkv=big) == -2
+    assert glob(Hq=(big - 1) * 8, Hkv=big - 1, ws=None) == -4  # fits; fails on the workspace
+    assert local(Hq=2 * big, Hkv=big, ws=None) == -4  # d = 256: 2^23 bytes fit
+    assert local(Hq=4 * big, Hkv=2 * big) == -2
+    assert vis(Hq=2 * big, Hkv=2 * big) == -2

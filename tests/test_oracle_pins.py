@@ -9,8 +9,9 @@
 - invariants: W >= S equals W = 0; GQA equals MHA with repeated KV heads;
   K=V equals the standard path fed v := k; p = 1 rotates every pair; the
   rotation is orthogonal and additive in the position; outputs are invariant
-  under a common position shift; probability rows sum to 1 with exactly the
-  window's keys non-zero; decode equals the last prefill row; a ring cache
+  under a common position shift; probability rows equal the dense brute-force
+  softmax weights, sum to 1 with exactly the window's keys non-zero, and times
+  the values give the prefill's output row; decode equals the last prefill row; a ring cache
   equals a linear one; writing a prefill's rows into a cache (in two parts, as
   a prompt and then new tokens) and decoding the last L tokens at once
   reproduces those prefill rows; one query token equals ordinary decode;
@@ -224,18 +225,42 @@ def test_relative_position_invariance():
     np.testing.assert_allclose(a, b, rtol=0, atol=1e-9)
 
 
-def test_probability_rows_sum_to_one_over_the_window():
-    B, S, Hq, Hkv, d = 1, 30, 4, 2, 16
-    q, k = rnd((B, S, Hq, d), 91), rnd((B, S, Hkv, d), 92)
-    pos = np.arange(S, dtype=np.int32)[None]
-    for W in (0, 1, 4, 29):
-        for i in (0, 3, 4, 17, 29):
-            for h in (0, 3):
-                pr = oracle.probs(q, k, pos, W, 1e4, 1.0, 0, i, h)
-                assert abs(pr.sum() - 1.0) < 1e-14
-                lo = 0 if W == 0 else max(0, i - W + 1)
-                nz = np.nonzero(pr)[0]
-                assert nz.min() == lo and nz.max() == i and nz.size == i - lo + 1
+PROB_CASES = [
+    # B, S, Hq, Hkv, d, theta, p (G = 1, 2, 4, 8; full, partial and no rotation)
+    (1, 30, 4, 2, 16, 1e4, 1.0),
+    (2, 21, 8, 1, 32, 1e6, 0.25),
+    (1, 19, 4, 1, 16, 1e4, 0.5),
+    (1, 17, 3, 3, 8, 1e4, 0.0),
+]
+
+
+@pytest.mark.parametrize("case", PROB_CASES)
+def test_probability_rows_are_the_weights_of_the_prefill(case):
+    """g4o_probs against the dense brute-force softmax weights (value pin, so a
+    dropped 1/sqrt(d), a wrong key rotation or a wrong GQA map fails it);
+    every row sums to 1 with exactly the window's keys non-zero; and the row
+    times the raw values reproduces g4o_prefill's output row, so the weights
+    pinned here are the ones the prefill uses."""
+    B, S, Hq, Hkv, d, theta, p = case
+    q, k, v = rnd((B, S, Hq, d), 91), rnd((B, S, Hkv, d), 92), rnd((B, S, Hkv, d), 93)
+    pos = (np.arange(S, dtype=np.int32) + 37)[None].repeat(B, 0)
+    G = Hq // Hkv
+    n_rot = int(math.floor(p * d / 2))
+    for W in (0, 1, 4, S - 1):
+        want = brute.probabilities(q.astype(np.float64), k.astype(np.float64), pos, W, theta,
+                                   n_rot)
+        out = oracle.prefill(q, k, v, pos, W, theta, p)
+        for b in range(B):
+            for i in (0, 3, 4, S // 2, S - 1):
+                for h in sorted({0, G - 1, Hq - 1}):
+                    pr = oracle.probs(q, k, pos, W, theta, p, b, i, h)
+                    np.testing.assert_allclose(pr, want[b, h, i], rtol=0, atol=1e-12)
+                    assert abs(pr.sum() - 1.0) < 1e-14
+                    lo = 0 if W == 0 else max(0, i - W + 1)
+                    nz = np.nonzero(pr)[0]
+                    assert nz.min() == lo and nz.max() == i and nz.size == i - lo + 1
+                    row = pr @ v[b, :, h // G].astype(np.float64)
+                    np.testing.assert_allclose(row, out[b, i, h], rtol=0, atol=1e-12)
 
 
 def _sequence(B, L, Hq, Hkv, d, seed):
@@ -397,6 +422,13 @@ MUTANTS = {
     "key_rotated_with_table_sign": ("kr[2 * t + 1] = x0 * c[2 * t + 1] + x1 * c[2 * t];",
                                     "kr[2 * t + 1] = -x0 * c[2 * t + 1] + x1 * c[2 * t];"),
     "rotated_values": ("o[e] += w * g4o_in(v, dtype, voff + e);", "o[e] += w * kr[e];"),
+    "probs_dropped_scale": ("probs[j] = s / sqrt((double)d);", "probs[j] = s;"),
+    "probs_gqa_mapping": ("const int G = Hq / Hkv, g = h / G, n_rot = g4o_nrot(d, p);\n  double* qr",
+                          "const int G = Hq / Hkv, g = h % Hkv, n_rot = g4o_nrot(d, p);\n  double* qr"),
+    "probs_key_unrotated": ("g4o_rope(kr, d, n_rot, theta, (double)pos[(size_t)b * S + j]);\n    double s",
+                            "double s"),
+    "probs_window_off_by_one": ("if (j < j0 || j > i) { probs[j] = -INFINITY; continue; }",
+                                "if (j <= j0 || j > i) { probs[j] = -INFINITY; continue; }"),
     "multi_query_position": ("Pj = P - L + 1 + j;", "Pj = P - L + j;"),
     "multi_ring_slot_by_window": ("const int64_t slot = window > 0 ? t % capacity : t;\n          const size_t koff",
                                   "const int64_t slot = window > 0 ? t % window : t;\n          const size_t koff"),
@@ -445,4 +477,11 @@ def test_mutant_is_caught(name, mutant_dir):
         got, want = _closed_loop(B=1, S=S, L=L, Hq=4, Hkv=2, d=16, W=W, C=C, theta=1e4, p=1.0,
                                  kv_shared=False, seed=77, lib=lib)
         caught |= not np.allclose(got, want, rtol=0, atol=1e-12, equal_nan=False)
+    # the probability rows against the dense brute-force weights
+    for W in (0, 5):
+        want = brute.probabilities(q.astype(np.float64), k.astype(np.float64), pos, W, theta,
+                                   d // 2)
+        for i, h in ((11, 3), (7, 6)):
+            pr = oracle.probs(q, k, pos, W, theta, p, 0, i, h, lib=lib)
+            caught |= not np.allclose(pr, want[0, h, i], rtol=0, atol=1e-12)
     assert caught, f"mutant {name} survived the pins"

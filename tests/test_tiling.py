@@ -33,6 +33,11 @@ SHAPES = [  # S, Hkv, D, G, MB, W, NST
     (129, 1, 512, 2, 1, 0, 3), (190, 2, 512, 4, 1, 40, 2), (1, 1, 512, 8, 1, 0, 3),
     (33, 8, 256, 1, 2, 1, 3), (262144, 2, 512, 8, 1, 0, 3), (262144, 8, 256, 2, 2, 1024, 3),
     (8192, 8, 256, 2, 2, 1024, 3), (32768, 4, 512, 8, 1, 0, 3),
+    # the shipped d = 256 instance (local layers and the vision encoder): one
+    # 32-row block per wave, 2-stage ring, two workgroups per CU
+    (8192, 8, 256, 2, 1, 1024, 2), (262144, 8, 256, 2, 1, 1024, 2), (131072, 8, 256, 2, 1, 512, 2),
+    (1100, 8, 256, 2, 1, 512, 2), (333, 2, 256, 2, 1, 64, 2), (97, 8, 256, 1, 1, 0, 2),
+    (2520, 8, 256, 1, 1, 0, 2), (10080, 8, 256, 1, 1, 0, 2), (700, 1, 256, 8, 1, 0, 2),
 ]
 
 
@@ -52,6 +57,34 @@ def test_every_tile_load_stays_inside_k(shape):
             assert kv0 * rb + extent <= S * rb
             if kt > kt1:  # padding tile: every key is past the last token
                 assert kt * BN > t_end - 1
+
+
+VISION_SHAPES = [  # S, Hkv, G, valid patches per image
+    (2520, 8, 1, [2520, 2520, 2520, 2496]), (10080, 8, 1, [10080]), (300, 2, 2, [300, 1, 0, 33]),
+    (1100, 1, 8, [1099, 1100, 64, 65]),
+]
+
+
+@pytest.mark.parametrize("shape", VISION_SHAPES)
+def test_vision_tile_loads_stay_inside_k(shape):
+    """Vision instance (no causal mask): every query tile walks key tiles 0 ..
+    (n_b - 1) / 32 of its image, padded to the 2-deep ring; an empty image
+    loads nothing."""
+    S, Hkv, G, lengths = shape
+    D, NST = 256, 2
+    rb = Hkv * D * 2
+    for nv in lengths:
+        if nv == 0:
+            continue
+        kt0, kt1 = 0, (nv - 1) // BN
+        ktp = kt0 + (kt1 - kt0 + NST) // NST * NST - 1
+        for kt in range(kt0, ktp + 1):
+            kv0, rows = tile_rows(kt, S)
+            assert 1 <= rows <= BN
+            extent = rows * rb - (rb - 2 * D)
+            assert 0 < extent <= BN * rb and kv0 * rb + extent <= S * rb
+            if kt > kt1:  # padding tile: every key is past the image's patches
+                assert kt * BN >= nv
 
 
 # ---- decode grid numbering (unit_of_block in decode_common.hpp) ----
