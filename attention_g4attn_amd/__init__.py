@@ -14,7 +14,7 @@ from ._lib import lib as _g4lib
 
 F32, BF16 = 0, 1
 STATUS = {0: "G4A_OK", -1: "G4A_EINVAL", -2: "G4A_EUNSUPPORTED", -3: "G4A_EALIGN",
-          -4: "G4A_EWORKSPACE", -5: "G4A_EHIP"}
+          -4: "G4A_EWORKSPACE", -5: "G4A_EHIP", -6: "G4A_ESCRATCH"}
 
 
 class G4AttnError(RuntimeError):
@@ -227,6 +227,28 @@ def decode(q, k_cache, v_cache, pos, window, theta, p, out=None, workspace=None,
                               Hkv, d, C, int(window), float(theta), float(p), _code(q),
                               _code(out), _ptr(workspace), nbytes, _stream())
     _check(rc, "g4attn_decode")
+    return out
+
+
+def decode_noalloc(q, k_cache, v_cache, pos, window, theta, p, out):
+    """g4attn_decode with its partials in the library's fixed 64 MiB device
+    scratch instead of a workspace: the call allocates nothing, so `out` must
+    be given.  Calls that overlap on one GPU race on the shared scratch."""
+    if out is None:
+        raise ValueError("decode_noalloc allocates nothing: pass out")
+    _input(q, 3)
+    B, Hq, d = q.shape
+    _ndim(k_cache, 4, "k_cache")
+    _, Hkv, C, _ = k_cache.shape
+    _like(k_cache, q, (B, Hkv, C, d), "k_cache")
+    _like(v_cache, q, (B, Hkv, C, d), "v_cache")
+    _positions(pos, (B,))
+    _out_ok(out, (B, Hq, d))
+    _dev(q, k_cache, v_cache, pos, out)
+    rc = _g4lib().g4attn_decode_noalloc(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out),
+                                        _ptr(pos), B, Hq, Hkv, d, C, int(window), float(theta),
+                                        float(p), _code(q), _code(out), _stream())
+    _check(rc, "g4attn_decode_noalloc")
     return out
 
 

@@ -18,6 +18,7 @@ SIGNATURES = {
     "g4attn_vision_prefill": ([P, P, P, P, P, P, I, I, I, I, I, F, I, I, P, Z, P], I),
     "g4attn_decode": ([P, P, P, P, P, I, I, I, I, I, I, F, F, I, I, P, Z, P], I),
     "g4attn_decode_workspace_bytes": ([I, I, I, I, I, I], Z),
+    "g4attn_decode_noalloc": ([P, P, P, P, P, I, I, I, I, I, I, F, F, I, I, P], I),
     "g4attn_decode_multi": ([P, P, P, P, P, I, I, I, I, I, I, I, F, F, I, I, P, Z, P], I),
     "g4attn_decode_multi_workspace_bytes": ([I, I, I, I, I, I, I], Z),
     "g4attn_fill_cache": ([P, P, P, I, I, I, I, P, P, I, I, I, P], I),

@@ -238,6 +238,33 @@ int decode(const void* q, const void* k_cache, const void* v_cache, void* out,
 
 }  // namespace
 
+G4A_API int g4attn_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                  void* out, const int32_t* pos, int B, int Hq, int Hkv, int d,
+                                  int capacity, int window, float theta, float p, int in_dtype,
+                                  int out_dtype, void* stream) {
+  // Sizes are checked against the fixed buffer before any HIP call; the rest
+  // of the validation is g4attn_decode's.
+  const bool bf16 = in_dtype == G4A_BF16;
+  size_t need = 0;
+  if (bf16) {
+    need = decode_ws_bytes(B, 1, Hq, Hkv, d, capacity, window, false);
+    if (need > g4a::kDecodeScratchBytes) return G4A_ESCRATCH;
+  }
+  if (B <= 0 || !bf16) {  // nothing launched, or the fp32 path (no partials)
+    return decode(q, k_cache, v_cache, out, pos, B, 1, Hq, Hkv, d, capacity, window, theta, p,
+                  in_dtype, out_dtype, nullptr, 0, stream, false);
+  }
+  if (need == 0) return G4A_EINVAL;  // sizes the workspace query rejects
+  int rc = check_common(Hq, Hkv, d, window, theta, p, in_dtype, out_dtype);
+  if (rc) return rc;
+  if (!q || !k_cache || !out || !pos) return G4A_EINVAL;
+  void* ws = nullptr;
+  const hipError_t e = g4a::decode_scratch(&ws);
+  if (e != hipSuccess) return finish(e);
+  return decode(q, k_cache, v_cache, out, pos, B, 1, Hq, Hkv, d, capacity, window, theta, p,
+                in_dtype, out_dtype, ws, g4a::kDecodeScratchBytes, stream, false);
+}
+
 G4A_API size_t g4attn_decode_workspace_bytes(int B, int Hq, int Hkv, int d, int capacity,
                                              int window) {
   return decode_ws_bytes(B, 1, Hq, Hkv, d, capacity, window, false);
@@ -390,6 +417,9 @@ G4A_API const char* g4attn_strerror(int status) {
     case G4A_EALIGN: return "tensor pointer not 16-byte aligned";
     case G4A_EWORKSPACE: return "workspace missing or too small";
     case G4A_EHIP: return "HIP launch failed (see g4attn_last_hip_error)";
+    case G4A_ESCRATCH:
+      return "decode partials exceed the library's fixed 64 MiB scratch; use g4attn_decode "
+             "with a workspace";
   }
   return "unknown status";
 }

@@ -91,6 +91,12 @@ hipError_t launch_decode_fp8(const DecodeArgs& a, bool kv_shared, bool out_bf16,
 hipError_t launch_fill_cache(const FillArgs& a, hipStream_t st);
 hipError_t launch_fill_cache_fp8(const FillArgs& a, hipStream_t st);
 
+// Fixed per-device scratch of the decode that allocates nothing (64 MiB):
+// decode_scratch returns its device address on the current device, looked up
+// once per device.
+constexpr size_t kDecodeScratchBytes = size_t(64) << 20;
+hipError_t decode_scratch(void** ptr);
+
 // rows of the cache one decode workgroup covers, and chunks per (b, kv head)
 int decode_chunk_rows(int D, int capacity, int window, bool f32);
 int decode_num_chunks(int D, int capacity, int window, bool f32);

@@ -66,6 +66,7 @@ extern "C" {
 #define G4A_EALIGN (-3)      /* a tensor or workspace pointer is not 16-byte aligned */
 #define G4A_EWORKSPACE (-4)  /* workspace missing or smaller than the size query says */
 #define G4A_EHIP (-5)        /* the HIP runtime refused a launch; see g4attn_last_hip_error */
+#define G4A_ESCRATCH (-6)    /* g4attn_decode_noalloc: the partials exceed its fixed scratch */
 
 /* dtype codes */
 #define G4A_F32 0
@@ -177,6 +178,31 @@ int g4attn_decode(const void* q, const void* k_cache, const void* v_cache, void*
 
 /* Workspace bytes g4attn_decode needs for these sizes (0 on invalid sizes). */
 size_t g4attn_decode_workspace_bytes(int B, int Hq, int Hkv, int d, int capacity, int window);
+
+/*
+ * g4attn_decode without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  It allocates nothing.  The split partials
+ * go to a fixed scratch array of 64 MiB that the library holds in device
+ * memory on every GPU it runs on, until the process ends; its address on a
+ * device is looked up on the first call with that device current.
+ *   Arguments, layouts, results and errors are those of g4attn_decode, and it
+ *   runs the same kernels.  A problem whose partials (the size
+ *   g4attn_decode_workspace_bytes reports) exceed 64 MiB returns G4A_ESCRATCH
+ *   before anything is launched: for example batch 64 of a ring cache of any
+ *   size fits, as do 16 sequences over a 65536-row linear cache of head dim
+ *   512 with 16 query heads (33.7 MB); 64 such sequences (135 MB) do not.
+ *   f32 inputs need no partials and are never rejected for size.
+ *   Every call on one GPU shares that GPU's scratch: calls that overlap on
+ *   one GPU (on different streams or from different host threads without
+ *   ordering) race on it and give wrong results.  Calls ordered on one
+ *   stream are safe; the scratch needs no clearing between calls.
+ * Returns G4A_OK or a negative status.
+ */
+int g4attn_decode_noalloc(const void* q, const void* k_cache, const void* v_cache, void* out,
+                          const int32_t* pos, int B, int Hq, int Hkv, int d, int capacity,
+                          int window, float theta, float p, int in_dtype, int out_dtype,
+                          void* stream);
 
 /*
  * Cache fill: write the raw key (and value) rows of a prefill into the decode

@@ -36,7 +36,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_strerror_and_codes():
     lib = L.lib()
-    for code in (0, -1, -2, -3, -4, -5):
+    for code in (0, -1, -2, -3, -4, -5, -6):
         assert lib.g4attn_strerror(code)
     assert lib.g4attn_strerror(7) == b"unknown status"
     assert lib.g4attn_last_hip_error() == 0
@@ -275,3 +275,26 @@ def test_prefill_rejects_key_rows_past_the_24_bit_row_offset():
     assert local(Hq=2 * big, Hkv=big, ws=None) == -4  # d = 256: 2^23 bytes fit
     assert local(Hq=4 * big, Hkv=2 * big) == -2
     assert vis(Hq=2 * big, Hkv=2 * big) == -2
+
+
+def dec_noalloc(**kw):
+    args = dict(q=A, k=2 * A, v=None, out=4 * A, pos=5 * A, B=16, Hq=16, Hkv=2, d=512,
+                capacity=65536, window=0, theta=1e6, p=0.25, i=1, o=0, stream=None)
+    args.update(kw)
+    return L.lib().g4attn_decode_noalloc(*args.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    # partials past the fixed 64 MiB scratch: 64 x 16 heads x 64 chunks x 514 x 4 B
+    (dict(B=64), -6), (dict(B=8, capacity=262144), -6),
+    (dict(q=None), -1), (dict(pos=None), -1), (dict(out=None), -1), (dict(B=-1), -1),
+    (dict(capacity=0), -1), (dict(window=512, capacity=1024), -1), (dict(Hq=5), -1),
+    (dict(d=384), -2), (dict(Hq=48, Hkv=3, B=2), -2), (dict(i=0, o=1), -2),
+])
+def test_decode_noalloc_validation(kw, code):
+    """Rejected before any HIP call, the size check first."""
+    assert dec_noalloc(**kw) == code
+
+
+def test_decode_noalloc_empty_batch_is_noop():
+    assert dec_noalloc(B=0, q=None, k=None, out=None, pos=None) == 0
