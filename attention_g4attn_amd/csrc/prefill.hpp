@@ -211,16 +211,16 @@ __global__ void __launch_bounds__(256) rope_keys_kernel(const uint16_t* __restri
   }
 }
 
-// Exact attention row (token t, query head h) for a wave, with the row max m
-// (base-2 scaled) known in advance, so no rescaling is needed.  Lane e owns
-// dims e*(D/64) .. +D/64-1; every key's score is a wave-wide reduction.
-// Keys are read raw and rotated here.
+// Exact attention row (token t, query head h) for a wave: every key's score
+// is a wave-wide reduction (wave-uniform), so the running max and the
+// rescaling of the sums when it grows are uniform too.  Lane e owns dims
+// e*(D/64) .. +D/64-1.  Keys are read raw and rotated here.
 // VIS: keys 0 .. nv-1 (no causal mask), positions per half from pos [B*S, 2].
 template <int D, bool OBF, bool VIS = false>
 __device__ __noinline__ void exact_row(const uint16_t* qp, const uint16_t* kp, const uint16_t* vp,
                                        void* outp, const int32_t* posp, int S, int Hq, int Hkv,
                                        int W, int n_rot, float scale_log2e, int b, int hkv, int t,
-                                       int h, float m, const double* gtab, int nv = 0) {
+                                       int h, const double* gtab, int nv = 0) {
   constexpr int E = D / 64;  // dims per lane, even
   const int lane = threadIdx.x & 63;
   const uint16_t* qr = qp + (((size_t)b * S + t) * Hq + h) * D;
@@ -244,7 +244,7 @@ __device__ __noinline__ void exact_row(const uint16_t* qp, const uint16_t* kp, c
     qv[e] = x0;
     qv[e + 1] = x1;
   }
-  float o[E], l = 0.f;
+  float o[E], l = 0.f, m = -INFINITY;
 #pragma unroll
   for (int e = 0; e < E; ++e) o[e] = 0.f;
   const int lo = VIS ? 0 : (W > 0 ? max(0, t - W + 1) : 0);
@@ -267,7 +267,15 @@ __device__ __noinline__ void exact_row(const uint16_t* qp, const uint16_t* kp, c
       }
       part += qv[e] * x0 + qv[e + 1] * x1;
     }
-    const float p = __builtin_amdgcn_exp2f(wave_sum(part) * scale_log2e - m);
+    const float sc = wave_sum(part) * scale_log2e;
+    if (sc > m) {  // wave-uniform
+      const float c = __builtin_amdgcn_exp2f(m - sc);
+      l *= c;
+#pragma unroll
+      for (int e = 0; e < E; ++e) o[e] *= c;
+      m = sc;
+    }
+    const float p = __builtin_amdgcn_exp2f(sc - m);
     l += p;
 #pragma unroll
     for (int e = 0; e < E; ++e) o[e] += p * bf_lo(vr[lane * E + e]);
@@ -388,8 +396,25 @@ __global__ void __launch_bounds__(NW * 64, (wg_per_cu<D, MB, NST>())) prefill_ke
   // per tile), then one 16-byte-per-lane direct load per call, so that the
   // loads can be spread over the tile's score products instead of queueing
   // behind each other at the address unit all at once.
+  // Lane part of the direct-load offsets of rows of RB bytes (see load_part):
+  // a = chunk ^ (row-in-load << 2), lrb = row-in-load * row stride.
+  struct LaneLd {
+    uint32_t a, lrb;
+  };
+  auto lane_ld = [&](auto rbc, uint32_t rbytes) -> LaneLd {
+    constexpr int CPR = decltype(rbc)::value / 16;  // chunks per row
+    uint32_t ln = (uint32_t)lane;
+    if constexpr (RECOMP) asm volatile("" : "+v"(ln));
+    const uint32_t lr = ln / CPR;
+    const uint32_t rb = __builtin_amdgcn_readfirstlane(rbytes);
+    LaneLd r{(ln % CPR) ^ (lr << 2), (uint32_t)__umul24(lr, rb)};
+    // keeps the wave-uniform part of the row offset a separate scalar term
+    asm volatile("" : "+v"(r.lrb));
+    return r;
+  };
   struct TileSrc {
     __amdgpu_buffer_rsrc_t s, k, v;
+    LaneLd ls, lk;  // slab rows, raw rows
   };
   auto tile_src = [&](int kt) {
     // padding tiles past the sequence reload its last tile: finite data whose
@@ -401,25 +426,29 @@ __global__ void __launch_bounds__(NW * 64, (wg_per_cu<D, MB, NST>())) prefill_ke
     t.s = make_rsrc(sbase_g + toff * SW, rows * srow_bytes - (srow_bytes - 2 * SW));
     t.k = make_rsrc(kbase + toff * D, rows * row_bytes - (row_bytes - 2 * D));
     t.v = make_rsrc(vbase + toff * D, rows * row_bytes - (row_bytes - 2 * D));
+    t.ls = lane_ld(IC<2 * SW>{}, srow_bytes);
+    if constexpr (SW == D) t.lk = t.ls;  // same row size and stride
+    else t.lk = lane_ld(IC<2 * D>{}, row_bytes);
     return t;
   };
   // direct load n of this wave for one tensor: rows of RB bytes in HBM
-  // (stride rbytes), placed at dst with 16-byte chunks swizzled by row
-  auto load_part = [&](auto rbc, const __amdgpu_buffer_rsrc_t& rs, uint32_t rbytes, int n,
-                       unsigned char* dst) {
+  // (stride rbytes), placed at dst with 16-byte chunks swizzled by row.
+  // Lane ln fetches chunk c = ln % CPR of row r = r0 + lr, lr = ln / CPR, with
+  // r0 = (w * LPW + n) * RPI a multiple of RPI <= 4.  The low two bits of r
+  // are then (r0 & 3) | lr and bits 2-3 are those of r0, so swz(r) =
+  // swz(r0) ^ (lr << 2): the lane part A = c ^ (lr << 2) and lr * rb are the
+  // same for every load and tile, and a load adds only the wave-uniform
+  // swz(r0) and r0 * rb (three vector instructions per load).
+  auto load_part = [&](auto rbc, const __amdgpu_buffer_rsrc_t& rs, uint32_t rbytes,
+                       const LaneLd& ll, int n, unsigned char* dst) {
     constexpr int RB = decltype(rbc)::value;  // bytes per row in LDS
-    constexpr int CPR = RB / 16;              // chunks per row
     constexpr int RPI = 1024 / RB;            // rows per direct load
     constexpr int LPW = BN / RPI / NW;        // direct loads per wave
-    int ln = lane;
-    int wl = w;
-    uint32_t rb = __builtin_amdgcn_readfirstlane(rbytes);
-    if constexpr (RECOMP) asm volatile("" : "+v"(ln), "+s"(wl), "+s"(rb));
-    const int r0 = (wl * LPW + n) * RPI;  // first row of this load, wave-uniform
-    const int r = r0 + ln / CPR;
-    // r < BN and rb <= Hkv * D * 2 < 2^24: a 24-bit multiply (full rate; the
-    // 32-bit product was emitted as a 64-bit multiply-add, once per load)
-    const uint32_t voff = __umul24((uint32_t)r, rb) + ((uint32_t)((ln % CPR) ^ swz(r)) << 4);
+    static_assert(RPI >= 1 && RPI <= 4, "the lane part of the row stays in bits 0-1");
+    const uint32_t rb = __builtin_amdgcn_readfirstlane(rbytes);
+    const int r0 = (w * LPW + n) * RPI;  // first row of this load, wave-uniform
+    // rows < BN and rb <= Hkv * D * 2 < 2^24: r0 * rb fits 32 bits
+    const uint32_t voff = ((ll.a ^ (uint32_t)swz(r0)) << 4) + ll.lrb + (uint32_t)r0 * rb;
     lds_dma16(rs, voff, 0, dst + r0 * RB);
   };
   // loads per wave per tile: slab, raw keys (when the slab does not hold
@@ -431,9 +460,9 @@ __global__ void __launch_bounds__(NW * 64, (wg_per_cu<D, MB, NST>())) prefill_ke
   // load j (0 <= j < L::NLD) of a tile; j is a constant after unrolling
   auto load_one = [&](const TileSrc& t, auto stage, int j) {
     unsigned char* sp = stp(stage);
-    if (j < NL_S) load_part(IC<2 * SW>{}, t.s, srow_bytes, j, sp);
-    else if (j < NL_S + NL_K) load_part(IC<2 * D>{}, t.k, row_bytes, j - NL_S, sp + L::KOFF);
-    else load_part(IC<2 * D>{}, t.v, row_bytes, j - NL_S - NL_K, sp + L::VOFF);
+    if (j < NL_S) load_part(IC<2 * SW>{}, t.s, srow_bytes, t.ls, j, sp);
+    else if (j < NL_S + NL_K) load_part(IC<2 * D>{}, t.k, row_bytes, t.lk, j - NL_S, sp + L::KOFF);
+    else load_part(IC<2 * D>{}, t.v, row_bytes, t.lk, j - NL_S - NL_K, sp + L::VOFF);
   };
   auto issue_loads = [&](int kt, auto stage) {
     const TileSrc t = tile_src(kt);
@@ -448,17 +477,15 @@ __global__ void __launch_bounds__(NW * 64, (wg_per_cu<D, MB, NST>())) prefill_ke
     for (int i = 0; i < NDB; ++i) oacc[mb][i] = f32x16{};
   // Softmax state per row (base 2, scores scaled by log2(e)/sqrt(d)).  The
   // reference max m_ref is fixed at the first tile where the row sees a key,
-  // when O is still zero, so O never needs rescaling.  m_seen tracks the true
-  // running max.  If a later tile ever exceeds m_ref by more than 2^64 (P or O
-  // could overflow), the row is flagged in ovf and recomputed exactly after
-  // the epilogue, with m_seen as the reference.
+  // when O is still zero, so O never needs rescaling.  If a later score ever
+  // exceeds m_ref by more than 64 (P = 2^(s - m_ref) could overflow P or O),
+  // the row is flagged in ovf and recomputed exactly after the epilogue.
   constexpr float UNSET = -1e30f;
-  float m_ref[MB], m_seen[MB], l_run[MB];
+  float m_ref[MB], l_run[MB];
   int ovf = 0;  // bit mb: row of block mb overflowed its reference
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
     m_ref[mb] = UNSET;
-    m_seen[mb] = UNSET;
     l_run[mb] = 0.f;
   }
   const float cs = a.scale_log2e;
@@ -466,21 +493,24 @@ __global__ void __launch_bounds__(NW * 64, (wg_per_cu<D, MB, NST>())) prefill_ke
   // ---- scores S^T = K~ Q~^T of one tile (fragments stream in groups of FG, one group ahead) ----
   auto scores = [&](auto stage, f32x16 (&sacc)[MB], auto&& side) {
     unsigned char* sp = stp(stage);
-    int ln = lane;
+    uint32_t ln = (uint32_t)lane;
     if constexpr (RECOMP) asm volatile("" : "+v"(ln));
-    const int l32 = ln & 31, hl = ln >> 5;
-    // score operand (key l32, chunk c = 2s + hl): chunk position
-    // c ^ swz(l32) = 16*(s/8) + ((2*(s%8) + hl) ^ swz(l32))
-    const int sw_n = swz(l32);
-    int soff[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) soff[i] = ((2 * i + hl) ^ sw_n) << 4;
-    const int kbase_off = L::KOFF + l32 * (2 * D);
-    const int sbase_off = l32 * (2 * SW);
+    const uint32_t l32 = ln & 31, hl = ln >> 5;
+    // score operand (key l32, chunk c = 2s + hl) sits at chunk position
+    // 16*(s/8) + ((2*(s%8) + hl) ^ swz(l32)) of its row.  With i = s % 8 and
+    // swz = 2*sh + s0, (2i + hl) ^ swz = 2*(i ^ sh) + (hl ^ s0), so the byte
+    // offset is P ^ (i << 5) + 256*(s/8) with P = row + 16*(hl ^ s0) + 32*sh:
+    // rows start at multiples of 256 bytes, so the XOR only touches bits 5-7
+    // and commutes with the row, stage and 256-byte block offsets.
+    const uint32_t sw = (uint32_t)swz((int)l32);
+    const uint32_t lo = (((hl ^ sw) & 1) << 4) | ((sw >> 1) << 5);
+    const uint32_t ps = l32 * (2 * SW) + lo;  // slab rows
+    const uint32_t pk = l32 * (2 * D) + lo;   // raw key rows
     // k-step s lives in the slab for s < NSS, in the raw key tile otherwise
     auto frag = [&](int s) -> u32x4 {
-      if (s < NSS) return lds_at<u32x4>(sp, sbase_off + 256 * (s >> 3) + soff[s & 7]);
-      return lds_at<u32x4>(sp, kbase_off + 256 * (s >> 3) + soff[s & 7]);
+      const uint32_t x = (uint32_t)(s & 7) << 5;
+      if (s < NSS) return lds_at<u32x4>(sp, (int)((ps ^ x) + 256 * (s >> 3)));
+      return lds_at<u32x4>(sp, L::KOFF + (int)((pk ^ x) + 256 * (s >> 3)));
     };
     constexpr int NG = NDS / FG;
     u32x4 kf[2][FG];
@@ -524,13 +554,16 @@ __global__ void __launch_bounds__(NW * 64, (wg_per_cu<D, MB, NST>())) prefill_ke
     }
     const bool need_mask = (kv0 + BN - 1 > tw0) || (W > 0 && kv0 <= tw1 - W);
     if (need_mask) {  // wave-uniform
+      // key j is visible iff 0 <= tq - j < W (W = 0: 0 <= tq - j), i.e. the
+      // unsigned difference is below W (below 2^31 without a window)
+      const uint32_t wl = W > 0 ? (uint32_t)W : 0x80000000u;
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
-        const int lo = W > 0 ? tq[mb] - W + 1 : 0;
+        const int d0 = tq[mb] - kv0 - 4 * hl;  // tq - j for register 0
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int j = kv0 + 8 * (r >> 2) + 4 * hl + (r & 3);
-          sacc[mb][r] = (j <= tq[mb] && j >= lo) ? sacc[mb][r] : -INFINITY;
+          const uint32_t dj = (uint32_t)(d0 - (8 * (r >> 2) + (r & 3)));
+          sacc[mb][r] = dj < wl ? sacc[mb][r] : -INFINITY;
         }
       }
     }
@@ -543,17 +576,19 @@ __global__ void __launch_bounds__(NW * 64, (wg_per_cu<D, MB, NST>())) prefill_ke
     constexpr int K2 = decltype(k2c)::value;
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
+      // The tile max is needed only until every row of the wave has fixed
+      // its reference (wave-uniform test; after the first tiles it is skipped).
       if constexpr (K2 == 0) {
-      // balanced tree over the lane's 16 scores, then the other half-wave
-      const f32x16& v = sacc[mb];
-      const float a0 = fmaxf(fmaxf(v[0], v[1]), v[2]), a1 = fmaxf(fmaxf(v[3], v[4]), v[5]);
-      const float a2 = fmaxf(fmaxf(v[6], v[7]), v[8]), a3 = fmaxf(fmaxf(v[9], v[10]), v[11]);
-      const float a4 = fmaxf(fmaxf(v[12], v[13]), v[14]);
-      const float mx = max_xor32(fmaxf(fmaxf(fmaxf(a0, a1), a2), fmaxf(fmaxf(a3, a4), v[15])));
-      const float m_tile = mx * cs;  // -inf when the row sees no key here
-      m_seen[mb] = fmaxf(m_seen[mb], m_tile);
-      m_ref[mb] = m_ref[mb] == UNSET ? fmaxf(m_tile, UNSET) : m_ref[mb];
-      ovf |= (m_tile > m_ref[mb] + 64.f) << mb;
+        if (__builtin_amdgcn_ballot_w64(m_ref[mb] == UNSET)) {
+          // balanced tree over the lane's 16 scores, then the other half-wave
+          const f32x16& v = sacc[mb];
+          const float a0 = fmaxf(fmaxf(v[0], v[1]), v[2]), a1 = fmaxf(fmaxf(v[3], v[4]), v[5]);
+          const float a2 = fmaxf(fmaxf(v[6], v[7]), v[8]), a3 = fmaxf(fmaxf(v[9], v[10]), v[11]);
+          const float a4 = fmaxf(fmaxf(v[12], v[13]), v[14]);
+          const float mx = max_xor32(fmaxf(fmaxf(fmaxf(a0, a1), a2), fmaxf(fmaxf(a3, a4), v[15])));
+          const float m_tile = mx * cs;  // -inf when the row sees no key here
+          m_ref[mb] = m_ref[mb] == UNSET ? fmaxf(m_tile, UNSET) : m_ref[mb];
+        }
       }
       const float mr = m_ref[mb] == UNSET ? 0.f : m_ref[mb];
       float lsum = 0.f;
@@ -565,6 +600,9 @@ __global__ void __launch_bounds__(NW * 64, (wg_per_cu<D, MB, NST>())) prefill_ke
         lsum += p0 + p1;
         pf[mb][K2][i] = pack_bf16(p0, p1);
       }
+      // a score more than 2^64 above the reference makes this sum exceed
+      // 2^64 (infinity included): the row is recomputed exactly
+      ovf |= (lsum > 0x1p64f) << mb;
       l_run[mb] += lsum;
     }
   };
@@ -576,26 +614,27 @@ __global__ void __launch_bounds__(NW * 64, (wg_per_cu<D, MB, NST>())) prefill_ke
   // second half under the first group's products.
   auto values = [&](auto stage, auto&& make_p) {
     unsigned char* sp = stp(stage);
-    int ln = lane;
+    uint32_t ln = (uint32_t)lane;
     if constexpr (RECOMP) asm volatile("" : "+v"(ln));
     // value operand by transpose reads: lane (g = ln/16, i = ln%16) reads row
     // 4*(g/2) + i/4 (then +8 rows for the upper 4 keys, +16*k2) at dims
-    // 32*db + 16*(g%2) + 4*(i%4), i.e. chunk 4*db + tr_x, byte 8*(i%2)
-    const int tr_i = ln & 15, tr_g = ln >> 4;
-    const int tr_row = 4 * (tr_g >> 1) + (tr_i >> 2);
-    const int tr_x = 2 * (tr_g & 1) + ((tr_i & 3) >> 1);
-    // voff[h][e]: rows tr_row + 8h, 32-dim block db with db % 4 == e
-    int voff[2][4];
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        voff[h][e] = (tr_row + 8 * h) * (2 * D) + (tr_i & 1) * 8 +
-                     (((4 * e + tr_x) ^ swz(tr_row + 8 * h)) << 4);
+    // 32*db + 16*(g%2) + 4*(i%4), i.e. chunk 4*db + tr_x, byte 8*(i%2).
+    // For row r = tr_row + 8h, swz(r) = swz(tr_row) ^ 2h, and 4e + tr_x =
+    // 4e ^ tr_x (disjoint bits), so the chunk position of block db (e = db%4)
+    // is 4e ^ Q_h with Q_h = tr_x ^ swz(tr_row) ^ 2h: the byte offset is
+    // V_h ^ (e << 6), where V_h holds the row, the byte and Q_h << 4 (bits
+    // 4-7; the row and the 8-byte half sit in other bits), and
+    // V_1 = (V_0 ^ 32) + 8 rows.
+    const uint32_t tr_i = ln & 15, tr_g = ln >> 4;
+    const uint32_t tr_row = 4 * (tr_g >> 1) + (tr_i >> 2);
+    const uint32_t tr_x = 2 * (tr_g & 1) + ((tr_i & 3) >> 1);
+    const uint32_t v0 = tr_row * (2 * D) + (tr_i & 1) * 8 + ((tr_x ^ (uint32_t)swz((int)tr_row)) << 4);
+    const uint32_t v1 = (v0 ^ 32u) + 8 * (2 * D);
     auto vfrag = [&](int db, int k2) -> u32x4 {
       const int off = L::VOFF + 256 * (db >> 2) + (16 * k2) * (2 * D);
-      const u32x2 lo = lds_read_tr16(sp + off + voff[0][db & 3]);
-      const u32x2 hi = lds_read_tr16(sp + off + voff[1][db & 3]);
+      const uint32_t x = (uint32_t)(db & 3) << 6;
+      const u32x2 lo = lds_read_tr16(sp + off + (v0 ^ x));
+      const u32x2 hi = lds_read_tr16(sp + off + (v1 ^ x));
       return u32x4{lo[0], lo[1], hi[0], hi[1]};
     };
     constexpr int NG = 2 * NDB / FG;
@@ -805,11 +844,10 @@ __global__ void __launch_bounds__(NW * 64, (wg_per_cu<D, MB, NST>())) prefill_ke
         const int src_lane = __builtin_ctzll(rows);
         rows &= rows - 1;
         const int t = __shfl(tq[mb], src_lane), h = __shfl(hq[mb], src_lane);
-        const float mref = __shfl(m_seen[mb], src_lane);
         exact_row<D, OBF, VIS>(static_cast<const uint16_t*>(a.q),
                                static_cast<const uint16_t*>(a.k),
                                static_cast<const uint16_t*>(a.v), a.out, a.pos, S, a.Hq, a.Hkv,
-                               W, n_rot, cs, b, hkv, t, h, mref, gtab, nv);
+                               W, n_rot, cs, b, hkv, t, h, gtab, nv);
       }
     }
   }

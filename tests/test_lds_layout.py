@@ -25,16 +25,21 @@ def swz(r):
 
 
 def lds_tile(D):
-    """LDS bytes of one tile, as a dict chunk-position -> (key, first dim)."""
-    RPI = 1024 // (2 * D)
+    """LDS bytes of one tile of rows of D bf16 dims, as a dict chunk-position ->
+    (key, first dim).  Replays the kernel's load offsets: lane ln of the load
+    whose first row is r0 takes row r0 + lr, lr = ln // CPR, and global chunk
+    A ^ swz(r0) with A = (ln % CPR) ^ (lr << 2), which must equal the chunk
+    (ln % CPR) ^ swz(row) the layout stores at LDS byte 16*ln."""
+    RB = 2 * D
+    CPR, RPI = RB // 16, 1024 // RB
     lds = {}
     for r0 in range(0, BN, RPI):
         for ln in range(64):
-            if RPI == 1:
-                row, chunk = r0, ln ^ swz(r0)
-            else:
-                row, chunk = r0 + (ln >> 5), (ln & 31) ^ swz(r0 + (ln >> 5))
-            pos = r0 * (2 * D) + 16 * ln  # destination byte of this lane
+            lr = ln // CPR
+            a = (ln % CPR) ^ (lr << 2)
+            row, chunk = r0 + lr, a ^ swz(r0)
+            assert chunk == (ln % CPR) ^ swz(row)
+            pos = r0 * RB + 16 * ln  # destination byte of this lane
             assert pos not in lds
             lds[pos] = (row, 8 * chunk)
     assert len(lds) == BN * D // 8
@@ -48,25 +53,42 @@ def element(lds, byte):
 
 
 def score_offsets(D, lane, s):
+    """The kernel's form: P ^ ((s % 8) << 5) + 256*(s // 8), with
+    P = row + 16*((hl ^ swz) & 1) + 32*(swz >> 1)."""
     l32, hl = lane & 31, lane >> 5
-    soff = ((2 * (s % 8) + hl) ^ swz(l32)) << 4
-    return l32 * (2 * D) + 256 * (s // 8) + soff
+    sw = swz(l32)
+    p = l32 * (2 * D) + (((hl ^ sw) & 1) << 4) + ((sw >> 1) << 5)
+    off = (p ^ ((s % 8) << 5)) + 256 * (s // 8)
+    # the layout's definition: chunk 2s + hl of row l32 at 16*(s//8) + ((2(s%8) + hl) ^ swz)
+    assert off == l32 * (2 * D) + 256 * (s // 8) + (((2 * (s % 8) + hl) ^ sw) << 4)
+    return off
 
 
 def value_offsets(D, lane, db, k2, h):
+    """The kernel's form: V_h ^ ((db % 4) << 6) + 256*(db // 4) + 16*k2 rows,
+    V_0 = tr_row*2D + 8*(tr_i & 1) + ((tr_x ^ swz(tr_row)) << 4),
+    V_1 = (V_0 ^ 32) + 8 rows."""
     tr_i, tr_g = lane & 15, lane >> 4
     tr_row = 4 * (tr_g >> 1) + (tr_i >> 2)
     tr_x = 2 * (tr_g & 1) + ((tr_i & 3) >> 1)
-    voff = (tr_row + 8 * h) * (2 * D) + (tr_i & 1) * 8 + (((4 * (db % 4) + tr_x) ^ swz(tr_row + 8 * h)) << 4)
-    return voff + 256 * (db // 4) + 16 * k2 * (2 * D)
+    v0 = tr_row * (2 * D) + (tr_i & 1) * 8 + ((tr_x ^ swz(tr_row)) << 4)
+    v = v0 if h == 0 else (v0 ^ 32) + 8 * (2 * D)
+    off = (v ^ ((db % 4) << 6)) + 256 * (db // 4) + 16 * k2 * (2 * D)
+    # the layout's definition: chunk 4*db + tr_x of row tr_row + 8h at its swizzled place
+    want = ((tr_row + 8 * h) * (2 * D) + (tr_i & 1) * 8
+            + (((4 * (db % 4) + tr_x) ^ swz(tr_row + 8 * h)) << 4))
+    assert off == want + 256 * (db // 4) + 16 * k2 * (2 * D)
+    return off
 
 
 def banks16(addrs):
     return {(a >> 2) & 63 for a in addrs for a in (a, a + 4, a + 8, a + 12)}
 
 
-@pytest.mark.parametrize("D", [256, 512])
+@pytest.mark.parametrize("D", [128, 256, 512])
 def test_score_operand_reads(D):
+    """D = 128 is the rotated-key slab of the d = 512 K=V layer (256-byte rows,
+    four rows per direct load)."""
     lds = lds_tile(D)
     for s in range(D // 16):
         offs = [score_offsets(D, lane, s) for lane in range(64)]
