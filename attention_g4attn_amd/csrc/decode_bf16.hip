@@ -481,6 +481,8 @@ int decode_num_chunks(int D, int capacity, int window, bool f32) {
 hipError_t launch_decode_bf16(const DecodeArgs& a, bool kv_shared, bool out_bf16,
                               hipStream_t st) {
   if ((long long)a.B * a.Hkv == 0) return hipSuccess;
+  // K=V with several column blocks: one pass over each chunk for all of them
+  if (kv_shared && a.ncb >= 2) return launch_decode_mc(a, out_bf16, st);
   const hipError_t e = out_bf16 ? launch_split_d<true>(a, kv_shared, st)
                                 : launch_split_d<false>(a, kv_shared, st);
   if (e != hipSuccess) return e;

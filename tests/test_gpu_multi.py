@@ -108,6 +108,40 @@ def test_decode_multi_parity(name, mk, L, dtype):
     assert_parity(out, ref, dtype, f"{name} L={L}")
 
 
+# K=V with more than 16 (token, head) columns: every column block is computed
+# by one workgroup whose waves split the head dims (ring caches are one chunk
+# and written in place; linear caches go through the merge kernel)
+MANY_COLUMNS = [
+    # ring of 70 slots at window 64, G = 8, 5 tokens: 40 columns in 3 blocks
+    ("kv-ring-g8-L5", lambda: inputs.DecodeLayer("global", 3, 16, 2, 512, 70, 64, 1e6, 0.25), 5),
+    # G = 4, d = 256, every pair turning, 6 tokens: 24 columns in 2 blocks
+    ("kv-g4-d256-L6", lambda: inputs.DecodeLayer("global", 3, 8, 2, 256, 2100, 0, 1e4, 1.0), 6),
+    # G = 8, 7 tokens: 56 columns in 4 blocks, 2 chunks
+    ("kv-g8-L7", lambda: inputs.DecodeLayer("global", 3, 16, 2, 512, 1500, 0, 1e6, 0.25), 7),
+]
+
+
+@pytest.mark.parametrize("name,mk,L", MANY_COLUMNS, ids=[c[0] for c in MANY_COLUMNS])
+@pytest.mark.parametrize("out_dtype", [None, torch.bfloat16], ids=["f32out", "bf16out"])
+def test_decode_multi_many_columns_one_pass(name, mk, L, out_dtype):
+    layer = mk()
+    if layer.window > 0:  # a short sequence, a full ring, a wrapped ring
+        lengths = torch.tensor([L, layer.capacity - 1, 5 * layer.capacity + 3])
+    else:  # a sequence shorter than the tokens (NaN rows), one chunk edge, the capacity
+        lengths = torch.tensor([L - 2, 1025, layer.capacity])
+    out, ref = _run_multi(layer, L, torch.bfloat16, lengths, 1300 + L, out_dtype=out_dtype)
+    got = out.float()
+    if layer.window == 0:  # tokens 0, 1 of sequence 0 sit at negative positions
+        assert torch.isnan(got[0, :2]).all() and torch.isfinite(got[0, 2:]).all()
+        got, ref = got[:, 2:], ref[:, 2:]
+    assert torch.isfinite(got).all()
+    if out_dtype is None:
+        assert_parity(got, ref, torch.bfloat16, f"{name}")
+    else:
+        g = got.cpu().double().numpy()
+        assert np.all(np.abs(g - ref) <= 1e-2 + 2.0 ** -8 * np.abs(ref))
+
+
 def test_decode_multi_bf16_output():
     layer = inputs.DecodeLayer("global", 2, 16, 2, 512, 2100, 0, 1e6, 0.25)
     out, ref = _run_multi(layer, 3, torch.bfloat16, torch.tensor([2100, 40]), 900,
