@@ -10,30 +10,29 @@
 // columns.  That kernel, run once per 16-column block, streams every chunk of
 // the cache once per block; this one reads every tile once for all blocks.
 //
-// Work decomposition: one 4-wave workgroup per (sequence, KV head, chunk of
-// 1024 cache rows), numbered densely over the chunks with a visible row as in
-// the split kernel.  The workgroup walks its chunk in 16-row tiles that stream
-// from HBM through a 3-deep LDS ring (16-byte direct-to-LDS loads, a
-// quarter issued by each wave).  The head dims are split over the waves: wave w takes
-// score k-steps s = w, w+4, ... (32 dims each; with p-RoPE at p = 0.25 the
-// rotated k-steps 0..3 go one per wave) and output dim blocks db = w, w+4, ...
-// (16 dims each).  Per tile:
-//   1. every wave forms its partial S^T over its k-steps for every column
-//      block (16x16x32 products; keys rotated at their positions) and writes
-//      it to LDS;
-//   2. wave j sums the four partials of block j, masks, and updates the
-//      softmax of block j's columns; it writes P^T (bf16, in the B-operand
-//      layout of the value product) and, when a column's max grew by more
-//      than 2^8, the factor that rescales that column's outputs;
-//   3. every wave applies the factors to its output blocks and forms
-//      O^T += V^T P^T for its dim blocks of every column block (16x16x16
-//      products, V^T by LDS transpose reads).
-// Three barriers per tile separate the phases.  A wave holds 16 columns x
-// its D/4 output dims per block (8 f32x4 per block at D = 512), so two waves
-// fit per SIMD.  The chunk's (m, l, O) go to the workspace for the merge
-// kernel, or, when one chunk covers every row, straight to the output.
-#include <type_traits>
-
+// Work decomposition: one workgroup per (sequence, KV head, chunk of 1024
+// cache rows), numbered densely over the chunks with a visible row as in the
+// split kernel, with one wave per 16-column block.  The waves share the
+// chunk's 16-row tiles, which stream from HBM into a ring of NSL LDS slots
+// (16-byte direct-to-LDS loads, each wave issuing its share of a tile); apart
+// from that every wave works alone, as a wave of the split kernel does on its
+// block: S^T = K~ Q~^T over the whole head (keys rotated at their positions),
+// the softmax of its 16 columns, and O^T += V^T P^T over every output dim.
+// One barrier per tile: after it, tile i+1 is in LDS and the slot of tile i
+// is free for tile i+NSL.
+//
+// The head dims could be split over the waves instead (each wave a quarter
+// of the k-steps and output dims of every block, partial scores summed
+// through LDS), which needs three barriers per tile with the softmax of each
+// block on one wave between two of them: with shader-clock stamps a tile took
+// about 4800 cycles that way (scores 1150, softmax 1360, values 930, the rest
+// barriers and load issue), and 64 sequences of 4 draft tokens at G = 8,
+// D = 512 took 1200 us.
+//
+// With 2 blocks (17 to 32 columns) a workgroup is 2 waves with a 2-slot ring,
+// four workgroups per CU; with 3 or 4 blocks, 4 waves with a 4-slot ring, two
+// per CU.  Either way a CU holds 8 waves and 8 tile slots, as the split
+// kernel does for one block.
 #include "common.hpp"
 #include "decode_common.hpp"
 #include "kernels.hpp"
@@ -45,10 +44,6 @@ namespace {
 using namespace dec;
 
 constexpr int TRM = 16;  // cache rows per tile
-constexpr int NWM = 4;   // waves per workgroup
-
-template <int N>
-using ICM = std::integral_constant<int, N>;
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
@@ -63,46 +58,74 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const unsigned char* p) {
   return __builtin_bit_cast(u32x2, v);
 }
 
-// 16-byte chunk swizzle of tile row r, the one-block kernel's: a bijection on
+// Workgroup barrier that leaves the tile loads in flight: this wave's LDS
+// writes have completed, its vector-memory operations are not waited for.
+// (__syncthreads' release fence waits for every outstanding load, the
+// direct-to-LDS tile loads included, so with it no tile stays in flight
+// across a step.)  The memory clobber keeps the compiler from moving LDS
+// accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Buffer resource as four scalar words (base, stride 0, size in bytes, raw
+// 32-bit dwords), for loads issued from inline assembly.
+typedef uint32_t s32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ s32x4 rsrc_words(const void* base, uint32_t bytes) {
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  return s32x4{(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)p),
+               (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(p >> 32)) & 0xffffu,
+               (uint32_t)__builtin_amdgcn_readfirstlane(bytes), 0x00020000u};
+}
+
+// Non-temporal 16-byte direct load into LDS (lane l's bytes at ldst + 16 l),
+// issued from inline assembly.  The compiler's wait insertion cannot tell
+// which LDS object a builtin direct load writes, so after one it waits for
+// every outstanding load before the next LDS read, which drains the ring each
+// step; it does not see this one, and the kernel orders the tile reads itself
+// (wait_vmcnt, then a barrier).  The instruction writes no register.
+__device__ __forceinline__ void lds_dma16_nt_asm(s32x4 rs, uint32_t voff, unsigned char* ldst) {
+  // the low 32 bits of a generic address in the LDS aperture are the LDS
+  // offset (the aperture is 4 GiB aligned)
+  const uint32_t m = __builtin_amdgcn_readfirstlane((uint32_t)reinterpret_cast<uintptr_t>(ldst));
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen nt lds"
+               :: "s"(m), "v"(voff), "s"(rs) : "memory", "m0");
+}
+
+// 16-byte chunk swizzle of tile row r, the split kernel's: a bijection on
 // r % 16; a score read (16 lanes = 16 rows, one chunk) and a transpose read
 // (32 lanes = 8 rows x 2 adjacent chunks) each hit 16 bank groups.
 __device__ __forceinline__ int mswz(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
 
-// NCB = column blocks the instance holds (2 or 4); RK = score k-steps that
-// may hold turning pairs (4 when n_rot <= 64, else all).  The LDS ring is 3
-// deep (two workgroups per CU); a fourth stage measured no faster (1481
-// against 1461 us for 64 sequences of 4 draft tokens at G = 8, D = 512).
-template <int D, int G, int NCB, int RK, bool OBF>
-__global__ void __launch_bounds__(64 * NWM) __attribute__((amdgpu_waves_per_eu(2, 2)))
+// NCB = column blocks (= waves) of the instance, NSL = LDS tile slots; RK =
+// score k-steps that may hold turning pairs (4 when n_rot <= 64, else all).
+//
+// Key rotation.  Every block's scores need the same rotated keys, and the
+// rotation (an fp64 angle reduction and a hardware sine and cosine per pair)
+// costs more than the score products: timed without it, the 4-token decode
+// above ran in 950 instead of 1135 us.  With RK = 4 (p-RoPE at p <= 0.25:
+// dims below 128) the waves therefore rotate the tile once between them,
+// each the rows of its own share, into an LDS copy of those 128 dims, and a
+// second barrier per tile publishes it.  With every dim turning (RK = NS)
+// that copy would be a second tile; each wave rotates what it reads.
+template <int D, int G, int NCB, int NSL, int RK, bool OBF>
+__global__ void __launch_bounds__(64 * NCB) __attribute__((amdgpu_waves_per_eu(2, 2)))
 decode_mc_kernel(DecodeArgs a) {
   constexpr int NS = D / 32;       // score k-steps
   constexpr int NB = D / 16;       // output dim blocks
-  constexpr int KSW = NS / NWM;    // k-steps per wave
-  constexpr int DBW = NB / NWM;    // dim blocks per wave
   constexpr int KB = TRM * D * 2;  // one tile, bytes
   constexpr int NLD = KB / 1024;   // direct loads per tile
-  constexpr int NLW = NLD / NWM;   // per wave
-  constexpr int NST = 3;  // LDS ring depth
-  static_assert(G <= 8 && NCB <= 4 && RK <= NS && NS % NWM == 0 && NLD % NWM == 0, "shape");
-  __shared__ __attribute__((aligned(16))) unsigned char st0[KB];
-  __shared__ __attribute__((aligned(16))) unsigned char st1[KB];
-  __shared__ __attribute__((aligned(16))) unsigned char st2[KB];
-  __shared__ __attribute__((aligned(16))) unsigned char st3[NST > 3 ? KB : 16];
-  __shared__ __attribute__((aligned(16))) f32x4 xs[NWM][NCB][64];  // partial scores
-  __shared__ __attribute__((aligned(16))) u32x2 pb[NCB][64];        // P^T operands
-  __shared__ float alb[NCB][16];                                   // rescale factors
-  __shared__ int rsb[NCB];                                         // block rescaled?
-  __shared__ float mlb[NCB][16][2];                                // final (m, l)
-  __shared__ double gtab[D / 2];
-  auto stp = [&](auto s) -> unsigned char* {
-    if constexpr (decltype(s)::value == 0) return st0;
-    else if constexpr (decltype(s)::value == 1) return st1;
-    else if constexpr (decltype(s)::value == 2) return st2;
-    else return st3;
-  };
+  constexpr int NLW = NLD / NCB;   // per wave
+  static_assert(G <= 8 && NCB <= 4 && RK <= NS && NLD % NCB == 0 && NSL >= 2, "shape");
+  constexpr bool COOP = RK == 4;                    // rotate the tile once, together
+  constexpr int RW = TRM / NCB;                     // rows of a wave's share
+  static_assert(!COOP || (RW * 16) % 64 == 0, "rotation share");
+  __shared__ __attribute__((aligned(16))) unsigned char ring[NSL * KB];  // tile i in slot i % NSL
+  __shared__ __attribute__((aligned(16))) unsigned char rotk[COOP ? TRM * 256 : 16];  // dims < 128, rotated
+  __shared__ double gtab[COOP ? 64 : D / 2];
 
   const int lane = threadIdx.x & 63;
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // = column block
   const int l16 = lane & 15, g4 = lane >> 4;
   const Unit u = unit_of_block(a);  // every column block in one workgroup
   if (u.b < 0) return;
@@ -122,7 +145,7 @@ decode_mc_kernel(DecodeArgs a) {
   if (P < 0 || (W == 0 && P >= C)) {
     if (direct)
       for (int j = 0; j < ncb; ++j)
-        nan_columns<D, NWM, OBF>(a, ncol_of(j), [&](int n) { return col_out(j, n); });
+        nan_columns<D, NCB, OBF>(a, ncol_of(j), [&](int n) { return col_out(j, n); });
     return;
   }
   const int last = W > 0 ? min(P, C - 1) : P;
@@ -131,32 +154,30 @@ decode_mc_kernel(DecodeArgs a) {
   const int r1 = min(r0 + a.chunk, last + 1);
   const int nt = (r1 - r0 + TRM - 1) / TRM;
   const int n_rot = a.n_rot;
+  const bool active = w < ncb;  // wave-uniform: this block has columns
+  const bool col_ok = l16 < ncol_of(w);
+  const int Pq = col_ok ? col_pos(w, l16) : 0;  // this lane's column position
 
-  // this wave's k-steps of the queries of every block, as B operands
-  bool col_ok[NCB];
-  int pq[NCB];
-  u32x4 qf[NCB][KSW];
+  // the block's queries as B operands of the score product (columns past the
+  // block's last are zero)
+  u32x4 qf[NS];
+  {
+    const uint16_t* qrow =
+        static_cast<const uint16_t*>(a.q) + (col_ok ? col_out(w, l16) : col_out(0, 0));
 #pragma unroll
-  for (int j = 0; j < NCB; ++j) {
-    col_ok[j] = j < ncb && l16 < ncol_of(j);
-    pq[j] = col_ok[j] ? col_pos(j, l16) : 0;
-    const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + (col_ok[j] ? col_out(j, l16) : col_out(0, 0));
-#pragma unroll
-    for (int k = 0; k < KSW; ++k) {
-      const int s = NWM * k + w;
-      qf[j][k] = *reinterpret_cast<const u32x4*>(qrow + 8 * (4 * s + g4));
-    }
+    for (int s = 0; s < NS; ++s) qf[s] = *reinterpret_cast<const u32x4*>(qrow + 8 * (4 * s + g4));
   }
   const size_t hoff = ((size_t)b * a.Hkv + hkv) * C * D;
   const uint16_t* kbase = static_cast<const uint16_t*>(a.k) + hoff;
-  // this wave's quarter of tile i's rows into a stage; rows past r1 read as
-  // zeros; every cache row is read once by the launch: non-temporal
+  // this wave's share of tile i's rows into a slot (past the last tile: the
+  // last tile again); rows past r1 read as zeros; every cache row is read
+  // once by the launch: non-temporal
   auto issue = [&](int i, unsigned char* dst) {
-    const int rr0 = r0 + min(i, nt - 1) * TRM;  // past the last tile: repeat it
+    const int rr0 = r0 + min(i, nt - 1) * TRM;
     const uint32_t bytes = (uint32_t)min(TRM, r1 - rr0) * (2 * D);
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(kbase + (size_t)rr0 * D, bytes);
-    constexpr int CPR = D / 8;
-    constexpr int RPI = 64 / CPR;
+    const s32x4 rs = rsrc_words(kbase + (size_t)rr0 * D, bytes);
+    constexpr int CPR = D / 8;     // chunks per row
+    constexpr int RPI = 64 / CPR;  // rows per direct load
     int ln = lane;
     asm volatile("" : "+v"(ln));
 #pragma unroll
@@ -164,224 +185,200 @@ decode_mc_kernel(DecodeArgs a) {
       const int n = NLW * w + m;
       const int row = n * RPI + ln / CPR;
       const uint32_t voff = (uint32_t)row * (2 * D) + ((uint32_t)((ln % CPR) ^ mswz(row)) << 4);
-      lds_dma16(rs, voff, dst + n * 1024, true);
+      lds_dma16_nt_asm(rs, voff, dst + n * 1024);
     }
   };
-  for (int t = threadIdx.x; t < D / 2; t += 64 * NWM) gtab[t] = rope_rev_per_pos(t, D, a.log2_theta);
+  for (int t = threadIdx.x; t < (COOP ? 64 : D / 2); t += 64 * NCB)
+    gtab[t] = rope_rev_per_pos(t, D, a.log2_theta);
   __syncthreads();
-  // tiles 0 .. NST-2 in flight before the queries are rotated
-  issue(0, st0);
-  issue(1, st1);
-  if constexpr (NST > 3) issue(2, st2);
+  // tiles 0 .. NSL-2 in flight before the queries are rotated (all NSL-1
+  // issued, so the wait below counts them whatever nt is)
 #pragma unroll
-  for (int j = 0; j < NCB; ++j)
+  for (int t = 0; t < NSL - 1; ++t) issue(t, ring + t * KB);
 #pragma unroll
-    for (int k = 0; k < KSW; ++k) {
-      const int s = NWM * k + w;
-      qf[j][k] = col_ok[j] ? qf[j][k] : u32x4{0, 0, 0, 0};
-      if (s < RK) qf[j][k] = rotate_chunk_bf16(qf[j][k], 4 * s + g4, pq[j], n_rot, gtab);
-    }
+  for (int s = 0; s < NS; ++s) {
+    qf[s] = col_ok ? qf[s] : u32x4{0, 0, 0, 0};
+    if (s < RK) qf[s] = rotate_chunk_bf16(qf[s], 4 * s + g4, Pq, n_rot, gtab);
+  }
 
-  f32x4 oacc[NCB][DBW];
+  f32x4 oacc[NB];
 #pragma unroll
-  for (int j = 0; j < NCB; ++j)
-#pragma unroll
-    for (int k = 0; k < DBW; ++k) oacc[j][k] = f32x4{};
-  // softmax state of block w's columns (wave w < ncb owns block w)
-  float m_run = -INFINITY, l_run = 0.f;
+  for (int i = 0; i < NB; ++i) oacc[i] = f32x4{};
+  float m_run = -INFINITY, l_run = 0.f;  // per column (l16), base 2
   const float cs = a.scale_log2e;
-  const int jo = w;  // the block this wave owns
 
-  auto step = [&](int i, auto s) {
-    constexpr int S0 = decltype(s)::value;
-    unsigned char* kt = stp(s);
-    // ---- 1. partial scores of this wave's k-steps, every block ----
+  // S^T of tile i (register j = key 4*gq + j of column l16), the softmax
+  // update, and O^T += V^T P^T, from the tile in LDS at kt
+  auto compute = [&](int i, const unsigned char* kt) {
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int row = ln & 15, gq = ln >> 4;
+    f32x4 sacc;
     {
-      int ln = lane;
-      asm volatile("" : "+v"(ln));
-      const int row = ln & 15, gq = ln >> 4;
-      const int rr = min(r0 + i * TRM + row, r1 - 1);
-      const int tpos = W > 0 ? P - (P - rr) % C : rr;
+      const int r = min(r0 + i * TRM + row, r1 - 1);  // rows past the tile end are masked
+      const int tpos = W > 0 ? P - (P - r) % C : r;
+      (void)tpos;
       const int dsw = mswz(row);
-      f32x4 ps[NCB] = {};
+      f32x4 s0 = {}, s1 = {};  // even / odd k-steps: two independent chains
 #pragma unroll
-      for (int k = 0; k < KSW; ++k) {
-        const int sk = NWM * k + w;  // k-step: chunk 4*sk + gq of the row
-        const int c = 4 * sk + gq;
-        u32x4 kf = lds_at<u32x4>(kt, row * (2 * D) + 256 * (c >> 4) + (((c & 15) ^ dsw) << 4));
-        if (sk < RK) kf = rotate_chunk_bf16(kf, c, tpos, n_rot, gtab);
-#pragma unroll
-        for (int j = 0; j < NCB; ++j)
-          if (j < ncb) ps[j] = mfma16x16x32(kf, qf[j][k], ps[j]);
+      for (int s = 0; s < NS; ++s) {
+        const int c = 4 * s + gq;  // chunk of the row
+        u32x4 kf;
+        if (COOP && s < 4) {  // chunk c < 16: from the rotated copy
+          kf = *reinterpret_cast<const u32x4*>(rotk + row * 256 + ((c ^ dsw) << 4));
+        } else {
+          kf = *reinterpret_cast<const u32x4*>(kt + row * (2 * D) + 256 * (c >> 4) +
+                                              (((c & 15) ^ dsw) << 4));
+          if (!COOP && s < RK) kf = rotate_chunk_bf16(kf, c, tpos, n_rot, gtab);
+        }
+        if (s & 1) s1 = mfma16x16x32(kf, qf[s], s1);
+        else s0 = mfma16x16x32(kf, qf[s], s0);
       }
-#pragma unroll
-      for (int j = 0; j < NCB; ++j)
-        if (j < ncb) xs[w][j][lane] = ps[j];
+      sacc = s0 + s1;
     }
-    __syncthreads();
-    // tile i+NST-1 goes into the stage tile i-1 used (every wave is past its reads)
-    if (i + NST - 1 < nt) issue(i + NST - 1, stp(ICM<(S0 + NST - 1) % NST>{}));
-    // ---- 2. softmax of the owned block ----
-    if (jo < ncb) {
-      f32x4 sacc = xs[0][jo][lane];
-#pragma unroll
-      for (int v = 1; v < NWM; ++v) sacc += xs[v][jo][lane];
+    u32x2 pf;
+    {
       const int nrows = min(TRM, r1 - (r0 + i * TRM));
 #pragma unroll
-      for (int r = 0; r < 4; ++r) sacc[r] = 4 * g4 + r < nrows ? sacc[r] : -INFINITY;
-      if (QL > 1) {  // each column sees keys up to its own position
-        const int Pq = col_pos(jo, l16);
-        const int rk = r0 + i * TRM + 4 * g4;
-        const int m0 = W > 0 ? (P - rk) % C : 0;
+      for (int j = 0; j < 4; ++j) sacc[j] = 4 * gq + j < nrows ? sacc[j] : -INFINITY;
+      // each column sees keys up to its own position (in a ring, only the
+      // window before it)
+      const int rk = r0 + i * TRM + 4 * gq;     // this lane's first key row
+      const int m0 = W > 0 ? (P - rk) % C : 0;  // (P - row) mod C of that row
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int mj = m0 - r;
-          const int tp = W > 0 ? P - (mj >= 0 ? mj : mj + C) : rk + r;
-          const bool vis = tp <= Pq && (W == 0 || tp > Pq - W);
-          sacc[r] = vis ? sacc[r] : -INFINITY;
-        }
+      for (int j = 0; j < 4; ++j) {
+        const int mj = m0 - j;
+        const int tp = W > 0 ? P - (mj >= 0 ? mj : mj + C) : rk + j;  // key position
+        const bool vis = tp <= Pq && (W == 0 || tp > Pq - W);
+        sacc[j] = vis ? sacc[j] : -INFINITY;
       }
       float mx = fmaxf(fmaxf(sacc[0], sacc[1]), fmaxf(sacc[2], sacc[3]));
       mx = fmaxf(mx, __shfl_xor(mx, 16));
       mx = fmaxf(mx, __shfl_xor(mx, 32));
       const float mt = mx * cs;
-      const bool grow = __any(mt > m_run + 8.f);  // wave-uniform; rare after the first tile
-      float al = 1.f;
-      if (grow) {
+      if (__any(mt > m_run + 8.f)) {  // wave-uniform; rare after the first tile
         const float mn = fmaxf(m_run, mt);
-        al = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - mn);
+        // a column that has seen no key yet holds zeros (scaled by 0, not NaN)
+        const float al = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - mn);
+#pragma unroll
+        for (int db = 0; db < NB; ++db) oacc[db] *= al;
         l_run *= al;
         m_run = mn;
       }
-      const float mr = m_run == -INFINITY ? 0.f : m_run;
+      const float mr = m_run == -INFINITY ? 0.f : m_run;  // no key seen: every p is 0
       float p[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        p[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[r], cs, -mr));
-        l_run += p[r];
+      for (int j = 0; j < 4; ++j) {
+        p[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[j], cs, -mr));
+        l_run += p[j];
       }
-      pb[jo][lane] = u32x2{pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3])};
-      if (g4 == 0) alb[jo][l16] = al;
-      if (lane == 0) rsb[jo] = grow;
+      pf = u32x2{pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3])};
     }
-    __syncthreads();
-    // ---- 3. rescale and value products of this wave's dim blocks ----
     {
-      int ln = lane;
-      asm volatile("" : "+v"(ln));
-      const int row = ln & 15, gq = ln >> 4;
+      // V^T by transpose reads: source lane (gq, row) addresses tile row
+      // 4*gq + row/4, dims 16*db + 4*(row%4) .. +3 (chunk 2*db + (row%4)/2)
       const int trow = 4 * gq + (row >> 2);
       const int tch = (row & 3) >> 1;
       const int tdsw = mswz(trow);
-      u32x2 pf[NCB];
+      const unsigned char* vb = kt + trow * (2 * D) + (row & 1) * 8;
 #pragma unroll
-      for (int j = 0; j < NCB; ++j) {
-        if (j < ncb) {
-          if (__builtin_amdgcn_readfirstlane(rsb[j])) {  // wave-uniform
-            const float f = alb[j][l16];
-#pragma unroll
-            for (int k = 0; k < DBW; ++k) oacc[j][k] *= f;
-          }
-          pf[j] = pb[j][lane];
-        }
-      }
-#pragma unroll
-      for (int k = 0; k < DBW; ++k) {
-        const int db = NWM * k + w;  // chunk c = 2*db + tch of row trow
+      for (int db = 0; db < NB; ++db) {
         const int c = 2 * db + tch;
-        const u32x2 vf = lds_read_tr16(kt + trow * (2 * D) + (row & 1) * 8 + 256 * (c >> 4) +
-                                       (((c & 15) ^ tdsw) << 4));
-#pragma unroll
-        for (int j = 0; j < NCB; ++j)
-          if (j < ncb) oacc[j][k] = mfma16x16x16(vf, pf[j], oacc[j][k]);
+        const u32x2 vf = lds_read_tr16(vb + 256 * (c >> 4) + (((c & 15) ^ tdsw) << 4));
+        oacc[db] = mfma16x16x16(vf, pf, oacc[db]);
       }
     }
-    // tile i+1 must have landed in every wave's part before the next step;
-    // this wave's loads of tiles i+2 .. i+NST-1 may still run
-    if (i + NST - 1 < nt) wait_vmcnt<(NST - 2) * NLW>();
-    else wait_vmcnt<0>();
-    __syncthreads();
   };
-  wait_vmcnt<(NST - 2) * NLW>();  // this wave's part of tile 0
-  __syncthreads();
-  for (int i = 0; i < nt; i += NST) {
-    step(i, ICM<0>{});
-    if (i + 1 >= nt) break;
-    step(i + 1, ICM<1>{});
-    if (i + 2 >= nt) break;
-    step(i + 2, ICM<2 % NST>{});
-    if constexpr (NST > 3) {
-      if (i + 3 >= nt) break;
-      step(i + 3, ICM<3 % NST>{});
-    }
-  }
 
-  // ---- the chunk's (m, l, O): owners publish (m, l), every wave its dims ----
-  if (jo < ncb) {
-    l_run += __shfl_xor(l_run, 16);
-    l_run += __shfl_xor(l_run, 32);
-    if (g4 == 0) {
-      mlb[jo][l16][0] = m_run;
-      mlb[jo][l16][1] = l_run;
+  // the first 128 dims of this wave's rows of tile i, rotated at their
+  // positions, into rotk (same row swizzle as the tile); rows past r1 are
+  // zeros and stay zeros
+  auto rotate_share = [&](int i, const unsigned char* kt) {
+#pragma unroll
+    for (int m = 0; m < RW * 16 / 64; ++m) {
+      const int idx = 64 * m + lane;
+      const int row = RW * w + idx / 16, c = idx % 16;
+      const int r = min(r0 + i * TRM + row, r1 - 1);
+      const int tpos = W > 0 ? P - (P - r) % C : r;
+      const int sw = (c ^ mswz(row)) << 4;
+      const u32x4 kf = *reinterpret_cast<const u32x4*>(kt + row * (2 * D) + sw);
+      *reinterpret_cast<u32x4*>(rotk + row * 256 + sw) = rotate_chunk_bf16(kf, c, tpos, n_rot, gtab);
     }
+  };
+
+  wait_vmcnt<(NSL - 2) * NLW>();  // this wave's share of tile 0
+  lds_barrier();
+  for (int i = 0; i < nt; ++i) {
+    // tile i+NSL-1 goes into the slot tile i-1 used (every wave passed the
+    // barrier that ended step i-1)
+    const bool more = i + NSL - 1 < nt;
+    if (more) issue(i + NSL - 1, ring + ((i + NSL - 1) % NSL) * KB);
+    if constexpr (COOP) {  // rotk was last read in step i-1, before its end barrier
+      rotate_share(i, ring + (i % NSL) * KB);
+      lds_barrier();
+    }
+    if (active) compute(i, ring + (i % NSL) * KB);
+    // tile i+1 must have landed in every wave's share before the next step;
+    // this wave's loads of tiles i+2 .. i+NSL-1 may still run
+    if (more) wait_vmcnt<(NSL - 2) * NLW>();
+    else wait_vmcnt<0>();
+    lds_barrier();
   }
-  __syncthreads();
+  if (!active) return;
+
+  // ---- the chunk's (m, l, O) for this block's columns ----
+  l_run += __shfl_xor(l_run, 16);
+  l_run += __shfl_xor(l_run, 32);
+  if (!col_ok) return;
+  if (direct) {
+    // every column sees its own key unless its position is negative
+    const bool ok = Pq >= 0;
+    const float inv = 1.f / l_run;
+    const size_t orow = col_out(w, l16);
 #pragma unroll
-  for (int j = 0; j < NCB; ++j) {
-    if (j >= ncb || l16 >= ncol_of(j)) continue;
-    const float m = mlb[j][l16][0], l = mlb[j][l16][1];
-    if (direct) {
-      // every column sees its own key unless its position is negative
-      const bool ok = col_pos(j, l16) >= 0;
-      const float inv = 1.f / l;
-      const size_t orow = col_out(j, l16);
+    for (int db = 0; db < NB; ++db) {
+      const int e = 16 * db + 4 * g4;
+      const f32x4 o = ok ? oacc[db] * inv
+                         : f32x4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""),
+                                 __builtin_nanf("")};
+      if constexpr (OBF) {
+        const u32x2 pk = {pack_bf16(o[0], o[1]), pack_bf16(o[2], o[3])};
+        *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.out) + orow + e) = pk;
+      } else {
+        *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + orow + e) = o;
+      }
+    }
+  } else {
+    const size_t prow = (col_out(w, l16) / D) * a.nchunk + ch;
+    float* po = a.part_o + prow * D + 4 * g4;
 #pragma unroll
-      for (int k = 0; k < DBW; ++k) {
-        const int e = 16 * (NWM * k + w) + 4 * g4;
-        const f32x4 o = ok ? oacc[j][k] * inv
-                           : f32x4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""),
-                                   __builtin_nanf("")};
-        if constexpr (OBF) {
-          const u32x2 pk = {pack_bf16(o[0], o[1]), pack_bf16(o[2], o[3])};
-          *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.out) + orow + e) = pk;
-        } else {
-          *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + orow + e) = o;
-        }
-      }
-    } else {
-      const size_t prow = (col_out(j, l16) / D) * a.nchunk + ch;
-#pragma unroll
-      for (int k = 0; k < DBW; ++k) {
-        const int e = 16 * (NWM * k + w) + 4 * g4;
-        *reinterpret_cast<f32x4*>(a.part_o + prow * D + e) = oacc[j][k];
-      }
-      if (w == 0 && g4 == 0) {
-        a.part_ml[prow * 2 + 0] = m;
-        a.part_ml[prow * 2 + 1] = l;
-      }
+    for (int db = 0; db < NB; ++db) *reinterpret_cast<f32x4*>(po + 16 * db) = oacc[db];
+    if (g4 == 0) {
+      a.part_ml[prow * 2 + 0] = m_run;
+      a.part_ml[prow * 2 + 1] = l_run;
     }
   }
 }
 
-template <int D, int G, int NCB, bool OBF>
+template <int D, int G, int NCB, int NSL, bool OBF>
 hipError_t launch_mc_rk(const DecodeArgs& a, hipStream_t st) {
   DecodeArgs a1 = a;
   a1.ncb = 1;  // one workgroup per unit holds every column block
   const long long n = (long long)a.B * a.Hkv * a.nchunk;
   if (n > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   if (a.n_rot <= 64)
-    hipLaunchKernelGGL((decode_mc_kernel<D, G, NCB, 4, OBF>), dim3((unsigned)n), dim3(64 * NWM), 0,
-                       st, a1);
+    hipLaunchKernelGGL((decode_mc_kernel<D, G, NCB, NSL, 4, OBF>), dim3((unsigned)n),
+                       dim3(64 * NCB), 0, st, a1);
   else
-    hipLaunchKernelGGL((decode_mc_kernel<D, G, NCB, D / 32, OBF>), dim3((unsigned)n),
-                       dim3(64 * NWM), 0, st, a1);
+    hipLaunchKernelGGL((decode_mc_kernel<D, G, NCB, NSL, D / 32, OBF>), dim3((unsigned)n),
+                       dim3(64 * NCB), 0, st, a1);
   return hipGetLastError();
 }
 
 template <int D, int G, bool OBF>
 hipError_t launch_mc_g(const DecodeArgs& a, hipStream_t st) {
-  if (a.ncb <= 2) return launch_mc_rk<D, G, 2, OBF>(a, st);
-  return launch_mc_rk<D, G, 4, OBF>(a, st);
+  if (a.ncb <= 2) return launch_mc_rk<D, G, 2, 2, OBF>(a, st);
+  return launch_mc_rk<D, G, 4, 4, OBF>(a, st);
 }
 
 template <int D, bool OBF>
