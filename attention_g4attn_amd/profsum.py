@@ -3,9 +3,9 @@
   python -m attention_g4attn_amd.profsum stats <kernel_stats.csv> --cmd "<command>" --out <file>
   python -m attention_g4attn_amd.profsum traffic --fetch <counter_collection.csv>
       --write <counter_collection.csv> --kernel <name prefix> --copy-bytes N
-      --cmd-fetch "<command>" --cmd-write "<command>" --out <file>
+      --cmd-fetch "<command>" --cmd-write "<command>" --out <file> [--grid N] [--sources ...]
   python -m attention_g4attn_amd.profsum mfma <counter_collection.csv> --kernel <name prefix>
-      --cmd "<command>" --out <file>
+      --cmd "<command>" --out <file> [--grid N] [--sources ...]
 
 `traffic` scales FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of the kernel by
 what the same counters read for the plain device copy of --copy-bytes bytes in
@@ -49,11 +49,14 @@ def stats(args):
     open(args.out, "w").write("\n".join(lines) + "\n")
 
 
-def counter(path, name_prefix, counter_name):
-    """Per-dispatch values of one counter for kernels whose name starts with name_prefix."""
+def counter(path, name_prefix, counter_name, grid=None):
+    """Per-dispatch values of one counter for kernels whose name starts with
+    name_prefix (and, given grid, launched with that many work-items)."""
     per = {}
     for r in csv.DictReader(open(path)):
         if r["Counter_Name"] != counter_name or not r["Kernel_Name"].startswith(name_prefix):
+            continue
+        if grid is not None and int(r["Grid_Size"]) != grid:
             continue
         key = r["Dispatch_Id"]
         per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
@@ -61,8 +64,8 @@ def counter(path, name_prefix, counter_name):
 
 
 def traffic(args):
-    f_k = counter(args.fetch, args.kernel, "FETCH_SIZE")
-    w_k = counter(args.write, args.kernel, "WRITE_SIZE")
+    f_k = counter(args.fetch, args.kernel, "FETCH_SIZE", args.grid)
+    w_k = counter(args.write, args.kernel, "WRITE_SIZE", args.grid)
     f_c = counter(args.fetch, "__amd_rocclr_copyBuffer", "FETCH_SIZE")
     w_c = counter(args.write, "__amd_rocclr_copyBuffer", "WRITE_SIZE")
     if not (f_k and w_k and f_c and w_c):
@@ -75,6 +78,7 @@ def traffic(args):
     lines = [
         "# HBM traffic of one launch, from rocprofv3 counters",
         f"kernel: {args.kernel}",
+        f"grid_size: {args.grid if args.grid is not None else 'any'}",
         f"command_fetch: {args.cmd_fetch}",
         f"command_write: {args.cmd_write}",
         f"dispatches: {len(f_k)} (fetch run), {len(w_k)} (write run)",
@@ -104,6 +108,8 @@ def mfma(args):
     for r in csv.DictReader(open(args.csv)):
         if not r["Kernel_Name"].startswith(args.kernel):
             continue
+        if args.grid is not None and int(r["Grid_Size"]) != args.grid:
+            continue
         d = per.setdefault(r["Dispatch_Id"], {})
         d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
         d["_ns"] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
@@ -117,6 +123,7 @@ def mfma(args):
     lines = [
         "# Matrix-core activity of one launch, from rocprofv3 counters",
         f"kernel: {args.kernel}",
+        f"grid_size: {args.grid if args.grid is not None else 'any'}",
         f"command: {args.cmd}",
         f"dispatches: {len(per)}",
         f"sq_valu_mfma_busy_cycles_per_dispatch: {b:.6e}",
@@ -148,6 +155,7 @@ def main():
     t.add_argument("--out", required=True)
     t.add_argument("--sources", nargs="+", default=KERNEL_SOURCES,
                    help="files whose sha256 identifies the kernel version")
+    t.add_argument("--grid", type=int, default=None, help="only launches of this grid size")
     m = sub.add_parser("mfma")
     m.add_argument("csv")
     m.add_argument("--kernel", required=True)
@@ -155,6 +163,7 @@ def main():
     m.add_argument("--out", required=True)
     m.add_argument("--sources", nargs="+", default=KERNEL_SOURCES,
                    help="files whose sha256 identifies the kernel version")
+    m.add_argument("--grid", type=int, default=None, help="only launches of this grid size")
     a = ap.parse_args()
     {"stats": stats, "traffic": traffic, "mfma": mfma}[a.what](a)
 

@@ -33,7 +33,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle baseline sample")
-    ap.add_argument("--only", choices=["all", "local", "global", "decode", "fp8"], default="all",
+    ap.add_argument("--only", choices=["all", "local", "global", "decode", "fp8", "vision", "multi"], default="all",
                     help="restrict the step to one kernel kind (profiling runs)")
     ap.add_argument("--seq", type=int, default=None, help="override the prefill length")
     ap.add_argument("--no-configs", action="store_true",
@@ -47,6 +47,25 @@ PROFILES = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles")
 TRAFFIC_SUMMARY = os.path.join(PROFILES, "prefill_global_kv512_s262144_hbm_traffic.txt")
 DECODE_TRAFFIC_SUMMARY = os.path.join(PROFILES, "decode_global_kv512_b64_hbm_traffic.txt")
 MFMA_SUMMARY = os.path.join(PROFILES, "prefill_global_kv512_s262144_mfma_busy.txt")
+# the other kernels' counter summaries: (entry, file, figure)
+OTHER_COUNTERS = [
+    ("local_prefill_hbm_bytes_per_launch", "prefill_local_d256_w1024_s262144_hbm_traffic.txt",
+     "hbm_bytes_per_launch"),
+    ("local_prefill_mfma_busy", "prefill_local_d256_w1024_s262144_mfma_busy.txt",
+     "mfma_busy_fraction_at_2.4GHz"),
+    ("local_decode_hbm_bytes_per_launch", "decode_local_d256_ring512_b64_hbm_traffic.txt",
+     "hbm_bytes_per_launch"),
+    ("decode_multi_global_q4_hbm_bytes_per_launch",
+     "decode_multi_q4_global_kv512_b64_hbm_traffic.txt", "hbm_bytes_per_launch"),
+    ("decode_fp8_global_hbm_bytes_per_launch", "decode_fp8_global_kv512_b64_hbm_traffic.txt",
+     "hbm_bytes_per_launch"),
+    ("decode_fp8_local_hbm_bytes_per_launch", "decode_fp8_local_d256_ring512_b64_hbm_traffic.txt",
+     "hbm_bytes_per_launch"),
+    ("vision_budget280_b4_mfma_busy", "prefill_vision_budget280_b4_mfma_busy.txt",
+     "mfma_busy_fraction_at_2.4GHz"),
+    ("vision_budget1120_b1_mfma_busy", "prefill_vision_budget1120_b1_mfma_busy.txt",
+     "mfma_busy_fraction_at_2.4GHz"),
+]
 
 
 def measured_traffic(path=TRAFFIC_SUMMARY, key="hbm_bytes_per_launch"):
@@ -194,11 +213,16 @@ def main():
         if D_glo is not None:
             per_kind["global_decode"].append(next(pairs))
     print(f"# timed {args.steps} steps in {wall:.2f}s", file=sys.stderr, flush=True)
-    only_fp8 = args.only == "fp8"  # the fp8-cache timings alone (for counter runs)
-    extra = {} if args.no_configs or only_fp8 else time_configs(g4, inputs, torch)
-    nxt = {} if args.no_configs or only_fp8 else time_next(g4, inputs, torch)
-    if only_fp8:
+    # fp8, vision, multi: that side timing alone (for counter runs)
+    side = args.only in ("fp8", "vision", "multi")
+    extra = {} if args.no_configs or side else time_configs(g4, inputs, torch)
+    nxt = {} if args.no_configs or side else time_next(g4, inputs, torch)
+    if args.only == "fp8":
         nxt["fp8"] = time_fp8(g4, inputs, torch)
+    elif args.only == "vision":
+        nxt["vision"] = time_vision(g4, inputs, torch)
+    elif args.only == "multi":
+        nxt.update(time_next(g4, inputs, torch))
     elif not args.no_configs:
         nxt["fp8"] = time_fp8(g4, inputs, torch)
         nxt["vision"] = time_vision(g4, inputs, torch)
@@ -230,7 +254,7 @@ def main():
                                      "tok_per_s": dglo.B / tg * 1e3}
         kind_rep["group_decode_tok_per_s"] = dloc.B / (5 * tl + tg) * 1e3
 
-    if not args.no_configs and not only_fp8:
+    if not args.no_configs and not side:
         nxt["schedules"] = time_schedules(g4, inputs, torch)
 
     roof = None
@@ -243,7 +267,7 @@ def main():
                 # matrix-core busy fraction of the same launch from its counters
                 "mfma_busy": (measured_traffic(MFMA_SUMMARY, "mfma_busy_fraction_at_2.4GHz")
                               if S == inputs.GROUP_S else None),
-                "kernel": "g4a::pf::prefill_kernel<512, 8, true, false, 128, 3, 1, true, false>",
+                "kernel": "g4a::pf::prefill_kernel<512, 8, true, false, 128, 4, 1, true, false>",
                 "flops_per_launch": fl_glo, "ms_per_launch": t}
     roof_dec = None
     if run_decode:
@@ -282,6 +306,9 @@ def main():
         "roofline": roof,
         "roofline_decode": roof_dec,
         "cpu_baseline": cpu,
+        # figures of the committed counter summaries (None once the kernel changed)
+        "counters": {k: measured_traffic(os.path.join(PROFILES, f), key)
+                     for k, f, key in OTHER_COUNTERS},
     }
     if args.copy_calibration > 0:
         n = args.copy_calibration << 20
