@@ -6,6 +6,8 @@
       --cmd-fetch "<command>" --cmd-write "<command>" --out <file> [--grid N] [--sources ...]
   python -m attention_g4attn_amd.profsum mfma <counter_collection.csv> --kernel <name prefix>
       --cmd "<command>" --out <file> [--grid N] [--sources ...]
+  python -m attention_g4attn_amd.profsum raw <counter_collection.csv> --kernel <name prefix>
+      --cmd "<command>" --out <file> [--grid N] [--sources ...]
 
 `traffic` scales FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of the kernel by
 what the same counters read for the plain device copy of --copy-bytes bytes in
@@ -138,6 +140,33 @@ def mfma(args):
     open(args.out, "w").write("\n".join(lines) + "\n")
 
 
+def raw(args):
+    """Mean per dispatch of every counter (base or derived) the run collected."""
+    per = {}
+    for r in csv.DictReader(open(args.csv)):
+        if not r["Kernel_Name"].startswith(args.kernel):
+            continue
+        if args.grid is not None and int(r["Grid_Size"]) != args.grid:
+            continue
+        d = per.setdefault(r["Dispatch_Id"], {})
+        d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+        d["_ns"] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+    if not per:
+        raise SystemExit("kernel dispatches missing from the counter file")
+    names = sorted({k for d in per.values() for k in d if k != "_ns"})
+    lines = [
+        "# Counters of one launch (mean over dispatches), from rocprofv3",
+        f"kernel: {args.kernel}",
+        f"grid_size: {args.grid if args.grid is not None else 'any'}",
+        f"command: {args.cmd}",
+        f"dispatches: {len(per)}",
+        f"dispatch_seconds: {statistics.mean(d['_ns'] for d in per.values()) * 1e-9:.6f}",
+    ]
+    lines += [f"{n}: {statistics.mean(d[n] for d in per.values() if n in d):.6g}" for n in names]
+    lines += [f"source_sha256: {source_hash(args.sources)}", "sources: " + ", ".join(args.sources)]
+    open(args.out, "w").write("\n".join(lines) + "\n")
+
+
 def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="what", required=True)
@@ -164,8 +193,16 @@ def main():
     m.add_argument("--sources", nargs="+", default=KERNEL_SOURCES,
                    help="files whose sha256 identifies the kernel version")
     m.add_argument("--grid", type=int, default=None, help="only launches of this grid size")
+    r = sub.add_parser("raw")
+    r.add_argument("csv")
+    r.add_argument("--kernel", required=True)
+    r.add_argument("--cmd", required=True)
+    r.add_argument("--out", required=True)
+    r.add_argument("--sources", nargs="+", default=KERNEL_SOURCES,
+                   help="files whose sha256 identifies the kernel version")
+    r.add_argument("--grid", type=int, default=None, help="only launches of this grid size")
     a = ap.parse_args()
-    {"stats": stats, "traffic": traffic, "mfma": mfma}[a.what](a)
+    {"stats": stats, "traffic": traffic, "mfma": mfma, "raw": raw}[a.what](a)
 
 
 if __name__ == "__main__":
