@@ -91,6 +91,7 @@ decode_split_kernel(DecodeArgs a) {
   __shared__ float mls[NW][16][2];
   __shared__ int tnext;  // next unclaimed tile of the chunk (NW > 1)
 
+
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l16 = lane & 15, g4 = lane >> 4;
@@ -239,7 +240,9 @@ decode_split_kernel(DecodeArgs a) {
     const int nrows = min(TR, r1 - (r0 + i * TR));
 #pragma unroll
     for (int j = 0; j < 4; ++j) sacc[j] = 4 * g4 + j < nrows ? sacc[j] : -INFINITY;
-    if (QL > 1) {  // wave-uniform: each column sees keys up to its own position
+    // wave-uniform: each column sees keys up to its own position, and a ring
+    // larger than the window holds keys before every column's window
+    if (QL > 1 || (W > 0 && C > W)) {
       const int rk = r0 + i * TR + 4 * g4;   // this lane's first key row
       const int m0 = W > 0 ? (P - rk) % C : 0;  // (P - row) mod C of that row
 #pragma unroll

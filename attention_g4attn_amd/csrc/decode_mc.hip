@@ -58,40 +58,6 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const unsigned char* p) {
   return __builtin_bit_cast(u32x2, v);
 }
 
-// Workgroup barrier that leaves the tile loads in flight: this wave's LDS
-// writes have completed, its vector-memory operations are not waited for.
-// (__syncthreads' release fence waits for every outstanding load, the
-// direct-to-LDS tile loads included, so with it no tile stays in flight
-// across a step.)  The memory clobber keeps the compiler from moving LDS
-// accesses across it.
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-
-// Buffer resource as four scalar words (base, stride 0, size in bytes, raw
-// 32-bit dwords), for loads issued from inline assembly.
-typedef uint32_t s32x4 __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ s32x4 rsrc_words(const void* base, uint32_t bytes) {
-  const uint64_t p = reinterpret_cast<uint64_t>(base);
-  return s32x4{(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)p),
-               (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(p >> 32)) & 0xffffu,
-               (uint32_t)__builtin_amdgcn_readfirstlane(bytes), 0x00020000u};
-}
-
-// Non-temporal 16-byte direct load into LDS (lane l's bytes at ldst + 16 l),
-// issued from inline assembly.  The compiler's wait insertion cannot tell
-// which LDS object a builtin direct load writes, so after one it waits for
-// every outstanding load before the next LDS read, which drains the ring each
-// step; it does not see this one, and the kernel orders the tile reads itself
-// (wait_vmcnt, then a barrier).  The instruction writes no register.
-__device__ __forceinline__ void lds_dma16_nt_asm(s32x4 rs, uint32_t voff, unsigned char* ldst) {
-  // the low 32 bits of a generic address in the LDS aperture are the LDS
-  // offset (the aperture is 4 GiB aligned)
-  const uint32_t m = __builtin_amdgcn_readfirstlane((uint32_t)reinterpret_cast<uintptr_t>(ldst));
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen nt lds"
-               :: "s"(m), "v"(voff), "s"(rs) : "memory", "m0");
-}
-
 // 16-byte chunk swizzle of tile row r, the split kernel's: a bijection on
 // r % 16; a score read (16 lanes = 16 rows, one chunk) and a transpose read
 // (32 lanes = 8 rows x 2 adjacent chunks) each hit 16 bank groups.

@@ -121,6 +121,12 @@ CASES = [
      (2,)),
     # separate K/V at d = 512, every pair turning, G = 4
     ("sep512", lambda L: inputs.DecodeLayer("local", 2, 8, 2, 512, 300, 0, 1e4, 1.0), (1, 5)),
+    # K=V rings with p-RoPE: keys past the ring's wrap take the second per-tile angle
+    ("kv-ring-p25", lambda L: inputs.DecodeLayer("global", 3, 16, 2, 512, 70 + L - 1, 64, 1e6,
+                                                 0.25), (1, 4)),
+    # K=V at d = 256 with 32 of 64 table pairs turning (per-pair select)
+    ("kv-d256-p25", lambda L: inputs.DecodeLayer("global", 2, 16, 2, 256, 900, 0, 1e4, 0.25),
+     (1, 2)),
 ]
 PARAMS = [(name, mk, L) for name, mk, Ls in CASES for L in Ls]
 

@@ -83,9 +83,10 @@ MULTI = [
     # local ring, G = 2: capacity exactly window + L - 1
     ("local-ring-min", lambda L: inputs.DecodeLayer("local", 3, 16, 8, 256, 64 + L - 1, 64,
                                                     1e4, 1.0), (1, 3, 8)),
-    # local ring of 512 slots plus room for the draft tokens
+    # local ring of 512 slots plus room for the draft tokens (with one token,
+    # the 7 oldest slots hold keys before the window)
     ("local-ring-512", lambda L: inputs.DecodeLayer("local", 2, 16, 8, 256, 519, 512, 1e4, 1.0),
-     (4, 8)),
+     (1, 4, 8)),
     # global K=V linear cache, G = 8: 1 to 4 column blocks, several 1024-row chunks
     ("global-kv", lambda L: inputs.DecodeLayer("global", 2, 16, 2, 512, 3000, 0, 1e6, 0.25),
      (1, 2, 3, 8)),

@@ -323,3 +323,72 @@ def test_staged_output_rows(p):
         # a 16-byte read is served 16 lanes at a time: 16 distinct bank quads
         for g in range(4):
             assert len({(lane ^ r) % 16 for lane in range(16 * g, 16 * g + 16)}) == 16
+
+
+# ---- fp8 K=V decode tiles: 16 rows of D one-byte codes, chunk c of row r at c ^ (r & 15) ----
+
+TRK = 16
+
+
+def kswz(r):
+    return r & 15
+
+
+def fp8_kv_tile(D):
+    CPR = D // 16
+    RPI = 64 // CPR
+    lds = {}
+    for n in range(TRK // RPI):
+        for ln in range(64):
+            row = n * RPI + ln // CPR
+            chunk = (ln % CPR) ^ kswz(row)
+            pos = n * 1024 + 16 * ln
+            assert pos not in lds and 0 <= chunk < CPR
+            lds[pos] = (row, 16 * chunk)
+    assert len(lds) == TRK * D // 16
+    return lds
+
+
+@pytest.mark.parametrize("D", [256, 512])
+def test_fp8_kv_decode_score_operand_reads(D):
+    """One key row per lane (row = lane % 16): the 16-byte read of chunk
+    4*u2 + gq holds the dims of k-steps 2*u2 and 2*u2 + 1 in kchunk order, and
+    each 16-lane read covers all 64 banks."""
+    lds = fp8_kv_tile(D)
+    for u2 in range(D // 64):
+        offs = []
+        for lane in range(64):
+            row, gq = lane & 15, lane >> 4
+            off = row * D + (((4 * u2 + gq) ^ kswz(row)) << 4)
+            offs.append(off)
+            for e in range(2):
+                for j in range(8):
+                    assert code_at(lds, off + 8 * e + j) == (row, 8 * kchunk(2 * u2 + e, gq) + j)
+        for g in range(4):
+            assert len(banks16(offs[16 * g:16 * g + 16])) == 64, (D, u2, g)
+
+
+@pytest.mark.parametrize("D", [256, 512])
+def test_fp8_kv_decode_value_operand_transpose_reads(D):
+    """8-bit transpose reads whose eight source rows are keys 4g .. 4g+3 twice:
+    the first four bytes lane l receives are dim 16*db + l % 16 of keys
+    4*(l // 16) .. +3, the keys its P^T operand holds (score register j of
+    lane group g is key 4g + j); no two different words share a bank."""
+    lds = fp8_kv_tile(D)
+    for db in range(D // 16):
+        src = []
+        for lane in range(64):
+            n, gq = lane & 15, lane >> 4
+            kr = 4 * gq + ((n >> 1) & 3)
+            src.append(kr * D + (n & 1) * 8 + ((db ^ kswz(kr)) << 4))
+        for half in range(2):
+            words = {w for a in src[32 * half:32 * half + 32] for w in (a >> 2, (a >> 2) + 1)}
+            banks = {}
+            for wd in words:
+                banks.setdefault(wd & 63, set()).add(wd)
+            assert all(len(v) == 1 for v in banks.values()), (D, db, half)
+        for lane in range(64):
+            grp, i = lane // 16, lane % 16
+            got = [code_at(lds, src[16 * grp + 2 * k + i // 8] + i % 8) for k in range(8)]
+            assert got[:4] == [(4 * grp + k, 16 * db + i) for k in range(4)], (D, db, lane)
+            assert got[4:] == got[:4]
