@@ -22,10 +22,12 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 // cache row is read once per launch, so it is loaded non-temporal: keeping it
 // in L2 helps nothing, and the batch-64 decodes ran at 55.4-57.0 us (local)
 // and 792-807 us (global) with the default policy against 52.4-52.5 and
-// 708-769 us non-temporal (same box).  With several column blocks (several
-// query tokens of G = 8 heads) the later blocks of a chunk read it again from
-// L2, and non-temporal loads made the 4-token global decode slower (1448 ->
-// 1643 us), so those keep the default policy.
+// 708-769 us non-temporal (same box).  With several column blocks in
+// separate workgroups (several query tokens over separate K and V caches)
+// the later blocks of a chunk read it again from L2, and non-temporal loads
+// made the 4-token global decode slower when it still ran that way (1448 ->
+// 1643 us), so those keep the default policy.  K=V caches with more than 16
+// columns read each tile once for every block (decode_mc.hip).
 constexpr int CPOL_NT = 2;
 
 // 16 bytes at voff of the resource into LDS at ldst + 16 * lane (reads past
