@@ -174,6 +174,10 @@ __device__ __forceinline__ double pair_rev(int t, int D, double log2_theta) {
 // Rotated key slab, one pass over the keys: ws[row][0 .. SW) = the first SW
 // dims of k[row] with pair t < n_rot turned by pos * theta^(-2t/D), rounded to
 // bf16; row = (b*S + j)*Hkv + hkv.  One 16-byte chunk (4 pairs) per thread.
+// The angle is reduced in fp64 and its sine and cosine come from the
+// hardware instructions, as for the queries and the decode's keys (the
+// library sincospif made the pass compute-bound: 0.52 ms for the 2 GiB of a
+// local layer at S = 262144).
 // VIS: pos is [B*S, 2] and the pairs of the chunk (all in one half) turn by
 // the component of their half.
 template <int SW, bool VIS = false>
@@ -202,7 +206,7 @@ __global__ void __launch_bounds__(256) rope_keys_kernel(const uint16_t* __restri
       for (int e = 0; e < 4; ++e) {
         const int t = 4 * c + e;
         float cs, sn;
-        rope_cs_accurate(p, g[e], cs, sn);
+        rope_cs_fast(p, g[e], cs, sn);
         const float x0 = bf_lo(x[e]), x1 = bf_hi(x[e]);
         const uint32_t r = pack_bf16(x0 * cs - x1 * sn, x0 * sn + x1 * cs);
         x[e] = t < n_rot ? r : x[e];
