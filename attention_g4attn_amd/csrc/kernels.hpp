@@ -84,12 +84,13 @@ hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t st);
 hipError_t launch_decode_bf16(const DecodeArgs& a, bool kv_shared, bool out_bf16,
                               hipStream_t st);
 hipError_t launch_decode_f32(const DecodeArgs& a, hipStream_t st);
-// K=V decode of more than 16 (query token, head) columns per KV head: every
-// column block in one workgroup, the head dims split over its waves
+// K=V decode of more than 16 (query token, head) columns per KV head: one
+// workgroup per chunk reads each cache tile once, one wave per 16-column block
 hipError_t launch_decode_mc(const DecodeArgs& a, bool out_bf16, hipStream_t st);
 // merge of the split partials (the chunks of every (token, query head))
 hipError_t launch_decode_merge(const DecodeArgs& a, bool out_bf16, hipStream_t st);
-// bf16 query over fp8 E4M3 caches; D in {256, 512}, G in {1, 2, 4, 8}
+// bf16 query over fp8 E4M3 caches; D in {256, 512}, G in {1, 2, 4, 8} (K=V
+// caches take a kernel of their own, with two 16-row tile slots per wave)
 hipError_t launch_decode_fp8(const DecodeArgs& a, bool kv_shared, bool out_bf16, hipStream_t st);
 hipError_t launch_fill_cache(const FillArgs& a, hipStream_t st);
 hipError_t launch_fill_cache_fp8(const FillArgs& a, hipStream_t st);
