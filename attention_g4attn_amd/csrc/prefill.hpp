@@ -839,22 +839,46 @@ __global__ void __launch_bounds__(NW * 64, (wg_per_cu<D, MB, NST>())) prefill_ke
       step(kt + 2, IC<2>{});
     }
   } else {
-    issue_loads(kt0, IC<0>{});
+    // Tile order: the n tiles of the (padded) span are visited starting at
+    // the one whose index is a multiple of n, wrapping round, so tile kt is
+    // computed at step (kt - kt0 + off) mod n with off = -kt0 mod n.  With
+    // a window every full span has the same length, so the workgroups that
+    // run together (consecutive query tiles of one KV head on one XCD) read
+    // each shared tile in the same step: L2 then holds a few tiles per step
+    // instead of the spans of all running windows, where the plain order
+    // reads a shared tile two steps later per query tile.  Window-1024 layer
+    // at S = 262144: 5.59 -> 5.51 ms with the key pass, same box.  Without a
+    // window kt0 = 0 and the order is the plain one.  The d = 512 instances
+    // keep the plain order: the rotation's registers make them spill.
+    constexpr bool ROT = D == 256 && !VIS;
+    const int n = ktp - kt0 + 1;
+    const int off = ROT ? (n - kt0 % n) % n : 0;
+    auto tile_at = [&](int i) {
+      if constexpr (!ROT) return kt0 + i;
+      const int j = i + off;
+      return kt0 + (j >= n ? j - n : j);
+    };
+    issue_loads(tile_at(0), IC<0>{});
     wait_vmcnt<0>();
     __syncthreads();
     // (Issuing the next tile's loads one per score group instead, which
     // needs every wave to compute every tile of the span, measured slower:
-    // 5.74 against 5.57 ms for the window-1024 layer at S = 262144.)
-    auto step = [&](int kt, auto s) {
+    // 5.74 against 5.57 ms for the window-1024 layer at S = 262144.  A split
+    // ring with the score part of each tile requested two tiles ahead, three
+    // score parts and two value parts in 80 KiB, timed 2% slower than this
+    // loop: the loads cost about 12% of the kernel, as measured by leaving
+    // them out, but not through their latency.)
+    auto step = [&](int i, auto s) {
       constexpr int S0 = decltype(s)::value;
-      if (kt + 1 <= ktp) issue_loads(kt + 1, IC<1 - S0>{});
+      if (i + 1 < n) issue_loads(tile_at(i + 1), IC<1 - S0>{});
+      const int kt = tile_at(i);
       if (visible(kt)) compute(kt, s, [](int) {});
       wait_vmcnt<0>();
       __syncthreads();
     };
-    for (int kt = kt0; kt <= ktp; kt += 2) {
-      step(kt, IC<0>{});
-      step(kt + 1, IC<1>{});
+    for (int i = 0; i < n; i += 2) {
+      step(i, IC<0>{});
+      step(i + 1, IC<1>{});
     }
   }
 

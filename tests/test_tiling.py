@@ -59,6 +59,42 @@ def test_every_tile_load_stays_inside_k(shape):
                 assert kt * BN > t_end - 1
 
 
+def rotated_order(kt0, ktp, rot=True):
+    """Tiles in the order the 2-deep loop of the d = 256 windowed instances
+    visits them: step i takes tile kt0 + (i + off) mod n, off = -kt0 mod n."""
+    n = ktp - kt0 + 1
+    off = (n - kt0 % n) % n if rot else 0
+    return [kt0 + (i + off - n if i + off >= n else i + off) for i in range(n)]
+
+
+@pytest.mark.parametrize("S,G,W", [(262144, 2, 1024), (8192, 2, 1024), (131072, 2, 512),
+                                   (1100, 2, 512), (333, 2, 64), (700, 8, 1024), (97, 1, 0)])
+def test_rotated_tile_order(S, G, W):
+    """Every span is visited exactly once; without a window the order is the
+    plain one; and two workgroups whose spans have the same length visit every
+    tile they share at the same step (the point of the rotation: the
+    workgroups that run together read a shared tile together)."""
+    NST = 2
+    TQ = 4 * 32 // G
+    step_of = {}  # span length -> {tile: step}
+    interior = set()  # span lengths of workgroups whose window starts inside the sequence
+    for t0, t_end, kt0, kt1 in wg_tiles(S, G, 1, W):
+        ktp = kt0 + (kt1 - kt0 + NST) // NST * NST - 1
+        order = rotated_order(kt0, ktp)
+        assert sorted(order) == list(range(kt0, ktp + 1))
+        if W == 0:
+            assert order == list(range(kt0, ktp + 1))
+        n = len(order)
+        seen = step_of.setdefault(n, {})
+        for i, kt in enumerate(order):
+            assert seen.setdefault(kt, i) == i, (t0, kt)
+        if W > 0 and t0 - W + 1 > 0 and t_end == t0 + TQ:
+            interior.add(n)
+    # query tiles aligned to key tiles give every interior workgroup the same
+    # span, so all of them share their tiles step for step
+    assert len(interior) <= (1 if TQ % BN == 0 else 2)
+
+
 VISION_SHAPES = [  # S, Hkv, G, valid patches per image
     (2520, 8, 1, [2520, 2520, 2520, 2496]), (10080, 8, 1, [10080]), (300, 2, 2, [300, 1, 0, 33]),
     (1100, 1, 8, [1099, 1100, 64, 65]),
