@@ -333,22 +333,13 @@ def time_configs(g4, inputs, torch, reps=5):
                                                             layer.p)),
                          dtype=torch.uint8, device="cuda")
 
-        def call():
+        def call(r):
             if layer.kind == "global":
                 g4.global_prefill(q, k, pos, 0, layer.theta, layer.p, out=out, workspace=ws)
             else:
                 g4.local_prefill(q, k, v, pos, layer.window, layer.theta, layer.p, out=out,
                                  workspace=ws)
-        call()
-        torch.cuda.synchronize()
-        stream = torch.cuda.current_stream()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(reps):
-            call()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1) / reps
+        ms = _event_time(torch, call, reps)
         fl = prefill_flops(layer)
         res[name] = {"ms": ms, "tflops": fl / ms / 1e9,
                      "frac_mfma": fl / ms / 1e9 / MFMA_BF16_PEAK_TFLOPS}
@@ -356,10 +347,22 @@ def time_configs(g4, inputs, torch, reps=5):
     return res
 
 
-def _event_time(torch, call, reps):
-    """Mean ms of reps calls on the current stream, after one warm-up call."""
-    call(0)
-    torch.cuda.synchronize()
+def _event_time(torch, call, reps, warm_s=0.05, min_s=0.1):
+    """Mean ms of call(r), r = 0, 1, ..., timed with events on the current
+    stream.  Calls first run for about warm_s seconds, so that a short kernel
+    is timed at the clock the GPU holds under load rather than while the
+    clock ramps up from idle; then at least reps calls, and enough to last
+    about min_s seconds, are timed."""
+    t0 = time.perf_counter()
+    n = 0
+    while True:
+        call(n)
+        torch.cuda.synchronize()
+        n += 1
+        if time.perf_counter() - t0 >= warm_s:
+            break
+    est = (time.perf_counter() - t0) / n
+    reps = max(reps, min(int(math.ceil(min_s / est)), 20000))
     stream = torch.cuda.current_stream()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
