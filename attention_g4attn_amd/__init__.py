@@ -284,11 +284,24 @@ def decode_multi(q, k_cache, v_cache, pos, window, theta, p, out=None, workspace
     return out
 
 
-def fill_cache(k, v, pos, k_cache, v_cache, window):
+def _fill_turn(v, theta, p):
+    """Rotary parameters of a fill: required when v is given (the keys of a
+    cache with separate values are cached turned); unused for K=V."""
+    if v is not None:
+        if theta is None or p is None:
+            raise ValueError("a cache with separate values holds turned keys: pass theta and p")
+        return float(theta), float(p)
+    return (1.0 if theta is None else float(theta)), (0.0 if p is None else float(p))
+
+
+def fill_cache(k, v, pos, k_cache, v_cache, window, theta=None, p=None):
     """Write prefill rows k, v [B, S, Hkv, d] into the caches (g4attn_fill_cache).
 
-    v None means K=V (only k_cache is written); window > 0 is a ring.
+    v None means K=V (only k_cache is written, rows copied raw); window > 0 is a
+    ring.  With v given, the keys are turned at their positions (theta, p of
+    the layer, required) before they are written, as decode expects them.
     """
+    theta, p = _fill_turn(v, theta, p)
     _input(k, 4, "k")
     B, S, Hkv, d = k.shape
     _like(v, k, (B, S, Hkv, d), "v")
@@ -302,7 +315,7 @@ def fill_cache(k, v, pos, k_cache, v_cache, window):
         _like(v_cache, k, (B, Hkv, C, d), "v_cache")
     _dev(k, v, pos, k_cache, v_cache)
     rc = _g4lib().g4attn_fill_cache(_ptr(k), _ptr(v), _ptr(pos), B, S, Hkv, d, _ptr(k_cache),
-                                  _ptr(v_cache), C, int(window), _code(k), _stream())
+                                  _ptr(v_cache), C, int(window), theta, p, _code(k), _stream())
     _check(rc, "g4attn_fill_cache")
     return k_cache, v_cache
 
@@ -328,12 +341,16 @@ def _scales(Hkv, *ts):
         _shape(t, (Hkv,), "scale")
 
 
-def fill_cache_fp8(k, v, pos, k_cache, v_cache, window, k_scale, v_scale=None):
+def fill_cache_fp8(k, v, pos, k_cache, v_cache, window, k_scale, v_scale=None, theta=None,
+                   p=None):
     """Quantize prefill rows k, v [B, S, Hkv, d] (bf16 or f32) into E4M3 caches
     [B, Hkv, capacity, d] (g4attn_fill_cache_fp8): code = E4M3(x / scale[h]).
 
-    v None means K=V (only k_cache is written, v_scale unused).
+    v None means K=V (only k_cache is written, v_scale unused).  With v given,
+    the keys are turned at their positions (theta, p required) before they
+    are quantized.
     """
+    theta, p = _fill_turn(v, theta, p)
     _input(k, 4, "k")
     B, S, Hkv, d = k.shape
     _like(v, k, (B, S, Hkv, d), "v")
@@ -351,7 +368,7 @@ def fill_cache_fp8(k, v, pos, k_cache, v_cache, window, k_scale, v_scale=None):
     _dev(k, v, pos, k_cache, v_cache, k_scale, v_scale)
     rc = _g4lib().g4attn_fill_cache_fp8(_ptr(k), _ptr(v), _ptr(k_scale), _ptr(v_scale), _ptr(pos),
                                         B, S, Hkv, d, _ptr(k_cache), _ptr(v_cache), C,
-                                        int(window), _code(k), _stream())
+                                        int(window), theta, p, _code(k), _stream())
     _check(rc, "g4attn_fill_cache_fp8")
     return k_cache, v_cache
 

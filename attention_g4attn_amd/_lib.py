@@ -21,8 +21,8 @@ SIGNATURES = {
     "g4attn_decode_noalloc": ([P, P, P, P, P, I, I, I, I, I, I, F, F, I, I, P], I),
     "g4attn_decode_multi": ([P, P, P, P, P, I, I, I, I, I, I, I, F, F, I, I, P, Z, P], I),
     "g4attn_decode_multi_workspace_bytes": ([I, I, I, I, I, I, I], Z),
-    "g4attn_fill_cache": ([P, P, P, I, I, I, I, P, P, I, I, I, P], I),
-    "g4attn_fill_cache_fp8": ([P, P, P, P, P, I, I, I, I, P, P, I, I, I, P], I),
+    "g4attn_fill_cache": ([P, P, P, I, I, I, I, P, P, I, I, F, F, I, P], I),
+    "g4attn_fill_cache_fp8": ([P, P, P, P, P, I, I, I, I, P, P, I, I, F, F, I, P], I),
     "g4attn_decode_fp8": ([P, P, P, P, P, P, P, I, I, I, I, I, I, I, F, F, I, P, Z, P], I),
     "g4attn_decode_fp8_workspace_bytes": ([I, I, I, I, I, I, I], Z),
     "g4attn_strerror": ([I], ctypes.c_char_p),

@@ -316,13 +316,28 @@ bool fill_args(g4a::FillArgs& a, const void* k, const void* v, const int32_t* po
 
 }  // namespace
 
+namespace {
+
+// Rotary parameters of a fill: the keys of a cache with separate values are
+// turned (pairs t < n_rot), so theta and p must be valid there, and the head
+// dim at most 512 (the per-block table of pair frequencies).
+int fill_turn_check(const void* v, int d, float theta, float p) {
+  if (!(theta > 0.f) || isinf(theta)) return G4A_EINVAL;
+  if (!(p >= 0.f && p <= 1.f)) return G4A_EINVAL;
+  if (v && rotated_pairs(d, p) > 0 && d > 512) return G4A_EUNSUPPORTED;
+  return G4A_OK;
+}
+
+}  // namespace
+
 G4A_API int g4attn_fill_cache(const void* k, const void* v, const int32_t* pos, int B, int S,
                               int Hkv, int d, void* k_cache, void* v_cache, int capacity,
-                              int window, int dtype, void* stream) {
+                              int window, float theta, float p, int dtype, void* stream) {
   if (B < 0 || S < 0 || Hkv <= 0 || d <= 0 || capacity <= 0 || window < 0) return G4A_EINVAL;
   if (dtype != G4A_F32 && dtype != G4A_BF16) return G4A_EUNSUPPORTED;
   const int esize = dtype == G4A_F32 ? 4 : 2;
   if (((long long)d * esize) % 16) return G4A_EUNSUPPORTED;
+  if (int rc = fill_turn_check(v, d, theta, p)) return rc;
   if (B == 0 || S == 0) return G4A_OK;
   if (!k || !pos || !k_cache || (v && !v_cache)) return G4A_EINVAL;
   if (misaligned(k) || (v && misaligned(v)) || misaligned(pos) || misaligned(k_cache) ||
@@ -332,6 +347,10 @@ G4A_API int g4attn_fill_cache(const void* k, const void* v, const int32_t* pos, 
   if (!fill_args(a, k, v, pos, B, S, Hkv, k_cache, v_cache, capacity, window,
                  (int)((long long)d * esize / 16)))
     return G4A_EINVAL;
+  a.in_f32 = dtype == G4A_F32;
+  a.d = d;
+  a.n_rot = rotated_pairs(d, p);
+  a.log2_theta = log2((double)theta);
   return finish(g4a::launch_fill_cache(a, static_cast<hipStream_t>(stream)));
 }
 
@@ -390,10 +409,11 @@ G4A_API int g4attn_decode_fp8(const void* q, const void* k_cache, const void* v_
 G4A_API int g4attn_fill_cache_fp8(const void* k, const void* v, const float* k_scale,
                                   const float* v_scale, const int32_t* pos, int B, int S, int Hkv,
                                   int d, void* k_cache, void* v_cache, int capacity, int window,
-                                  int in_dtype, void* stream) {
+                                  float theta, float p, int in_dtype, void* stream) {
   if (B < 0 || S < 0 || Hkv <= 0 || d <= 0 || capacity <= 0 || window < 0) return G4A_EINVAL;
   if (in_dtype != G4A_F32 && in_dtype != G4A_BF16) return G4A_EUNSUPPORTED;
   if (d % 16) return G4A_EUNSUPPORTED;
+  if (int rc = fill_turn_check(v, d, theta, p)) return rc;
   if (B == 0 || S == 0) return G4A_OK;
   if (!k || !pos || !k_cache || !k_scale || (v && (!v_cache || !v_scale))) return G4A_EINVAL;
   if (misaligned(k) || (v && misaligned(v)) || misaligned(pos) || misaligned(k_cache) ||
@@ -404,6 +424,8 @@ G4A_API int g4attn_fill_cache_fp8(const void* k, const void* v, const float* k_s
     return G4A_EINVAL;
   a.in_f32 = in_dtype == G4A_F32;
   a.d = d;
+  a.n_rot = rotated_pairs(d, p);
+  a.log2_theta = log2((double)theta);
   a.k_scale = k_scale;
   a.v_scale = v ? v_scale : nullptr;
   return finish(g4a::launch_fill_cache_fp8(a, static_cast<hipStream_t>(stream)));

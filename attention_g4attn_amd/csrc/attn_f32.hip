@@ -41,7 +41,8 @@ struct CacheKeys {
 };
 
 // Attention of the G query heads in qs (already rotated) over keys 0..n-1 of
-// src; writes acc/l to out rows out_h[h].
+// src, each key turned at its position (pairs t < n_rot; 0 for keys cached
+// already turned); writes acc/l to out rows out_h[h].
 template <int D, int G, class Src>
 __device__ void attend_f32(const Src& src, int n, const float (*qs)[D], float (*ps)[64],
                            const double* gt, int n_rot, float scale, float* const* out_h) {
@@ -187,7 +188,8 @@ __global__ void __launch_bounds__(64) decode_f32_kernel(DecodeArgs a) {
   src.window = a.window;
   src.capacity = a.capacity;
   src.t0 = t0;
-  attend_f32<D, G>(src, Pj - t0 + 1, qs, ps, gt, a.n_rot, a.scale, outp);
+  // a cache with separate values holds its keys turned; K=V keys are raw
+  attend_f32<D, G>(src, Pj - t0 + 1, qs, ps, gt, a.v == a.k ? a.n_rot : 0, a.scale, outp);
 }
 
 template <int D>

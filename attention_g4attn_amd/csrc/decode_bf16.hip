@@ -1,9 +1,11 @@
-// Decode attention (one query token per sequence) over a KV cache of raw bf16
-// keys/values, split along the cache length, on the gfx950 matrix cores.
+// Decode attention (one query token per sequence) over a bf16 KV cache,
+// split along the cache length, on the gfx950 matrix cores.
 //
 // What is computed: the last row of causal attention over the tokens the
-// cache holds, with each cached key rotated at its own position (the cache
-// keeps raw keys; with K=V the one tensor must stay raw to serve as values).
+// cache holds, with each cached key turned at its own position.  A cache with
+// separate values holds its keys already turned (the fill turns each key
+// once), so only the query turns here; with K=V the one tensor stays raw to
+// serve as values, and its keys are turned per tile in registers.
 // Local layers use a ring cache of `window` slots (position t in slot
 // t mod window); global layers a linear K=V cache.  Sources: "Guia visual do
 // Gemma 4" (pt.news.hada.io), sections "Intercalacao de camadas de atencao",
@@ -20,8 +22,8 @@
 // faster than 1 wave per SIMD with a 2- or 3-slot private ring).  Per tile
 // the wave
 //   - reads the key rows as A operands of the 16x16x32 product (16 rows x 8
-//     dims per lane), rotates them at their positions in registers, and forms
-//     S^T = K~ Q~^T for the G query heads (padded to 16 columns);
+//     dims per lane), turns them at their positions in registers (K=V), and
+//     forms S^T = K~ Q~^T for the G query heads (padded to 16 columns);
 //   - updates the softmax per column (the output is rescaled only when a
 //     column's max grows by more than 2^8) and packs P^T straight from the
 //     score registers as the B operand of the 16x16x16 product;
@@ -229,7 +231,8 @@ decode_split_kernel(DecodeArgs a) {
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
       u32x4 kf = KREG ? kr[s] : lds_at<u32x4>(kt, koff[s & 3] + 256 * (s >> 2));
-      if (s < RK) kf = rotate_chunk_bf16(kf, 4 * s + gq, tpos, n_rot, gtab);  // per-pair select inside
+      // per-pair select inside; keys of a separate-value cache are cached turned
+      if (KVS && s < RK) kf = rotate_chunk_bf16(kf, 4 * s + gq, tpos, n_rot, gtab);
       if (s & 1) sacc1 = mfma16x16x32(kf, qf[s], sacc1);
       else sacc0 = mfma16x16x32(kf, qf[s], sacc0);
     }

@@ -57,11 +57,14 @@ struct FillArgs {
   void* v_cache;
   int B, S, Hkv, capacity, window;
   int row_chunks;  // 16-byte chunks per cache row (d * element size / 16)
-  // quantizing fill into fp8 caches: input dtype (0 f32, 1 bf16), head dim,
-  // per-KV-head scales
+  // input dtype (0 f32, 1 bf16), head dim; the fp8 fill's per-KV-head scales
   int in_f32, d;
   const float* k_scale;
   const float* v_scale;
+  // caches with separate values hold their keys turned at their positions:
+  // pairs t < n_rot, angle pos * theta^(-2t/d)
+  int n_rot;
+  double log2_theta;
 };
 
 // bf16 inputs, matrix-core path; D in {256, 512}, G in {1, 2, 4, 8}.

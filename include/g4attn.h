@@ -149,13 +149,20 @@ int g4attn_vision_prefill(const void* q, const void* k, const void* v, void* out
                           void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * Decode: one query token per sequence against a cache of raw (unrotated)
- * keys and values; the rotation of every cached key is applied on the fly at
- * the position that key holds.
+ * Decode: one query token per sequence against a KV cache.
  *   q        [B, Hq, d]              in_dtype
- *   k_cache  [B, Hkv, capacity, d]   in_dtype
- *   v_cache  [B, Hkv, capacity, d]   in_dtype, or NULL for K=V (k_cache is
- *                                    read raw as the values)
+ *   k_cache  [B, Hkv, capacity, d]   in_dtype.  With a separate v_cache it
+ *                                    holds every key already turned at its
+ *                                    own position t (R(t) k, pairs
+ *                                    t < floor(p*d/2), as g4attn_fill_cache
+ *                                    writes it); for K=V it holds the raw
+ *                                    tensor, whose keys are turned here.
+ *   v_cache  [B, Hkv, capacity, d]   in_dtype, or NULL (or k_cache itself)
+ *                                    for K=V (k_cache is read raw as the
+ *                                    values)
+ * Turning each key once when it enters the cache, not at every step, is this
+ * library's reading of the cache the pages leave unspecified; a K=V cache
+ * cannot hold turned keys, since its values are the raw tensor.
  *   out      [B, Hq, d]              out_dtype
  *   pos      [B] int32: position P of each query token; its own key/value
  *            must already be in the cache.
@@ -205,7 +212,7 @@ int g4attn_decode_noalloc(const void* q, const void* k_cache, const void* v_cach
                           void* stream);
 
 /*
- * Cache fill: write the raw key (and value) rows of a prefill into the decode
+ * Cache fill: write the key (and value) rows of a prefill into the decode
  * cache layout, so decoding continues where the prefill ended (the KV cache
  * grows with the prompt and the generated tokens: "Visao geral do modelo
  * Gemma 4", section "Principais Consideracoes para o planejamento de
@@ -222,12 +229,19 @@ int g4attn_decode_noalloc(const void* q, const void* k_cache, const void* v_cach
  *   keep their contents.  Positions written in one call must differ modulo
  *   capacity (consecutive positions do); otherwise which row lands in a
  *   shared slot is unspecified.
+ *   theta, p: the layer's rotary base and rotated fraction (as for decode;
+ *            validated also for K=V, where they are not used).
  *   dtype: G4A_F32 or G4A_BF16; d * element size must be a multiple of 16.
- * Bytes are copied unchanged.  Returns G4A_OK or a negative status.
+ * With separate values (v given), each key row is turned at its position
+ * (pairs t < floor(p*d/2) by pos * theta^(-2t/d)) in fp32 and rounded to
+ * dtype (bf16: round to nearest even) before it is written; value rows, and
+ * the rows of a K=V cache, are copied unchanged.  A turning fill (v given,
+ * p*d >= 2) needs d <= 512 (G4A_EUNSUPPORTED otherwise).
+ * Returns G4A_OK or a negative status.
  */
 int g4attn_fill_cache(const void* k, const void* v, const int32_t* pos, int B, int S, int Hkv,
-                      int d, void* k_cache, void* v_cache, int capacity, int window, int dtype,
-                      void* stream);
+                      int d, void* k_cache, void* v_cache, int capacity, int window, float theta,
+                      float p, int dtype, void* stream);
 
 /*
  * Decode of q_len query tokens per sequence at once: the verify step of
@@ -274,8 +288,9 @@ size_t g4attn_decode_multi_workspace_bytes(int B, int q_len, int Hq, int Hkv, in
  * E4M3 with a scale per KV head is the reading this library takes.  The cache
  * is half the bytes of a bf16 one, which halves decode's memory traffic.
  *
- * Cache fill into fp8 caches: as g4attn_fill_cache (same slots, same rules),
- * each element quantized on the way:
+ * Cache fill into fp8 caches: as g4attn_fill_cache (same slots, same rules,
+ * keys of a cache with separate values turned first, in fp32), each element
+ * quantized on the way:
  *     code = E4M3(x / scale[h])
  * with the quotient rounded once to fp32 (IEEE division), then rounded to the
  * nearest E4M3 value, ties to the even mantissa; |quotient| >= 448 (infinity
@@ -289,16 +304,18 @@ size_t g4attn_decode_multi_workspace_bytes(int B, int q_len, int Hq, int Hkv, in
  */
 int g4attn_fill_cache_fp8(const void* k, const void* v, const float* k_scale,
                           const float* v_scale, const int32_t* pos, int B, int S, int Hkv, int d,
-                          void* k_cache, void* v_cache, int capacity, int window, int in_dtype,
-                          void* stream);
+                          void* k_cache, void* v_cache, int capacity, int window, float theta,
+                          float p, int in_dtype, void* stream);
 
 /*
  * Decode of q_len query tokens per sequence (1 <= q_len <= 8; 1 is ordinary
  * decode) over fp8 caches: exactly g4attn_decode_multi over the dequantized
  * cache (code value x scale of the KV head).
  *   q        [B, q_len, Hq, d]  bfloat16
- *   k_cache, v_cache  [B, Hkv, capacity, d] uint8 E4M3 codes; v_cache NULL
- *            (or equal to k_cache): K=V, the values are k_cache with k_scale
+ *   k_cache, v_cache  [B, Hkv, capacity, d] uint8 E4M3 codes, the key codes
+ *            of turned keys as g4attn_fill_cache_fp8 writes them; v_cache NULL
+ *            (or equal to k_cache): K=V, raw codes, the values are k_cache
+ *            with k_scale
  *   k_scale, v_scale  [Hkv] fp32 device arrays, positive and finite
  *   out      [B, q_len, Hq, d]  out_dtype (G4A_F32 or G4A_BF16)
  *   pos, window, capacity, theta, p: as for g4attn_decode_multi (a ring needs

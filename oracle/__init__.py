@@ -9,7 +9,8 @@ Array conventions (row-major, contiguous):
   prefill  q [B,S,Hq,d], k/v [B,S,Hkv,d], pos [B,S] int32
   decode   q [B,Hq,d], k_cache/v_cache [B,Hkv,C,d], pos [B] int32
   decode_multi q [B,L,Hq,d], caches as decode, pos [B] (last query's position)
-  fill_cache k/v [B,S,Hkv,d], pos [B,S] -> caches [B,Hkv,C,d]
+  fill_cache k/v [B,S,Hkv,d], pos [B,S] -> caches [B,Hkv,C,d]; with separate
+             values the cached keys are turned at their positions
   fp8 caches  uint8 E4M3 codes [B,Hkv,C,d] with float32 scales [Hkv]
   vision_prefill q [B,S,Hq,d], k/v [B,S,Hkv,d], pos2 [B,S,2] (w, h), lengths [B]
 Inputs are float32, or bf16 given as their uint16 bit patterns; outputs fp64.
@@ -41,6 +42,8 @@ def load(path):
     lib.g4o_probs.restype = I
     lib.g4o_rope.argtypes = [P, I, I, D, D]
     lib.g4o_rope.restype = None
+    lib.g4o_rotate_rows.argtypes = [P, I, P, L, I, I, D, D, P]
+    lib.g4o_rotate_rows.restype = I
     lib.g4o_nrot.argtypes = [I, D]
     lib.g4o_nrot.restype = I
     lib.g4o_vision_prefill.argtypes = [P, P, P, I, P, P, I, I, I, I, I, D, P, L, P]
@@ -157,11 +160,16 @@ def probs(q, k, pos, window, theta, p, b, i, h, lib=None):
 
 
 def decode(q, k_cache, v_cache, pos, window, theta, p, lib=None):
-    """One query token per sequence against a raw KV cache (v_cache None: K=V)."""
-    q, dt = _in(q)
-    k_cache, dk = _in(k_cache)
+    """One query token per sequence against a KV cache.  With v_cache, k_cache
+    holds the keys already turned at their positions (what fill_cache writes);
+    v_cache None: K=V, k_cache holds the raw tensor.  float32, bf16 bits or
+    float64 (all three arrays alike).  v_cache given as k_cache itself is K=V."""
+    if v_cache is k_cache:
+        v_cache = None
+    q, dt = _in(q, f64=True)
+    k_cache, dk = _in(k_cache, f64=True)
     if v_cache is not None:
-        v_cache, dv = _in(v_cache)
+        v_cache, dv = _in(v_cache, f64=True)
         assert dv == dk and v_cache.shape == k_cache.shape
     assert dt == dk
     B, Hq, d = q.shape
@@ -177,7 +185,10 @@ def decode(q, k_cache, v_cache, pos, window, theta, p, lib=None):
 
 
 def decode_multi(q, k_cache, v_cache, pos, window, theta, p, lib=None):
-    """L query tokens per sequence (q [B,L,Hq,d]; pos [B] = last query's position)."""
+    """L query tokens per sequence (q [B,L,Hq,d]; pos [B] = last query's position).
+    Caches as for decode (v_cache given as k_cache itself is K=V)."""
+    if v_cache is k_cache:
+        v_cache = None
     q, dt = _in(q, f64=True)
     k_cache, dk = _in(k_cache, f64=True)
     if v_cache is not None:
@@ -196,9 +207,56 @@ def decode_multi(q, k_cache, v_cache, pos, window, theta, p, lib=None):
     return out
 
 
-def fill_cache(k, v, pos, k_cache, v_cache, window, lib=None):
+def rotate_rows(x, pos, theta, p, lib=None):
+    """fp64 R(pos[b, i]) x[b, i, h] for x [B, S, H, d] (float32, bf16 bits or
+    float64) and pos [B, S]: each head vector turned at its token's position."""
+    x, dt = _in(x, f64=True)
+    B, S, H, d = x.shape
+    pos = np.ascontiguousarray(pos, dtype=np.int32)
+    assert pos.shape == (B, S)
+    out = np.empty(x.shape, np.float64)
+    rc = _lib(lib).g4o_rotate_rows(_ptr(x), dt, _ptr(pos), B * S, H, d, float(theta), float(p),
+                                   _ptr(out))
+    if rc != 0:
+        raise ValueError(f"g4o_rotate_rows failed ({rc})")
+    return out
+
+
+def f64_to_bf16_bits(x):
+    """bf16 bit patterns of fp64 values, rounded once to the nearest bf16 (8
+    significant bits), ties to even."""
+    x = np.asarray(x, np.float64)
+    m, e = np.frexp(x)  # x = m 2^e, 1/2 <= |m| < 1
+    r = np.ldexp(np.rint(m * 256.0), e - 8)
+    return (r.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+def _turned_keys(k, pos, theta, p, lib):
+    """The keys a cache with separate values holds: k turned at its positions,
+    rounded to k's element type (float32 or bf16 bits)."""
+    if theta is None or p is None:
+        raise ValueError("a cache with separate values holds turned keys: pass theta and p")
+    r = rotate_rows(k, pos, theta, p, lib)
+    if k.dtype == np.float32:
+        return r.astype(np.float32)
+    if k.dtype == np.uint16:
+        return f64_to_bf16_bits(r)
+    raise TypeError(f"keys to turn must be float32 or bf16 bits, got {k.dtype}")
+
+
+def fill_cache(k, v, pos, k_cache, v_cache, window, theta=None, p=None, lib=None):
     """Copies of k_cache (and v_cache) with the prefill rows k, v [B,S,Hkv,d] written in
-    (float32, bf16 bits, or uint8 E4M3 codes; bytes are copied unchanged)."""
+    (float32, bf16 bits, or uint8 E4M3 codes).  With separate values (v given,
+    float rows), the keys are first turned at their positions with theta and
+    p and rounded to their element type; otherwise bytes are copied unchanged."""
+    k = np.ascontiguousarray(k)
+    if v is not None and k.dtype != np.uint8:
+        k = _turned_keys(k, pos, theta, p, lib)
+    return _place(k, v, pos, k_cache, v_cache, window, lib)
+
+
+def _place(k, v, pos, k_cache, v_cache, window, lib=None):
+    """The rows k (and v) placed into copies of the caches, bytes unchanged."""
     k = np.ascontiguousarray(k)
     assert k.dtype in (np.float32, np.uint16, np.uint8), k.dtype
     kc = np.array(k_cache, copy=True, order="C")
@@ -255,17 +313,28 @@ def dequantize_e4m3(codes, scale, lib=None):
     return e4m3_values(lib)[np.asarray(codes, np.uint8)] * scale[None, :, None, None]
 
 
-def fill_cache_fp8(k, v, pos, k_cache, v_cache, window, k_scale, v_scale, lib=None):
-    """fill_cache into E4M3 caches: the rows are quantized with the per-KV-head
-    scales, then written as the plain fill writes bytes."""
+def fill_cache_fp8(k, v, pos, k_cache, v_cache, window, k_scale, v_scale, theta=None, p=None,
+                   lib=None):
+    """fill_cache into E4M3 caches: with separate values the keys are turned
+    at their positions and rounded to float32 first; the rows are quantized
+    with the per-KV-head scales, then placed as the plain fill places bytes."""
+    k = np.ascontiguousarray(k)
+    if v is not None:
+        if theta is None or p is None:
+            raise ValueError("a cache with separate values holds turned keys: pass theta and p")
+        k = rotate_rows(k, pos, theta, p, lib).astype(np.float32)
     kq = quantize_e4m3(k, k_scale, lib)
     vq = None if v is None else quantize_e4m3(v, v_scale, lib)
-    return fill_cache(kq, vq, pos, k_cache, v_cache, window, lib=lib)
+    return _place(kq, vq, pos, k_cache, v_cache, window, lib=lib)
 
 
 def decode_fp8(q, k_codes, v_codes, k_scale, v_scale, pos, window, theta, p, lib=None):
     """decode_multi over E4M3 caches (v_codes None: K=V, values use k_scale):
-    the caches are dequantized exactly in fp64 and decoded as raw caches."""
+    the caches are dequantized exactly in fp64 and decoded as decode_multi
+    reads them (with separate values the key codes are of turned keys;
+    v_codes given as k_codes itself is K=V)."""
+    if v_codes is k_codes:
+        v_codes = None
     kc = dequantize_e4m3(k_codes, k_scale, lib)
     vc = None if v_codes is None else dequantize_e4m3(v_codes, v_scale, lib)
     qf = np.asarray(q)

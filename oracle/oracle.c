@@ -95,6 +95,26 @@ void g4o_rope(double* x, int d, int n_rot, double theta, double pos) {
   }
 }
 
+/*
+ * R(pos[i]) applied to every head vector of token i: x [n, H, d] of dtype 0
+ * (fp32), 1 (bf16 bits) or 2 (fp64), pos [n]; out [n, H, d] fp64.  This is
+ * the key a separate-key cache holds for token i (see g4o_decode).
+ */
+int g4o_rotate_rows(const void* x, int dtype, const int32_t* pos, int64_t n, int H, int d,
+                    double theta, double p, double* out) {
+  if (!x || !pos || !out || n < 0 || H <= 0 || d <= 0 || d % 2 || dtype < 0 || dtype > 2 ||
+      !(theta > 0.0) || !(p >= 0.0 && p <= 1.0))
+    return G4O_EINVAL;
+  const int n_rot = g4o_nrot(d, p);
+  for (int64_t i = 0; i < n; ++i)
+    for (int h = 0; h < H; ++h) {
+      const size_t off = ((size_t)i * H + h) * (size_t)d;
+      for (int e = 0; e < d; ++e) out[off + e] = g4o_in(x, dtype, off + e);
+      g4o_rope(out + off, d, n_rot, theta, (double)pos[i]);
+    }
+  return G4O_OK;
+}
+
 /* First visible key of query index i (window 0 = unbounded). */
 static int64_t g4o_first_key(int64_t i, int window) {
   if (window <= 0) return 0;
@@ -273,9 +293,13 @@ int g4o_probs(const void* q, const void* k, int dtype, const int32_t* pos, int B
 }
 
 /*
- * Decode: one query token per sequence against a KV cache of raw (unrotated)
- * keys/values.
- *   q [B, Hq, d];  k_cache, v_cache [B, Hkv, capacity, d] (v_cache NULL: K=V);
+ * Decode: one query token per sequence against a KV cache.
+ *   q [B, Hq, d];  k_cache, v_cache [B, Hkv, capacity, d].
+ *   With a value cache, k_cache holds every key already turned at its own
+ *   position (R(t) k_t, as the fill writes it; values are never turned), so
+ *   only the query is turned here.  v_cache NULL: K=V, k_cache holds the raw
+ *   tensor, turned at each key's position for the scores and read raw as the
+ *   values.
  *   pos [B]: position of the query token, whose own key is already cached.
  *   window > 0: ring cache, capacity == window, position t lives in slot
  *               t mod window; the query sees positions max(0, P-W+1) .. P.
@@ -288,8 +312,9 @@ int g4o_decode(const void* q, const void* kc, const void* vc, int dtype, const i
                double* out) {
   int rc = g4o_check(B, 1, Hq, Hkv, d, window, theta, p);
   if (rc) return rc;
-  if (!q || !kc || !pos || !out || capacity <= 0 || (dtype != 0 && dtype != 1)) return G4O_EINVAL;
+  if (!q || !kc || !pos || !out || capacity <= 0 || dtype < 0 || dtype > 2) return G4O_EINVAL;
   if (window > 0 && capacity != window) return G4O_EINVAL;
+  const int key_turn = vc == NULL;  /* K=V: keys are turned here */
   if (!vc) vc = kc;
   const int G = Hq / Hkv, n_rot = g4o_nrot(d, p);
   const double scale = 1.0 / sqrt((double)d);
@@ -325,7 +350,7 @@ int g4o_decode(const void* q, const void* kc, const void* vc, int dtype, const i
           const int64_t slot = window > 0 ? t % window : t;
           const size_t koff = (((size_t)b * Hkv + g) * capacity + slot) * (size_t)d;
           for (int e = 0; e < d; ++e) kr[e] = g4o_in(kc, dtype, koff + e);
-          g4o_rope(kr, d, n_rot, theta, (double)t);
+          if (key_turn) g4o_rope(kr, d, n_rot, theta, (double)t);
           for (int hh = 0; hh < G; ++hh) {
             double s = 0.0;
             for (int e = 0; e < d; ++e) s += qr[hh * d + e] * kr[e];
@@ -356,7 +381,7 @@ int g4o_decode(const void* q, const void* kc, const void* vc, int dtype, const i
 }
 
 /*
- * Cache fill: the raw k (and v) rows of a prefill, written into the decode
+ * Cache fill: the k (and v) rows of a prefill, written into the decode
  * cache layout so that decoding continues where the prefill ended (the KV
  * cache grows with prompt and generated tokens: "Visao geral do modelo
  * Gemma 4", section "Principais Consideracoes para o planejamento de
@@ -368,7 +393,9 @@ int g4o_decode(const void* q, const void* kc, const void* vc, int dtype, const i
  *   window = 0 (linear): every token with 0 <= pos[b,i] < capacity goes to
  *     row pos[b,i].
  * Tokens with a negative position are not written.  Bytes are copied
- * unchanged; slots not written keep their contents.
+ * unchanged; slots not written keep their contents.  The keys of a cache with
+ * separate values are turned first (g4o_rotate_rows, then rounded to the
+ * cache's element type); this function only places rows.
  */
 int g4o_fill_cache(const void* k, const void* v, int esize, const int32_t* pos, int B, int S,
                    int Hkv, int d, int capacity, int window, void* k_cache, void* v_cache) {
@@ -397,8 +424,9 @@ int g4o_fill_cache(const void* k, const void* v, int esize, const int32_t* pos, 
  * Decode of L query tokens per sequence at once, the verify step of
  * speculative decoding (every model carries a draft model for it: "Visao
  * geral do modelo Gemma 4", section "Recursos"); L = 1 is ordinary decode.
- *   q [B, L, Hq, d]; k_cache, v_cache [B, Hkv, capacity, d] of raw rows
- *   (v_cache NULL: K=V); pos [B]: position P of the last query token.  Query
+ *   q [B, L, Hq, d]; k_cache, v_cache [B, Hkv, capacity, d] as for
+ *   g4o_decode (with a value cache the keys are cached turned; v_cache NULL:
+ *   K=V, raw); pos [B]: position P of the last query token.  Query
  *   token j sits at Pj = P - L + 1 + j, and the keys of all L tokens are
  *   already cached.
  *   window > 0: ring, position t in slot t mod capacity.  The ring holds
@@ -418,6 +446,7 @@ int g4o_decode_multi(const void* q, const void* kc, const void* vc, int dtype, c
   if (!q || !kc || !pos || !out || capacity <= 0 || L < 1 || dtype < 0 || dtype > 2)
     return G4O_EINVAL;
   if (window > 0 && capacity < window + L - 1) return G4O_EINVAL;
+  const int key_turn = vc == NULL;  /* K=V: keys are turned here */
   if (!vc) vc = kc;
   const int G = Hq / Hkv, n_rot = g4o_nrot(d, p);
   const double scale = 1.0 / sqrt((double)d);
@@ -450,7 +479,7 @@ int g4o_decode_multi(const void* q, const void* kc, const void* vc, int dtype, c
           const int64_t slot = window > 0 ? t % capacity : t;
           const size_t koff = (((size_t)b * Hkv + g) * capacity + slot) * (size_t)d;
           for (int e = 0; e < d; ++e) kr[e] = g4o_in(kc, dtype, koff + e);
-          g4o_rope(kr, d, n_rot, theta, (double)t);
+          if (key_turn) g4o_rope(kr, d, n_rot, theta, (double)t);
           double s = 0.0;
           for (int e = 0; e < d; ++e) s += qr[e] * kr[e];
           sc[jj] = s * scale;

@@ -159,7 +159,7 @@ def test_decode_multi_workspace_size():
 
 def fill(**kw):
     args = dict(k=A, v=2 * A, pos=3 * A, B=1, S=16, Hkv=8, d=256, kc=4 * A, vc=5 * A,
-                capacity=512, window=512, dtype=1, stream=None)
+                capacity=512, window=512, theta=1e4, p=1.0, dtype=1, stream=None)
     args.update(kw)
     return L.lib().g4attn_fill_cache(*args.values())
 
@@ -169,9 +169,19 @@ def fill(**kw):
     (dict(B=-1), -1), (dict(Hkv=0), -1), (dict(capacity=0), -1), (dict(window=-1), -1),
     (dict(dtype=5), -2), (dict(d=4), -2),  # 8 bytes a row: not whole 16-byte chunks
     (dict(k=A + 2), -3), (dict(kc=4 * A + 8), -3),
+    (dict(theta=0.0), -1), (dict(theta=float("inf")), -1), (dict(p=-0.5), -1), (dict(p=2.0), -1),
+    (dict(theta=0.0, v=None), -1),  # checked for K=V too
+    (dict(d=1024), -2),             # keys turned with d > 512
 ])
 def test_fill_cache_validation(kw, code):
     assert fill(**kw) == code
+
+
+def test_fill_cache_turn_limit_applies_only_when_keys_turn():
+    # d = 1024 is refused only where keys would be turned: K=V copies, and
+    # p = 0 turns nothing (these reach the alignment check and stop there)
+    assert fill(d=1024, v=None, k=A + 2) == -3
+    assert fill(d=1024, p=0.0, k=A + 2) == -3
 
 
 def test_fill_cache_empty_is_noop():
@@ -222,7 +232,7 @@ def test_decode_fp8_workspace_size():
 
 def fill8(**kw):
     args = dict(k=A, v=2 * A, ks=6 * A, vs=7 * A, pos=3 * A, B=1, S=16, Hkv=8, d=256, kc=4 * A,
-                vc=5 * A, capacity=512, window=512, dtype=1, stream=None)
+                vc=5 * A, capacity=512, window=512, theta=1e4, p=1.0, dtype=1, stream=None)
     args.update(kw)
     return L.lib().g4attn_fill_cache_fp8(*args.values())
 
@@ -233,6 +243,7 @@ def fill8(**kw):
     (dict(capacity=0), -1), (dict(window=-1), -1),
     (dict(dtype=5), -2), (dict(d=24), -2),  # rows must be whole 16-code chunks
     (dict(k=A + 2), -3), (dict(kc=4 * A + 8), -3), (dict(vs=7 * A + 4), -3),
+    (dict(theta=-1.0), -1), (dict(p=1.5), -1), (dict(d=1024), -2),
 ])
 def test_fill_cache_fp8_validation(kw, code):
     assert fill8(**kw) == code

@@ -109,10 +109,12 @@ def test_decode_multi_checks(kw, exc, msg):
     (dict(v_cache=None), ValueError, "v_cache"),
     (dict(pos=T(1, 16, dtype=i64)), TypeError, "pos"),
     (dict(v=T(1, 16, 4, 256)), ValueError, "v"),
+    (dict(theta=None), ValueError, "turned keys"),
+    (dict(p=None), ValueError, "turned keys"),
 ])
 def test_fill_cache_checks(kw, exc, msg):
     a = dict(k=T(1, 16, 8, 256), v=T(1, 16, 8, 256), pos=T(1, 16, dtype=i32),
-             k_cache=T(1, 8, 32, 256), v_cache=T(1, 8, 32, 256), window=32)
+             k_cache=T(1, 8, 32, 256), v_cache=T(1, 8, 32, 256), window=32, theta=1e4, p=1.0)
     a.update(kw)
     with pytest.raises(exc, match=msg):
         g4.fill_cache(**a)
@@ -127,11 +129,12 @@ u8 = torch.uint8
     (dict(k_scale=T(4, dtype=f32)), ValueError, "scale"),
     (dict(k_scale=T(8, dtype=bf)), TypeError, "scale"),
     (dict(v_scale=None), ValueError, "v_scale"),
+    (dict(theta=None), ValueError, "turned keys"),
 ])
 def test_fill_cache_fp8_checks(kw, exc, msg):
     a = dict(k=T(1, 16, 8, 256), v=T(1, 16, 8, 256), pos=T(1, 16, dtype=i32),
              k_cache=T(1, 8, 32, 256, dtype=u8), v_cache=T(1, 8, 32, 256, dtype=u8), window=32,
-             k_scale=T(8, dtype=f32), v_scale=T(8, dtype=f32))
+             k_scale=T(8, dtype=f32), v_scale=T(8, dtype=f32), theta=1e4, p=1.0)
     a.update(kw)
     with pytest.raises(exc, match=msg):
         g4.fill_cache_fp8(**a)

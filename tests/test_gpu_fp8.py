@@ -1,17 +1,20 @@
 """Low-precision (FP8 E4M3) KV caches through the C ABI, against the fp64 oracle
 (GPU).
 
-- g4attn_fill_cache_fp8 quantizes: its codes are compared bit for bit with
+- g4attn_fill_cache_fp8 quantizes: its codes are compared with
   oracle.fill_cache_fp8 (bf16 and fp32 inputs; ring, wrapped ring, linear and
   K=V caches; quotients that saturate, that fall in the subnormal range, and
-  that sit exactly halfway between two codes).
+  that sit exactly halfway between two codes) bit for bit, except the turned
+  keys of caches with separate values (fp32 turn on the GPU, exact in the
+  oracle): a quotient next to a rounding boundary may take the neighbouring
+  code there.
 - g4attn_decode_fp8 is compared element by element with oracle.decode_fp8 on
   the same codes and scales: ring and linear caches, K=V and separate K/V at
   d = 256 and 512, G = 1 to 8, 1 to 8 query tokens (1 to 4 column blocks),
   several 1024-row chunks (merge kernel), ragged last tiles, bf16 output,
   positions out of range (NaN rows).
 - Closed loop: prefill rows -> fill_cache_fp8 -> decode_fp8 matches the
-  oracle's fill (bit for bit) and decode of the same rows.
+  oracle's fill (as above) and decode of the same rows.
 - Full size: batch-64 decode at the local ring-512 and the global 64K shapes,
   every sequence checked; the fill of a 256K-token global prefill, sampled
   rows checked bit for bit.
@@ -48,9 +51,22 @@ def halfway_inputs(shape, scale, dtype):
     return x.to(dtype).to(DEV)
 
 
+def assert_turned_codes(got, want, what):
+    """Codes of turned keys: equal, or neighbouring codes (no code value lies
+    between theirs) where the GPU's fp32 turn and the oracle's exact one put
+    the quotient on either side of a rounding boundary; rare."""
+    vals = oracle.e4m3_values()
+    grid = np.unique(vals[np.isfinite(vals)])
+    g, w = vals[got], vals[want]
+    lo, hi = np.minimum(g, w), np.maximum(g, w)
+    between = np.searchsorted(grid, hi, "left") - np.searchsorted(grid, lo, "right")
+    assert ((got == want) | (between == 0)).all(), f"{what}: codes more than one step apart"
+    assert (got != want).mean() < 0.01, f"{what}: {(got != want).mean():.3%} of key codes differ"
+
+
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
 @pytest.mark.parametrize("case", ["ring", "ring-wrap", "linear", "linear-kv", "halfway"])
-def test_fill_cache_fp8_bit_exact(case, dtype):
+def test_fill_cache_fp8_parity(case, dtype):
     B, Hkv, d = 2, 3, 256
     if case == "ring":
         S, C, W, off, kv = 40, 64, 64, 0, False
@@ -78,13 +94,15 @@ def test_fill_cache_fp8_bit_exact(case, dtype):
     vc = None if v is None else torch.full((B, Hkv, C, d), 0xA5, dtype=torch.uint8, device=DEV)
     want_k, want_v = oracle.fill_cache_fp8(to_oracle(k), None if v is None else to_oracle(v),
                                            pos.cpu().numpy(), np8(kc), np8(vc), W, np8(ks),
-                                           None if v is None else np8(vs))
+                                           None if v is None else np8(vs), 1e4, 1.0)
     print(f"fill_cache_fp8 {case} {dtype}", flush=True)
-    g4.fill_cache_fp8(k, v, pos, kc, vc, W, ks, None if v is None else vs)
+    g4.fill_cache_fp8(k, v, pos, kc, vc, W, ks, None if v is None else vs, 1e4, 1.0)
     torch.cuda.synchronize()
-    assert np.array_equal(np8(kc), want_k)
-    if v is not None:
-        assert np.array_equal(np8(vc), want_v)
+    if v is None:
+        assert np.array_equal(np8(kc), want_k)
+        return
+    assert np.array_equal(np8(vc), want_v)
+    assert_turned_codes(np8(kc), want_k, f"{case} {dtype}")
 
 
 def oracle_fp8(q, kc, vc, ks, vs, pos, window, theta, p):
@@ -206,8 +224,8 @@ def test_decode_fp8_many_sequences_mixed_lengths():
 @pytest.mark.parametrize("kind", ["local", "global"])
 def test_prefill_rows_fill_fp8_decode_closed_loop(kind):
     """Prefill rows quantized into the cache as a prompt and then new tokens;
-    the codes equal the oracle's, and decoding the new tokens at once equals
-    the oracle's decode of those codes."""
+    the codes match the oracle's (turned keys up to a neighbouring code), and
+    decoding the new tokens at once equals the oracle's decode of its codes."""
     L = 4
     if kind == "local":
         layer = inputs.Layer("local", 2, 300, 16, 8, 256, 64, 1e4, 1.0)
@@ -225,17 +243,20 @@ def test_prefill_rows_fill_fp8_decode_closed_loop(kind):
     for sl in (slice(0, S - L), slice(S - L, S)):
         kk, vv, pp = k[:, sl].contiguous(), None if kv else v[:, sl].contiguous(), \
             pos[:, sl].contiguous()
-        g4.fill_cache_fp8(kk, vv, pp, kc, vc, layer.window, ks, vs)
+        g4.fill_cache_fp8(kk, vv, pp, kc, vc, layer.window, ks, vs, layer.theta, layer.p)
         ok, ov = oracle.fill_cache_fp8(to_oracle(kk), None if kv else to_oracle(vv),
-                                       pp.cpu().numpy(), ok, ov, layer.window, np8(ks), np8(vs))
+                                       pp.cpu().numpy(), ok, ov, layer.window, np8(ks), np8(vs),
+                                       layer.theta, layer.p)
     last = torch.full((layer.B,), S - 1, dtype=torch.int32, device=DEV)
     print(f"fp8 closed loop {layer} C={C}", flush=True)
     out = g4.decode_fp8(q[:, S - L:].contiguous(), kc, vc, ks, vs, last, layer.window,
                         layer.theta, layer.p)
     torch.cuda.synchronize()
-    assert np.array_equal(np8(kc), ok)
-    if not kv:
+    if kv:
+        assert np.array_equal(np8(kc), ok)
+    else:
         assert np.array_equal(np8(vc), ov)
+        assert_turned_codes(np8(kc), ok, f"closed loop {kind}")
     ref = oracle.decode_fp8(to_oracle(q[:, S - L:]), ok, ov, np8(ks), np8(vs),
                             last.cpu().numpy(), layer.window, layer.theta, layer.p)
     assert_parity(out, ref, torch.bfloat16, f"fp8 closed loop {kind}")
@@ -270,8 +291,8 @@ def test_fill_fp8_group_global_prefill_s262144_sampled_rows():
 
 
 def test_decode_fp8_ring_at_large_positions():
-    """Ring decode at positions near 2^24 (the angle reduction and the
-    angle-addition tables at large arguments), 3 query tokens, G = 2."""
+    """Ring decode at positions near 2^24 (the queries' angle reduction at
+    large arguments; the keys are cached turned), 3 query tokens, G = 2."""
     layer = inputs.DecodeLayer("local", 2, 16, 8, 256, 64 + 2, 64, 1e4, 1.0)
     q, kc, vc, ks, vs, _, _ = inputs.decode_inputs_fp8(layer, 73, 0, DEV,
                                                        torch.tensor([66, 66]), 3)

@@ -23,6 +23,7 @@ import pytest
 import torch
 
 import oracle
+from tests import brute
 
 F8 = torch.float8_e4m3fn
 
@@ -134,10 +135,12 @@ def test_decode_fp8_equals_decode_of_the_values(kv_shared):
 @pytest.mark.parametrize("kind", ["ring", "linear-kv"])
 def test_closed_loop_on_grid_inputs_equals_prefill(kind):
     """Keys and values already on the fp8 grid (code value x head scale, also
-    exact in bf16) survive quantization, so fill + decode gives the prefill rows."""
+    exact in bf16) survive quantization, so fill + decode gives the prefill rows.
+    The ring (separate values) uses p = 0, where turning the keys is the
+    identity, so they stay on the grid; the turned fill is pinned below."""
     rng = np.random.default_rng(13)
     if kind == "ring":
-        B, S, L, Hq, Hkv, d, W, C, theta, p, shared = 2, 29, 3, 4, 2, 16, 8, 10, 1e4, 1.0, False
+        B, S, L, Hq, Hkv, d, W, C, theta, p, shared = 2, 29, 3, 4, 2, 16, 8, 10, 1e4, 0.0, False
     else:
         B, S, L, Hq, Hkv, d, W, C, theta, p, shared = 1, 21, 2, 8, 1, 32, 0, 24, 1e6, 0.25, True
     tv = torch_values()
@@ -152,10 +155,43 @@ def test_closed_loop_on_grid_inputs_equals_prefill(kind):
     kc = np.full((B, Hkv, C, d), 0x7F, np.uint8)  # NaN codes where nothing is written
     vc = None if shared else kc.copy()
     kc, vc = oracle.fill_cache_fp8(k, None if shared else v, pos, kc, vc, W, ks,
-                                   None if shared else vs)
+                                   None if shared else vs, theta, p)
     got = oracle.decode_fp8(q[:, S - L:], kc, vc, ks, None if shared else vs,
                             np.full(B, S - 1, np.int32), W, theta, p)
     np.testing.assert_allclose(got, pre[:, S - L:], rtol=0, atol=1e-13)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_fill_fp8_with_separate_values_turns_then_quantizes_the_keys(dtype):
+    """Key codes are E4M3(float32(R(t) k_t) / scale): the brute-force rotation,
+    rounded to float32, through the encoder pinned above; value codes are
+    E4M3(v / scale) unturned."""
+    rng = np.random.default_rng(21)
+    B, S, Hkv, d, C, theta, p = 2, 11, 2, 16, 12, 1e4, 1.0
+    k = rng.standard_normal((B, S, Hkv, d)).astype(np.float32)
+    v = rng.standard_normal((B, S, Hkv, d)).astype(np.float32)
+    pos = (np.arange(S, dtype=np.int32) + 300)[None].repeat(B, 0)
+    kin, vin = k, v
+    kf = k.astype(np.float64)
+    if dtype == "bf16":
+        kin = (k.view(np.uint32) >> 16).astype(np.uint16)
+        vin = (v.view(np.uint32) >> 16).astype(np.uint16)
+        kf = oracle.bf16_bits_to_f64(kin)
+        v = oracle.bf16_bits_to_f64(vin).astype(np.float32)
+    ks = np.array([0.05, 0.2], np.float32)
+    vs = np.array([0.1, 0.07], np.float32)
+    kt = brute.rotate(kf, pos, theta, d // 2).astype(np.float32)
+    want_k = torch_encode(kt / ks[None, None, :, None])
+    want_v = torch_encode(v / vs[None, None, :, None])
+    z = np.full((B, Hkv, C, d), 0x7F, np.uint8)
+    kc, vc = oracle.fill_cache_fp8(kin, vin, pos, z, z, C, ks, vs, theta, p)
+    for b in range(B):
+        for i in range(S - C, S):
+            s = pos[b, i] % C
+            assert np.array_equal(kc[b, :, s], want_k[b, i])
+            assert np.array_equal(vc[b, :, s], want_v[b, i])
+    with pytest.raises(ValueError):
+        oracle.fill_cache_fp8(kin, vin, pos, z, z, C, ks, vs)
 
 
 # --- mutants ---------------------------------------------------------------------
