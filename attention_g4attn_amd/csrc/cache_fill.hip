@@ -5,7 +5,7 @@
 //
 // Bound by HBM: one thread per 16-byte chunk, consecutive threads along a row,
 // so reads and writes are coalesced row by row.  A cache with separate values
-// stores its keys already turned at their positions (RoPE / p-RoPE, sections
+// stores its keys already turned at their positions (RoPE / p-RoPE, section
 // "p-RoPE" of "Guia visual do Gemma 4"), once, so that no decode step turns
 // them again; a K=V cache stores the raw tensor, which the decode reads raw
 // as the values.  The fp8 variant quantizes on the way (16 elements per
@@ -17,8 +17,9 @@ namespace g4a {
 
 namespace {
 
-// Revolutions per position of every turning pair of the head, for one block.
-// Returns true when this launch turns keys at all (separate values, n_rot > 0).
+// Revolutions per position of every pair of the head (a bf16 chunk turn reads
+// all four pairs of its chunk before selecting), for one block.  Returns true
+// when this launch turns keys at all (separate values, n_rot > 0).
 __device__ __forceinline__ bool build_turn_table(const FillArgs& a, double* gtab) {
   if (!a.v || a.n_rot == 0) return false;
   for (int t = threadIdx.x; t < a.d / 2; t += 256) gtab[t] = rope_rev_per_pos(t, a.d, a.log2_theta);
