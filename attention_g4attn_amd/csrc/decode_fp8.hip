@@ -192,8 +192,7 @@ decode_fp8_kernel(DecodeArgs a) {
 
   // scores of tile i: half h holds keys 8*gq + 4h + j in register j of lane
   // (gq, column); the two halves are two independent accumulation chains
-  auto scores = [&](int i, f32x4& s0, f32x4& s1) {
-    const int rr0 = r0 + i * TR8;
+  auto scores = [&](f32x4& s0, f32x4& s1) {
     int ln = lane;
     asm volatile("" : "+v"(ln));
     const int row = ln & 15, gq = ln >> 4;
@@ -292,7 +291,7 @@ decode_fp8_kernel(DecodeArgs a) {
     const int tn = claim();
     wait_vmcnt<NLD>();  // keys of t (its values may still be in flight)
     f32x4 s0, s1;
-    scores(t, s0, s1);
+    scores(s0, s1);
     if (tn < nt) issue(kbase, tn, kt);
     const u32x4 pf = softmax(t, s0, s1);
     if (tn < nt) wait_vmcnt<NLD>();  // values of t (the next keys may be in flight)
