@@ -179,6 +179,10 @@ int g4attn_vision_prefill(const void* q, const void* k, const void* v, void* out
  *   bytes for split partial results; its contents need no initialisation
  *   and are garbage afterwards.  Calls that share one workspace must be
  *   ordered on one stream.
+ * The waves of a workgroup claim cache tiles at run time, so the order of
+ * the partial sums, and the running max against which each P is rounded to
+ * bf16, can vary from call to call: results are reproducible to that
+ * rounding (about 1e-4 for unit-variance inputs), not bit for bit.
  * Returns G4A_OK or a negative status.
  */
 int g4attn_decode(const void* q, const void* k_cache, const void* v_cache, void* out,

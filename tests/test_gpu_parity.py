@@ -196,6 +196,29 @@ def test_decode_bf16_output(layer):
     assert np.all(np.abs(got - ref) <= 1e-2 + 2.0 ** -8 * np.abs(ref))
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
+def test_decode_value_cache_given_as_the_key_cache_is_k_equals_v(dtype):
+    """v_cache passed as k_cache itself is K=V: the keys are read raw and
+    turned (a separate value cache would mean keys cached turned), the same
+    result as v_cache = None, on the GPU and in the oracle.  (Two decodes of
+    the same inputs may differ slightly: waves claim tiles at run time, so a
+    column's reference max, against which P is rounded to bf16, and the
+    order the partials are summed in vary; about 1e-4 here.)"""
+    layer = inputs.DecodeLayer("global", 2, 16, 2, 512, 1500, 0, 1e6, 0.25)
+    lengths = torch.tensor([1500, 37])
+    q, kc, _, pos, _ = inputs.decode_inputs(layer, 97, 0, dtype, DEV, lengths)
+    print(f"decode v_cache=k_cache {dtype}", flush=True)
+    a = g4.decode(q, kc, None, pos, 0, layer.theta, layer.p)
+    b = g4.decode(q, kc, kc, pos, 0, layer.theta, layer.p)
+    torch.cuda.synchronize()
+    # reading the keys as cached turned would move the scores by O(1)
+    assert (a - b).abs().max().item() <= 2e-3
+    qo, ko, po = to_oracle(q), to_oracle(kc), pos.cpu().numpy()
+    ref = oracle.decode(qo, ko, None, po, 0, layer.theta, layer.p)
+    assert np.array_equal(oracle.decode(qo, ko, ko, po, 0, layer.theta, layer.p), ref)
+    assert_parity(b, ref, dtype, "v_cache = k_cache")
+
+
 def test_decode_ring_bad_positions_nan():
     """The ring path finishes rows in place: a negative position gives NaN there too."""
     layer = inputs.DecodeLayer("local", 3, 4, 2, 256, 512, 512, 1e4, 1.0)
