@@ -224,7 +224,9 @@ def rotate_rows(x, pos, theta, p, lib=None):
 
 def f64_to_bf16_bits(x):
     """bf16 bit patterns of fp64 values, rounded once to the nearest bf16 (8
-    significant bits), ties to even."""
+    significant bits), ties to even; overflow gives infinity.  (Below 2^-126,
+    bf16's subnormal range, this keeps 8 significant bits instead of the
+    coarser subnormal grid; turned keys never get there.)"""
     x = np.asarray(x, np.float64)
     m, e = np.frexp(x)  # x = m 2^e, 1/2 <= |m| < 1
     r = np.ldexp(np.rint(m * 256.0), e - 8)
