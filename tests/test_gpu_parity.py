@@ -59,6 +59,9 @@ SMALL = [
     inputs.Layer("global", 1, 203, 8, 2, 512, 0, 1e6, 0.25),  # G=4: 32 tokens per workgroup
     inputs.Layer("global", 1, 211, 8, 1, 512, 96, 1e6, 0.25),  # window on the K=V path
     inputs.Layer("local", 1, 1100, 8, 4, 256, 512, 1e4, 1.0),  # small-model window 512
+    # window not a multiple of the 32-key tile: spans of 34 tiles visited in
+    # rotated order, a short span at the start, a ragged last query tile
+    inputs.Layer("local", 2, 2500, 4, 2, 256, 1000, 1e4, 1.0),
 ]
 
 
