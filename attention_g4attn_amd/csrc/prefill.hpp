@@ -303,10 +303,12 @@ __device__ __noinline__ void exact_row(const uint16_t* qp, const uint16_t* kp, c
 // s < SW/16 read the slab, the others the raw key tile.
 // NST = LDS ring depth (2 or 3): each tile is computed whole (scores,
 // softmax, value product) while the next one or two tiles load.
-// SPREAD: the loads of tile kt+2 are issued one at a time inside the score
-// products of tile kt instead of all at once before them.  Every wave must then
-// compute every tile that holds a visible key for any wave of the workgroup,
-// which holds without a window when a workgroup's tokens fit in one tile.
+// SPREAD: the software-pipelined loop of the global K=V instances.  The loads
+// of tile kt+NST-1 are issued one at a time inside the score products of tile
+// kt+1, and pairs of waves share their 64 rows' value products (each wave
+// keeps half of the output dims).  Every wave must then compute every tile
+// that holds a visible key for any wave of the workgroup, which holds
+// without a window when a workgroup's tokens fit in one tile.
 template <int D, int G, bool KVS, bool OBF, int SW, int NST, int MB, bool SPREAD, bool VIS>
 __global__ void __launch_bounds__(NW * 64, (wg_per_cu<D, MB, NST>())) prefill_kernel(PrefillArgs a) {
   constexpr int RW = 32 * MB;          // rows per wave
@@ -316,12 +318,13 @@ __global__ void __launch_bounds__(NW * 64, (wg_per_cu<D, MB, NST>())) prefill_ke
   constexpr int NSS = SW / 16;         // k-steps read from the slab
   constexpr int NDB = D / 32;          // 32-dim blocks of the output
   using L = Lds<D, KVS, SW, NST>;
-  static_assert(L::TOTAL <= 160 * 1024, "LDS budget");
+  static_assert(L::TOTAL + (SPREAD ? 2 * NW * 2 * 1024 : 0) <= 160 * 1024, "LDS budget");
+  static_assert(!SPREAD || (D == 512 && NW == 4), "pairs of waves split the 512 output dims");
   static_assert(SW >= 128 && SW <= D && NDS % 8 == 0 && NSS % 8 == 0, "tile shape");
   static_assert(L::STAGE % (1024 * NW) == 0, "stage = whole direct loads per wave");
   static_assert(NST >= 2 && NST <= 4, "ring");
-  static_assert(!SPREAD || (NST == 4 && TQ <= BN && MB == 1),
-                "the pipelined loop needs the 4-deep ring, TQ <= BN and one block per wave");
+  static_assert(!SPREAD || ((NST == 3 || NST == 4) && TQ <= BN && MB == 1),
+                "the pipelined loop needs a 3- or 4-deep ring, TQ <= BN and one block per wave");
   static_assert(NST != 4 || SPREAD, "the 4-deep ring is the pipelined loop's");
   static_assert(!VIS || (!SPREAD && SW == D && D % 64 == 0), "vision: full slab, halves of whole chunks");
   // With two query blocks per wave, or at two workgroups per CU, the score
@@ -333,6 +336,10 @@ __global__ void __launch_bounds__(NW * 64, (wg_per_cu<D, MB, NST>())) prefill_ke
   __shared__ __attribute__((aligned(16))) unsigned char st1[L::STAGE];
   __shared__ __attribute__((aligned(16))) unsigned char st2[NST >= 3 ? L::STAGE : 16];
   __shared__ __attribute__((aligned(16))) unsigned char st3[NST >= 4 ? L::STAGE : 16];
+  // pipelined instances: P of each wave's rows, passed to the other wave of
+  // its pair ([step parity][wave][key half][lane], 16 bytes each)
+  constexpr int PXB = SPREAD ? 2 * NW * 2 * 1024 : 16;
+  __shared__ __attribute__((aligned(16))) unsigned char pxb[PXB];
   // ring stage s (a compile-time constant) -> its LDS object
   auto stp = [&](auto s) -> unsigned char* {
     if constexpr (decltype(s)::value == 0) return st0;
@@ -728,70 +735,74 @@ __global__ void __launch_bounds__(NW * 64, (wg_per_cu<D, MB, NST>())) prefill_ke
   // The tile count is padded up to a multiple of the ring depth; padding tiles
   // lie past the last query token, so every key in them is masked.
   const int ktp = kt0 + (kt1 - kt0 + NST) / NST * NST - 1;  // last (padded) tile
-  if constexpr (NST == 4) {
+  if constexpr (SPREAD) {
     static_assert(L::NLD <= NDS / FG, "one load per score group");
     // Software-pipelined loop (SPREAD instances: K=V, no window, TQ <= BN, so
     // every wave computes every tile up to the workgroup's last token kt1).
-    // Step kt enters with the scores of tile kt done (unmasked) and tiles
-    // kt, kt+1 in LDS.  It runs the score products of tile kt+1 with the
-    // loads of tile kt+3 issued one per group, then the softmax of tile kt
-    // (its scores long complete, so no wait for the chain), then the value
-    // products of tile kt.  The barrier at the end frees the stage of tile kt
-    // for the loads of tile kt+4.  Loads past the last tile repeat it
-    // (clamped) and are drained at the end.
-    // Measured with shader-clock stamps (S = 32768, 32/4 heads, 2.04 GHz):
-    // a tile took 3680 cycles with the softmax placed between the score
-    // products, 3460 with it after the chain (vector instructions between
-    // dependent products slow the chain more than they save), and 3180 with
-    // no loads at all; moving half the loads into the value chain, or
-    // issuing them from inline assembly so that only one tile's loads are
-    // waited for at the barrier, timed slower.  Same-box timings: 27.1-27.3
-    // ms against 27.5-27.7 ms for the unpipelined 3-deep loop.
-    issue_loads(kt0, IC<0>{});
-    issue_loads(kt0 + 1, IC<1>{});
-    issue_loads(kt0 + 2, IC<2>{});
-    wait_vmcnt<2 * L::NLD>();
-    __syncthreads();
-    f32x16 sa[MB], sb[MB];
-    scores(IC<0>{}, sa, [](int) {}, [](int) {});
-    wait_vmcnt<L::NLD>();
-    __syncthreads();
-    auto step = [&](int kt, auto s, f32x16 (&cur)[MB], f32x16 (&nxt)[MB]) {
-      constexpr int S0 = decltype(s)::value;
-      if (kt > kt1) return;  // padding steps of the unrolled loop
-      mask(kt, cur);
-      float mr[MB], pe[MB], lp[MB][2];
+    // Same-box timings against one wave per row block on a 4-deep ring
+    // (outputs bit for bit the same): S = 32768 at 32/4 heads 26.55 against
+    // 27.19-27.30 ms, S = 262144 at 16/2 heads 842 against 861 ms.  The
+    // 3-deep ring alone measured the same as the 4-deep one: the fence of
+    // each barrier makes every load land within the step that issues it.
+    //
+    // Waves 2m and 2m+1 form a pair that shares their 64 query rows: each
+    // wave computes the scores and P of its own 32 rows, and keeps the output
+    // of all 64 rows for half of the 512 dims (half = w & 1).  Each value
+    // fragment read from LDS then feeds two products (own rows, partner's
+    // rows), so a wave reads 16 KiB of value operands per tile instead of 32;
+    // the partner's P (2 KiB) comes through LDS.  Every output element sums
+    // the same products in the same order as with one wave per row block.
+    //
+    // Step kt enters with P of tile kt made and stored in the exchange buffer
+    // and tiles kt, kt+1 in LDS.  It runs the score products of tile kt+1
+    // with the loads of tile kt+NST-1 issued one per group, then the value
+    // products of tile kt (both waves' P of tile kt read back from the
+    // buffer, so no P stays in registers across the score products) with the
+    // softmax of tile kt+1 made two score registers per group of value
+    // products, and stores that P.  The barrier at the
+    // end frees the stage of tile kt and publishes the new P.  Loads past the
+    // last tile repeat it (clamped) and are drained at the end.
+    const int half = w & 1;  // output dims 256*half .. +255, wave-uniform
+    auto pslot = [&](int par, int wave, int k2) -> unsigned char* {
+      return pxb + ((par * NW + wave) * 2 + k2) * 1024 + lane * 16;
+    };
+    auto put_p = [&](int par, const u32x4 (&pd)[MB][2]) {
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2) *reinterpret_cast<u32x4*>(pslot(par, w, k2)) = pd[0][k2];
+    };
+    auto get_p = [&](int par, int wave, u32x4 (&pd)[MB][2]) {
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2) pd[0][k2] = *reinterpret_cast<const u32x4*>(pslot(par, wave, k2));
+    };
+    // Softmax of one tile's scores sc into P: mask and reference first, then
+    // begin_tile; part(g) makes P for score register g (the pair (g-1, g) is
+    // packed once g is odd); end_tile adds the tile's sums.  The sums of the
+    // two key halves are kept apart and added in the order of the unpipelined
+    // loop, so both loops give bit-identical rows.
+    float mr[MB], pe[MB], lp[MB][2];
+    auto begin_tile = [&](int kt, f32x16 (&sc)[MB]) {
+      mask(kt, sc);
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
-        ref_max(cur, mb);
+        ref_max(sc, mb);
         mr[mb] = m_ref[mb] == UNSET ? 0.f : m_ref[mb];
         pe[mb] = 0.f;
         lp[mb][0] = lp[mb][1] = 0.f;
       }
-      u32x4 pf[MB][2];
-      // P for score register g of every block: the pair (g-1, g) is packed
-      // into the B operand once g is odd.  The sums of the two key halves
-      // are kept apart and added in the order of the unpipelined loop, so
-      // both loops give bit-identical rows.
-      auto part = [&](int g) {
+    };
+    auto part = [&](int g, const f32x16 (&sc)[MB], u32x4 (&pd)[MB][2]) {
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(cur[mb][g], cs, -mr[mb]));
-          if (g & 1) {
-            pf[mb][g >> 3][(g & 7) >> 1] = pack_bf16(pe[mb], p);
-            lp[mb][g >> 3] += pe[mb] + p;
-          } else {
-            pe[mb] = p;
-          }
+      for (int mb = 0; mb < MB; ++mb) {
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[mb][g], cs, -mr[mb]));
+        if (g & 1) {
+          pd[mb][g >> 3][(g & 7) >> 1] = pack_bf16(pe[mb], p);
+          lp[mb][g >> 3] += pe[mb] + p;
+        } else {
+          pe[mb] = p;
         }
-      };
-      const TileSrc t = tile_src(kt + 3);
-      if (kt < kt1)
-        scores(IC<(S0 + 1) % 4>{}, nxt, [&](int g) {
-          if (g < L::NLD) load_one(t, IC<(S0 + 3) % 4>{}, g);
-        }, [](int) {});
-#pragma unroll
-      for (int g = 0; g < 16; ++g) part(g);
+      }
+    };
+    auto end_tile = [&]() {
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
 #pragma unroll
@@ -802,19 +813,113 @@ __global__ void __launch_bounds__(NW * 64, (wg_per_cu<D, MB, NST>())) prefill_ke
           l_run[mb] += lp[mb][k2];
         }
       }
-      values(s, [&](u32x4 (&po)[MB][2], auto k2c) {
-        constexpr int K2 = decltype(k2c)::value;
+    };
+    // O^T += V^T P^T for this wave's half of the dims, own rows in output
+    // blocks 0..7 and the partner's rows in blocks 8..15, with both P read
+    // from the exchange buffer of parity par; side(g) runs after group g of
+    // value fragments
+    auto values_pair = [&](auto stage, int par, auto&& side) {
+      u32x4 pown[MB][2], ppar[MB][2];
+      get_p(par, w, pown);
+      get_p(par, w ^ 1, ppar);
+      // dims 256*half start 512 bytes into each raw row, a whole number of
+      // 256-byte swizzle blocks
+      unsigned char* sp = stp(stage) + 512 * half;
+      uint32_t ln = (uint32_t)lane;
+      const uint32_t tr_i = ln & 15, tr_g = ln >> 4;
+      const uint32_t tr_row = 4 * (tr_g >> 1) + (tr_i >> 2);
+      const uint32_t tr_x = 2 * (tr_g & 1) + ((tr_i & 3) >> 1);
+      const uint32_t v0 = tr_row * (2 * D) + (tr_i & 1) * 8 + ((tr_x ^ (uint32_t)swz((int)tr_row)) << 4);
+      const uint32_t v1 = (v0 ^ 32u) + 8 * (2 * D);
+      auto vfrag = [&](int db, int k2) -> u32x4 {
+        const int off = L::VOFF + 256 * (db >> 2) + (16 * k2) * (2 * D);
+        const uint32_t x = (uint32_t)(db & 3) << 6;
+        const u32x2 lo = lds_read_tr16(sp + off + (v0 ^ x));
+        const u32x2 hi = lds_read_tr16(sp + off + (v1 ^ x));
+        return u32x4{lo[0], lo[1], hi[0], hi[1]};
+      };
+      constexpr int NH = NDB / 2;   // 32-dim blocks of this wave's half
+      constexpr int NG = 2 * NH / FG;
+      static_assert(NH % FG == 0, "a group stays within one key half");
+      u32x4 vf[2][FG];
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) po[mb][K2] = pf[mb][K2];
-      }, [](int) {});
-      wait_vmcnt<L::NLD>();
+      for (int i = 0; i < FG; ++i) vf[0][i] = vfrag(i % NH, i / NH);
+#pragma unroll
+      for (int g = 0; g < NG; ++g) {
+        if (g + 1 < NG) {
+#pragma unroll
+          for (int i = 0; i < FG; ++i) {
+            const int f = FG * (g + 1) + i;
+            vf[(g + 1) & 1][i] = vfrag(f % NH, f / NH);
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < FG; ++i) {
+          const int f = FG * g + i;
+          oacc[0][f % NH] = mfma32x32x16(vf[g & 1][i], pown[0][f / NH], oacc[0][f % NH]);
+          oacc[0][NH + f % NH] = mfma32x32x16(vf[g & 1][i], ppar[0][f / NH], oacc[0][NH + f % NH]);
+        }
+        side(g);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    issue_loads(kt0, IC<0>{});
+    issue_loads(kt0 + 1, IC<1>{});
+    if constexpr (NST == 4) issue_loads(kt0 + 2, IC<2>{});
+    wait_vmcnt<(NST - 2) * L::NLD>();
+    __syncthreads();
+    {
+      f32x16 s0[MB];
+      u32x4 p0[MB][2];
+      scores(IC<0>{}, s0, [](int) {}, [](int) {});
+      begin_tile(kt0, s0);
+#pragma unroll
+      for (int g = 0; g < 16; ++g) part(g, s0, p0);
+      end_tile();
+      put_p(0, p0);
+    }
+    wait_vmcnt<(NST - 3) * L::NLD>();
+    __syncthreads();
+    auto step = [&](int kt, auto s, auto parc) {
+      constexpr int S0 = decltype(s)::value;
+      constexpr int PAR = decltype(parc)::value;
+      if (kt > kt1) return;  // padding steps of the unrolled loop
+      const bool more = kt < kt1;  // wave-uniform
+      u32x4 pnxt[MB][2];
+      f32x16 nxt[MB];
+      const TileSrc t = tile_src(kt + NST - 1);
+      if (more) {
+        scores(IC<(S0 + 1) % NST>{}, nxt, [&](int g) {
+          if (g < L::NLD) load_one(t, IC<(S0 + NST - 1) % NST>{}, g);
+        }, [](int) {});
+        begin_tile(kt + 1, nxt);
+      } else {
+        // last tile: the parts below run on zeros and their sums are dropped
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) nxt[mb] = f32x16{};
+      }
+      values_pair(s, PAR, [&](int g) {
+        part(2 * g, nxt, pnxt);
+        part(2 * g + 1, nxt, pnxt);
+      });
+      if (more) {
+        end_tile();
+        put_p(PAR ^ 1, pnxt);
+      }
+      wait_vmcnt<(NST - 3) * L::NLD>();
       __syncthreads();
     };
-    for (int kt = kt0; kt <= ktp; kt += 4) {
-      step(kt, IC<0>{}, sa, sb);
-      step(kt + 1, IC<1>{}, sb, sa);
-      step(kt + 2, IC<2>{}, sa, sb);
-      step(kt + 3, IC<3>{}, sb, sa);
+    // unrolled by a multiple of the ring depth and of 2 (the P buffers)
+    constexpr int U = NST == 4 ? 4 : 6;
+    for (int kt = kt0; kt <= kt1; kt += U) {
+      step(kt, IC<0>{}, IC<0>{});
+      step(kt + 1, IC<1 % NST>{}, IC<1>{});
+      step(kt + 2, IC<2 % NST>{}, IC<0>{});
+      step(kt + 3, IC<3 % NST>{}, IC<1>{});
+      if constexpr (U == 6) {
+        step(kt + 4, IC<4 % NST>{}, IC<0>{});
+        step(kt + 5, IC<5 % NST>{}, IC<1>{});
+      }
     }
     wait_vmcnt<0>();
   } else if constexpr (NST == 3) {
@@ -933,6 +1038,47 @@ __global__ void __launch_bounds__(NW * 64, (wg_per_cu<D, MB, NST>())) prefill_ke
           }
         }
       }
+    }
+  } else if constexpr (SPREAD) {
+    // each wave writes its half of the dims for its own rows (blocks 0..7)
+    // and the partner's rows (blocks 8..15); the row sums and overflow flags
+    // of the partner's rows come through LDS (the loop ended with a barrier
+    // after the last reads of the exchange buffer)
+    const float lt = l_run[0] + __shfl_xor(l_run[0], 32);
+    ovf |= __shfl_xor(ovf, 32);
+    float* xl = reinterpret_cast<float*>(pxb);
+    int* xo = reinterpret_cast<int*>(pxb + NW * 64 * 4);
+    xl[w * 64 + lane] = lt;
+    xo[w * 64 + lane] = ovf;
+    __syncthreads();
+    const float lt_p = xl[(w ^ 1) * 64 + lane];
+    const int ovf_p = xo[(w ^ 1) * 64 + lane];
+    const int rp = RW * (w ^ 1) + l32;  // the partner's row of this lane
+    const int tp = t0 + rp / G, hp = hkv * G + rp % G;
+    const int hf = w & 1;
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      const bool ok = rb ? (tp < S && !(ovf_p & 1)) : (row_ok[0] && !(ovf & 1));
+      if (!ok) continue;
+      const float inv = 1.f / (rb ? lt_p : lt);
+      const size_t obase = rb ? (((size_t)b * S + tp) * a.Hq + hp) * D
+                              : (((size_t)b * S + tq[0]) * a.Hq + hq[0]) * D;
+#pragma unroll
+      for (int db = 0; db < NDB / 2; ++db)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int dim = 256 * hf + 32 * db + 8 * g4 + 4 * hl;
+          const f32x16& o = oacc[0][(NDB / 2) * rb + db];
+          const float o0 = o[4 * g4 + 0] * inv, o1 = o[4 * g4 + 1] * inv;
+          const float o2 = o[4 * g4 + 2] * inv, o3 = o[4 * g4 + 3] * inv;
+          if constexpr (OBF) {
+            u32x2 pk = {pack_bf16(o0, o1), pack_bf16(o2, o3)};
+            *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.out) + obase + dim) = pk;
+          } else {
+            *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + obase + dim) =
+                f32x4{o0, o1, o2, o3};
+          }
+        }
     }
   } else {
 #pragma unroll

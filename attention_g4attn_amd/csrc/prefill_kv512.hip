@@ -9,9 +9,10 @@ template <int G, bool OBF>
 static hipError_t kv512(const PrefillArgs& a, hipStream_t st) {
   // without a window, 4 or 8 query heads per KV head put a workgroup's tokens
   // in one key tile: every wave computes every tile, so the loop can be
-  // software-pipelined (4-deep ring, loads spread over the products)
+  // software-pipelined (3-deep ring, loads spread over the products, pairs
+  // of waves sharing their rows' value products)
   if constexpr (G >= 4)
-    if (a.n_rot <= 64 && a.window == 0) return pf::launch<512, G, true, OBF, 128, 4, 1, true>(a, st);
+    if (a.n_rot <= 64 && a.window == 0) return pf::launch<512, G, true, OBF, 128, 3, 1, true>(a, st);
   if (a.n_rot <= 64) return pf::launch<512, G, true, OBF, 128, 3, 1>(a, st);
   return pf::launch<512, G, true, OBF, 512, 2, 1>(a, st);
 }
