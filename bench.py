@@ -267,7 +267,7 @@ def main():
                 # matrix-core busy fraction of the same launch from its counters
                 "mfma_busy": (measured_traffic(MFMA_SUMMARY, "mfma_busy_fraction_at_2.4GHz")
                               if S == inputs.GROUP_S else None),
-                "kernel": "g4a::pf::prefill_kernel<512, 8, true, false, 128, 4, 1, true, false>",
+                "kernel": "g4a::pf::prefill_kernel<512, 8, true, false, 128, 3, 1, true, false>",
                 "flops_per_launch": fl_glo, "ms_per_launch": t}
     roof_dec = None
     if run_decode:
